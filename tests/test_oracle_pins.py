@@ -1,0 +1,195 @@
+"""Pins of the float64 attention oracle against things other than itself:
+the pages' worked examples, closed forms, scipy routines and brute force."""
+
+import math
+
+import numpy as np
+import pytest
+import scipy.special
+from hypothesis import given, settings, strategies as st
+
+from oracle import (allowed, attention_brute, attention_ref, merge_partials,
+                    online_softmax_steps)
+from tests.conftest import read_golden
+
+
+def _floats(s):
+    return [float(t) for t in s.split()]
+
+
+@pytest.mark.parametrize("name", ["online_softmax_x6.txt",
+                                  "online_softmax_exercise7.txt"])
+def test_online_softmax_worked_examples(name):
+    g = read_golden(name)
+    x = _floats(g["x"])
+    steps, sm = online_softmax_steps(x, int(g["block"]))
+    dec = int(g["decimals"])
+    assert [round(m, dec) for m, _ in steps] == _floats(g["steps_m"])
+    assert [round(l, dec) for _, l in steps] == _floats(g["steps_l"])
+    direct = scipy.special.softmax(np.asarray(x))
+    assert np.max(np.abs(np.asarray(sm) - direct)) < 1e-15
+    if "softmax" in g:
+        assert [round(t, dec) for t in sm] == _floats(g["softmax"])
+
+
+def test_online_softmax_shift_invariance():
+    rng = np.random.default_rng(7)
+    x = rng.normal(size=37) * 4
+    _, a = online_softmax_steps(x, 5)
+    _, b = online_softmax_steps(x + 123.25, 5)
+    assert np.max(np.abs(np.asarray(a) - np.asarray(b))) < 1e-14
+
+
+def test_merge_matches_whole_row():
+    rng = np.random.default_rng(11)
+    x = rng.normal(size=20) * 3
+    v = rng.normal(size=(20, 5))
+    cut = 8
+
+    def part(xs, vs):
+        m = xs.max()
+        e = np.exp(xs - m)
+        return m, e.sum(), e @ vs
+
+    m, l, o = merge_partials(part(x[:cut], v[:cut]), part(x[cut:], v[cut:]))
+    w = scipy.special.softmax(x)
+    assert abs(m - x.max()) == 0
+    assert abs(l - np.exp(x - x.max()).sum()) < 1e-13
+    assert np.max(np.abs(o - w @ v)) < 1e-14
+    # Order independence.
+    m2, l2, o2 = merge_partials(part(x[cut:], v[cut:]), part(x[:cut], v[:cut]))
+    assert m2 == m and abs(l2 - l) < 1e-14 and np.max(np.abs(o2 - o)) < 1e-15
+
+
+def _rand_case(seed, B, Hq, Hkv, L, dqk, dv, std=1.0):
+    rng = np.random.default_rng(seed)
+    q = rng.normal(size=(B, Hq, L, dqk)) * std
+    k = rng.normal(size=(B, Hkv, L, dqk)) * std
+    v = rng.normal(size=(B, Hkv, L, dv))
+    return q, k, v
+
+
+@settings(max_examples=60, deadline=None)
+@given(seed=st.integers(0, 10_000),
+       L=st.integers(1, 11),
+       dqk=st.integers(1, 4), dv=st.integers(1, 4),
+       group=st.sampled_from([1, 2]), Hkv=st.sampled_from([1, 2]),
+       B=st.sampled_from([1, 2]),
+       causal=st.booleans(),
+       wl=st.integers(-1, 5), wr=st.integers(-1, 5),
+       use_seg=st.booleans(), cap=st.sampled_from([0.0, 0.7, 3.0]))
+def test_ref_matches_brute_force(seed, L, dqk, dv, group, Hkv, B, causal, wl,
+                                 wr, use_seg, cap):
+    Hq = Hkv * group
+    q, k, v = _rand_case(seed, B, Hq, Hkv, L, dqk, dv)
+    rng = np.random.default_rng(seed + 1)
+    seg = rng.integers(0, 3, size=(B, L)) if use_seg else None
+    kw = dict(scale=0.8, soft_cap=cap, causal=causal, window_left=wl,
+              window_right=wr, seg_q=seg, seg_kv=seg)
+    o, lse = attention_ref(q, k, v, panel=3, **kw)
+    ob, lb = attention_brute(q, k, v, **kw)
+    ob = np.asarray(ob)
+    lb = np.asarray(lb)
+    assert np.array_equal(np.isinf(lse), np.isinf(lb))
+    fin = np.isfinite(lb)
+    assert np.max(np.abs(lse[fin] - lb[fin]), initial=0) < 1e-12
+    assert np.max(np.abs(o - ob)) < 1e-12
+
+
+def test_probability_rows_sum_to_one_and_o_in_hull():
+    q, k, v = _rand_case(3, 1, 2, 2, 64, 8, 4)
+    ones = np.ones_like(v)
+    o, _ = attention_ref(q, k, ones, scale=0.5, causal=True, window_left=9)
+    assert np.max(np.abs(o - 1.0)) < 1e-14
+    o, _ = attention_ref(q, k, v, scale=0.5, causal=True, window_left=9)
+    for d in range(v.shape[3]):
+        assert np.all(o[..., d] <= v[..., d].max() + 1e-12)
+        assert np.all(o[..., d] >= v[..., d].min() - 1e-12)
+
+
+def test_causal_first_row_is_v0():
+    q, k, v = _rand_case(4, 1, 3, 3, 40, 16, 8)
+    scale = 1 / math.sqrt(16)
+    o, lse = attention_ref(q, k, v, scale=scale, causal=True)
+    assert np.array_equal(o[0, :, 0, :], v[0, :, 0, :])
+    s00 = scale * np.einsum("hd,hd->h", q[0, :, 0], k[0, :, 0])
+    assert np.max(np.abs(lse[0, :, 0] - s00)) < 1e-14
+
+
+def test_dense_equals_scipy_softmax():
+    q, k, v = _rand_case(5, 1, 2, 2, 50, 16, 12)
+    scale = 0.3
+    o, lse = attention_ref(q, k, v, scale=scale, panel=7)
+    for h in range(2):
+        s = scale * q[0, h] @ k[0, h].T
+        assert np.max(np.abs(o[0, h] - scipy.special.softmax(s, axis=1) @ v[0, h])) < 1e-13
+        assert np.max(np.abs(lse[0, h] - scipy.special.logsumexp(s, axis=1))) < 1e-13
+
+
+def test_lse_matches_scipy_logsumexp_on_masked_rows():
+    q, k, v = _rand_case(6, 1, 1, 1, 70, 8, 8)
+    seg = np.repeat(np.arange(5), 14)
+    scale, cap = 0.9, 2.5
+    _, lse = attention_ref(q, k, v, scale=scale, soft_cap=cap, causal=True,
+                           window_left=20, seg_q=seg)
+    s = cap * np.tanh(scale * (q[0, 0] @ k[0, 0].T) / cap)
+    for i in range(70):
+        js = [j for j in range(70) if j <= i and i - j <= 20 and seg[i] == seg[j]]
+        assert abs(lse[0, 0, i] - scipy.special.logsumexp(s[i, js])) < 1e-13
+
+
+def test_gqa_equals_mha_with_repeated_kv():
+    q, k, v = _rand_case(8, 2, 8, 2, 33, 8, 8)
+    kw = dict(scale=0.4, causal=True, window_left=12)
+    o, lse = attention_ref(q, k, v, **kw)
+    o2, lse2 = attention_ref(q, np.repeat(k, 4, axis=1), np.repeat(v, 4, axis=1), **kw)
+    assert np.max(np.abs(o - o2)) == 0 and np.max(np.abs(lse - lse2)) == 0
+    # Head 5 reads kv head 1 (contiguous groups of 4): differs from kv head 0.
+    o3, _ = attention_ref(q[:, 5:6], k[:, 1:2], v[:, 1:2], **kw)
+    assert np.max(np.abs(o3[:, 0] - o[:, 5])) == 0
+
+
+def test_soft_cap_bounds_and_limit():
+    q, k, v = _rand_case(9, 1, 1, 1, 30, 8, 8, std=3.0)
+    cap = 2.0
+    _, lse = attention_ref(q, k, v, scale=1.0, soft_cap=cap, causal=True)
+    # lse_i = ln sum_{j<=i} e^{s_ij} with |s_ij| < cap:
+    n = np.arange(1, 31)
+    assert np.all(lse[0, 0] < cap + np.log(n))
+    assert np.all(lse[0, 0] > -cap + np.log(n))
+    o_inf, lse_inf = attention_ref(q, k, v, scale=1.0, causal=True)
+    # cap * tanh(s / cap) = s - s^3 / (3 cap^2) + ...: at cap 1e8 and
+    # |s| < 100 the difference is below 1e-10.
+    o_big, lse_big = attention_ref(q, k, v, scale=1.0, soft_cap=1e8, causal=True)
+    assert np.max(np.abs(o_big - o_inf)) < 1e-9
+    assert np.max(np.abs(lse_big - lse_inf)) < 1e-9
+
+
+def test_rows_subset_and_empty_rows():
+    q, k, v = _rand_case(10, 1, 2, 1, 48, 8, 8)
+    seg_q = np.repeat(np.arange(4), 12)
+    seg_kv = seg_q.copy()
+    seg_kv[seg_kv == 2] = 9    # queries of document 2 see no key
+    kw = dict(scale=0.5, causal=True, seg_q=seg_q, seg_kv=seg_kv)
+    o, lse = attention_ref(q, k, v, **kw)
+    rows = np.array([47, 0, 25, 13])
+    o2, lse2 = attention_ref(q, k, v, rows=rows, **kw)
+    assert np.array_equal(o[:, :, rows], o2) and np.array_equal(lse[:, :, rows], lse2)
+    empty = seg_q == 2
+    assert np.all(np.isneginf(lse[:, :, empty])) and np.all(o[:, :, empty] == 0)
+    assert np.all(np.isfinite(lse[:, :, ~empty]))
+
+
+def test_allowed_definition_examples():
+    i = np.arange(6)[:, None]
+    j = np.arange(6)[None, :]
+    a = allowed(i, j, L_q=6, L_kv=6, causal=True, window_left=2)
+    expect = np.array([[1 if (jj <= ii and ii - jj <= 2) else 0
+                        for jj in range(6)] for ii in range(6)], bool)
+    assert np.array_equal(a, expect)
+    # padding beyond the lengths is masked
+    a = allowed(np.arange(8)[:, None], np.arange(8)[None, :], L_q=5, L_kv=6)
+    assert a[:5, :6].all() and not a[5:, :].any() and not a[:, 6:].any()
+    # right window only
+    a = allowed(i, j, L_q=6, L_kv=6, window_right=1)
+    assert a[0, 1] and not a[0, 2] and a[5, 0]
