@@ -1,0 +1,11 @@
+"""Block-sparse (Splash) attention forward for AMD MI355X (gfx950).
+
+The work is done by ``libsplash.so`` (HIP kernels + host mask compiler,
+C ABI in include/splash.h); this package only marshals arguments.  The
+library is loaded on first use and its absence is an error.
+"""
+
+from .api import MaskTables, compile_mask, fwd_tile, splash_fwd
+from ._lib import SplashError
+
+__all__ = ["MaskTables", "compile_mask", "fwd_tile", "splash_fwd", "SplashError"]

@@ -1,0 +1,224 @@
+"""Python binding of the C ABI: ``compile_mask`` and ``splash_fwd``.
+
+Argument marshalling only: the mask tables come from ``attn_mask_compile``
+(host C++) and the forward runs in the library's HIP kernels.  PyTorch
+provides device memory, host<->device copies and the current stream.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+
+from . import _lib
+
+_DTYPES = {"f32": _lib.SPLASH_F32, "bf16": _lib.SPLASH_BF16}
+_MASK_MODES = {"computed": _lib.SPLASH_MASK_COMPUTED, "stored": _lib.SPLASH_MASK_STORED}
+
+
+def _ptr(arr: Optional[np.ndarray]):
+    return None if arr is None else arr.ctypes.data_as(ctypes.c_void_p)
+
+
+def _seg_array(seg, L):
+    if seg is None:
+        return None
+    a = np.ascontiguousarray(np.asarray(seg).reshape(-1), dtype=np.int32)
+    if a.shape[0] != L:
+        raise ValueError(f"segment ids have length {a.shape[0]}, expected {L}")
+    return a
+
+
+@dataclass
+class MaskTables:
+    """Host copy of the MaskInfo execution table (see include/splash.h)."""
+
+    L_q: int
+    L_kv: int
+    block_q: int
+    block_kv: int
+    n_q_blocks: int
+    n_kv_blocks: int
+    n_active: int
+    n_partial: int
+    n_patterns: int
+    block_mask: np.ndarray
+    active_rows: np.ndarray
+    active_cols: np.ndarray
+    block_code: np.ndarray
+    mask_next: np.ndarray
+    bounds: np.ndarray
+    row_ptr: np.ndarray
+    row_order: np.ndarray
+    partial_mask_blocks: np.ndarray
+    _device: dict = field(default_factory=dict, repr=False)
+
+    def device(self, device):
+        """Device copies (torch tensors) of the arrays the forward reads."""
+        import torch
+        key = str(torch.device(device))
+        if key not in self._device:
+            def up(a, dt):
+                t = torch.from_numpy(np.ascontiguousarray(a)).to(dt)
+                if t.numel() == 0:   # keep a valid, non-null allocation
+                    t = torch.zeros(1, dtype=dt)
+                return t.to(device)
+            self._device[key] = {
+                "row_ptr": up(self.row_ptr, torch.int32),
+                "row_order": up(self.row_order, torch.int32),
+                "active_cols": up(self.active_cols, torch.int32),
+                "block_code": up(self.block_code, torch.int8),
+                "mask_next": up(self.mask_next, torch.int32),
+                "partial_mask_blocks": up(self.partial_mask_blocks.reshape(-1), torch.uint8),
+            }
+        return self._device[key]
+
+
+def compile_mask(L_q: int, block_q: int, block_kv: int, *, L_kv: Optional[int] = None,
+                 causal: bool = False, window_left: int = -1, window_right: int = -1,
+                 seg_q=None, seg_kv=None) -> MaskTables:
+    """Run ``attn_mask_compile`` (both phases) and return the host tables."""
+    lib = _lib.load()
+    L_kv = L_q if L_kv is None else L_kv
+    sq = _seg_array(seg_q, L_q)
+    skv = _seg_array(seg_kv, L_kv) if seg_kv is not None else None
+    desc = _lib.MaskDesc(L_q, L_kv, block_q, block_kv, int(bool(causal)), window_left,
+                         window_right, _ptr(sq), _ptr(skv))
+    sizes = _lib.MaskSizes()
+    _lib.check(lib.attn_mask_compile(ctypes.byref(desc), ctypes.byref(sizes), None))
+    nq, nkv, na, npat = sizes.n_q_blocks, sizes.n_kv_blocks, sizes.n_active, sizes.n_patterns
+    arrays = {
+        "block_mask": np.zeros(nq * nkv, np.int8),
+        "active_rows": np.zeros(na, np.int32),
+        "active_cols": np.zeros(na, np.int32),
+        "block_code": np.zeros(na, np.int8),
+        "mask_next": np.zeros(na, np.int32),
+        "bounds": np.zeros(na, np.uint8),
+        "row_ptr": np.zeros(nq + 1, np.int32),
+        "row_order": np.zeros(nq, np.int32),
+        "partial_mask_blocks": np.zeros(npat * block_q * block_kv, np.uint8),
+    }
+    tabs = _lib.MaskTablesC(*(_ptr(arrays[name]) for name, _ in _lib.MaskTablesC._fields_))
+    _lib.check(lib.attn_mask_compile(ctypes.byref(desc), ctypes.byref(sizes), ctypes.byref(tabs)))
+    arrays["block_mask"] = arrays["block_mask"].reshape(nq, nkv)
+    arrays["partial_mask_blocks"] = arrays["partial_mask_blocks"].reshape(npat, block_q, block_kv)
+    return MaskTables(L_q, L_kv, block_q, block_kv, nq, nkv, na, sizes.n_partial, npat, **arrays)
+
+
+def fwd_tile(dtype: str, d_qk: int, d_v: int):
+    """(block_q, block_kv) the forward kernel uses for this dtype and head dims."""
+    lib = _lib.load()
+    bq, bkv = ctypes.c_int32(), ctypes.c_int32()
+    _lib.check(lib.splash_fwd_tile(_DTYPES[dtype], d_qk, d_v, ctypes.byref(bq), ctypes.byref(bkv)))
+    return bq.value, bkv.value
+
+
+def _torch_dtype_name(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return "bf16"
+    if t.dtype == torch.float32:
+        return "f32"
+    raise TypeError(f"unsupported dtype {t.dtype}; use torch.float32 or torch.bfloat16")
+
+
+def splash_fwd(q, k, v, *, scale: Optional[float] = None, soft_cap: float = 0.0,
+               causal: bool = False, window_left: int = -1, window_right: int = -1,
+               seg_q=None, seg_kv=None, tables: Optional[MaskTables] = None,
+               mask_mode: str = "computed", out=None, lse=None, return_lse: bool = True,
+               stream=None):
+    """Block-sparse attention forward on the GPU.
+
+    q [B, Hq, L, d_qk], k [B, Hkv, L, d_qk], v [B, Hkv, L, d_v]: contiguous
+    torch tensors on one GPU, all float32 or all bfloat16.  ``seg_q`` /
+    ``seg_kv``: segment ids [L] (shared by the batch) or [B, L].  ``tables``:
+    a MaskTables compiled for this mask at the kernel's block sizes
+    (``fwd_tile``); compiled here when omitted.  Returns (o, lse) with o like q
+    but with d_v, lse float32 [B, Hq, L] (None if ``return_lse`` is False).
+    """
+    import torch
+    lib = _lib.load()
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("q, k and v must be GPU tensors")
+    dt = _torch_dtype_name(q)
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k and v must share one dtype")
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, L, d]")
+    B, Hq, L, d_qk = q.shape
+    Hkv = k.shape[1]
+    d_v = v.shape[3]
+    if tuple(k.shape) != (B, Hkv, L, d_qk) or tuple(v.shape[:3]) != (B, Hkv, L):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+    if scale is None:
+        scale = 1.0 / float(d_qk) ** 0.5
+    bq, bkv = fwd_tile(dt, d_qk, d_v)
+
+    seg_q_dev = seg_kv_dev = None
+    per_batch = False
+    if seg_q is not None:
+        sq = torch.as_tensor(np.asarray(seg_q.cpu() if hasattr(seg_q, "cpu") else seg_q),
+                             dtype=torch.int32)
+        sq = sq.reshape(-1, L)
+        skv = None
+        if seg_kv is not None:
+            skv = torch.as_tensor(np.asarray(seg_kv.cpu() if hasattr(seg_kv, "cpu") else seg_kv),
+                                  dtype=torch.int32).reshape(-1, L)
+        rows_q = sq.expand(B, L) if sq.shape[0] == 1 else sq
+        rows_kv = None if skv is None else (skv.expand(B, L) if skv.shape[0] == 1 else skv)
+        if rows_q.shape[0] != B or (rows_kv is not None and rows_kv.shape[0] != B):
+            raise ValueError("segment ids must be [L] or [B, L]")
+        per_batch = B > 1 and (not bool((rows_q == rows_q[:1]).all()) or
+                               (rows_kv is not None and not bool((rows_kv == rows_kv[:1]).all())))
+        seg_q_dev = rows_q.contiguous().to(q.device)
+        seg_kv_dev = None if rows_kv is None else rows_kv.contiguous().to(q.device)
+
+    if out is None:
+        out = torch.empty((B, Hq, L, d_v), dtype=q.dtype, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, L), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+
+    batches = range(B) if per_batch else [None]
+    for bsel in batches:
+        if tables is None or per_batch:
+            ids_q = None if seg_q_dev is None else seg_q_dev[bsel or 0].cpu().numpy()
+            ids_kv = None if seg_kv_dev is None else seg_kv_dev[bsel or 0].cpu().numpy()
+            tabs = compile_mask(L, bq, bkv, causal=causal, window_left=window_left,
+                                window_right=window_right, seg_q=ids_q, seg_kv=ids_kv)
+        else:
+            tabs = tables
+        if (tabs.block_q, tabs.block_kv, tabs.L_q) != (bq, bkv, L):
+            raise ValueError(f"tables were compiled for L={tabs.L_q} blocks "
+                             f"{tabs.block_q}x{tabs.block_kv}; need L={L} blocks {bq}x{bkv}")
+        dev = tabs.device(q.device)
+        if bsel is None:
+            qb, kb, vb, ob = q, k, v, out
+            lb = lse
+            sqb, skb, nb = seg_q_dev, seg_kv_dev, B
+        else:
+            sl = slice(bsel, bsel + 1)
+            qb, kb, vb, ob = q[sl], k[sl], v[sl], out[sl]
+            lb = None if lse is None else lse[sl]
+            sqb = seg_q_dev[sl]
+            skb = None if seg_kv_dev is None else seg_kv_dev[sl]
+            nb = 1
+        args = _lib.FwdArgs(
+            _DTYPES[dt], nb, Hq, Hkv, L, d_qk, d_v,
+            qb.data_ptr(), kb.data_ptr(), vb.data_ptr(), ob.data_ptr(),
+            None if lb is None else lb.data_ptr(),
+            int(bool(causal)), window_left, window_right,
+            None if sqb is None else sqb.data_ptr(),
+            None if skb is None else skb.data_ptr(),
+            bq, bkv, tabs.n_q_blocks, tabs.n_active, tabs.n_patterns,
+            dev["row_ptr"].data_ptr(), dev["row_order"].data_ptr(),
+            dev["active_cols"].data_ptr(), dev["block_code"].data_ptr(),
+            dev["mask_next"].data_ptr(), dev["partial_mask_blocks"].data_ptr(),
+            _MASK_MODES[mask_mode], float(scale), float(soft_cap))
+        _lib.check(lib.splash_attn_fwd(ctypes.byref(args), ctypes.c_void_p(stream)))
+    return out, (lse if return_lse else None)

@@ -1,0 +1,75 @@
+// Launch parameters of the forward kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace splash {
+
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;          // may be null
+  int32_t B, Hq, Hkv, L, group;  // group = Hq / Hkv
+  // mask
+  int32_t causal, window_left, window_right;
+  const int32_t* seg_q;   // [B, L] or null
+  const int32_t* seg_kv;  // [B, L] or null (then seg_q is used)
+  int32_t mask_stored;    // 1: partial blocks read patterns
+  // tables
+  int32_t n_q_blocks;
+  const int32_t* row_ptr;
+  const int32_t* row_order;
+  const int32_t* active_cols;
+  const int8_t* block_code;
+  const int32_t* mask_next;
+  const uint8_t* patterns;
+  // arithmetic
+  float scale;        // softmax scale
+  float scale_log2;   // scale * log2(e)
+  float soft_cap;     // > 0 when the cap is on
+  // work-group -> (head, row) mapping
+  int32_t xcd_units;      // number of units spread over XCDs (0: plain order)
+  int32_t unit_heads;     // query heads per unit
+};
+
+// Launchers (return the hipError_t of the launch).
+hipError_t launch_fwd_f32(const FwdParams& p, int d_qk, int d_v, hipStream_t s);
+hipError_t launch_fwd_bf16(const FwdParams& p, int d_qk, int d_v, hipStream_t s);
+
+// Block sizes used by each kernel family.
+constexpr int kF32BlockQ = 64;
+constexpr int kF32BlockKV = 64;
+constexpr int kBf16BlockQ = 128;
+constexpr int kBf16BlockKV = 64;
+
+// Number of XCDs of an MI355X; consecutive work-group ids are dispatched
+// round-robin over them.
+constexpr int kNumXcd = 8;
+
+// Maps a linear work-group id to (flattened head b*Hq+h, q-block row rank).
+// When xcd_units > 0, all work-groups of one unit (a K/V head group or a
+// single query head) land on the same XCD so that they share its L2; within
+// an XCD, rows are taken longest-first across that XCD's units.
+__device__ __forceinline__ void map_workgroup(const FwdParams& p, int wg, int* head, int* rank) {
+  const int n_heads = p.B * p.Hq;
+  if (p.xcd_units > 0) {
+    const int xcd = wg % kNumXcd;
+    const int slot = wg / kNumXcd;
+    const int units_per_xcd = p.xcd_units / kNumXcd;
+    const int per_rank = units_per_xcd * p.unit_heads;
+    const int rk = slot / per_rank;
+    const int rem = slot - rk * per_rank;
+    const int unit_local = rem / p.unit_heads;
+    const int sub = rem - unit_local * p.unit_heads;
+    *head = (unit_local * kNumXcd + xcd) * p.unit_heads + sub;
+    *rank = rk;
+  } else {
+    *rank = wg / n_heads;
+    *head = wg - *rank * n_heads;
+  }
+}
+
+}  // namespace splash

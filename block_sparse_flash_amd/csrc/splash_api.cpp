@@ -1,0 +1,155 @@
+// splash_fwd_tile / splash_attn_fwd: argument validation, kernel selection
+// and launch.  See include/splash.h for the contract of each call.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+
+#include "errors.h"
+#include "fwd_params.h"
+#include "splash.h"
+
+namespace {
+
+bool dims_supported(int32_t dtype, int32_t d_qk, int32_t d_v) {
+  if (dtype == SPLASH_F32) return (d_qk == 64 || d_qk == 128) && (d_v == 64 || d_v == 128);
+  if (dtype == SPLASH_BF16)
+    return (d_qk == 64 || d_qk == 128 || d_qk == 192) && (d_v == 64 || d_v == 128);
+  return false;
+}
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+// Work-group placement: a "unit" (one K/V head group, else one query head)
+// is kept on one XCD when the unit count divides evenly over the XCDs.
+void choose_xcd_units(const splash_fwd_args& a, splash::FwdParams* p) {
+  p->xcd_units = 0;
+  p->unit_heads = 1;
+  const char* env = std::getenv("SPLASH_XCD_MAP");
+  if (env && env[0] == '0') return;
+  const int64_t kv_units = static_cast<int64_t>(a.B) * a.Hkv;
+  const int64_t q_units = static_cast<int64_t>(a.B) * a.Hq;
+  if (kv_units % splash::kNumXcd == 0) {
+    p->xcd_units = static_cast<int32_t>(kv_units);
+    p->unit_heads = a.Hq / a.Hkv;
+  } else if (q_units % splash::kNumXcd == 0) {
+    p->xcd_units = static_cast<int32_t>(q_units);
+    p->unit_heads = 1;
+  }
+}
+
+}  // namespace
+
+extern "C" int splash_fwd_tile(int32_t dtype, int32_t d_qk, int32_t d_v, int32_t* block_q,
+                               int32_t* block_kv) {
+  splash::clear_error();
+  if (!block_q || !block_kv) return splash::fail(SPLASH_EINVAL, "splash_fwd_tile: NULL output");
+  if (dtype != SPLASH_F32 && dtype != SPLASH_BF16)
+    return splash::fail(SPLASH_EDTYPE, "splash_fwd_tile: unknown dtype %d", dtype);
+  if (!dims_supported(dtype, d_qk, d_v))
+    return splash::fail(SPLASH_EUNSUPPORTED, "splash_fwd_tile: head dims (%d, %d) not built for dtype %d",
+                        d_qk, d_v, dtype);
+  *block_q = dtype == SPLASH_F32 ? splash::kF32BlockQ : splash::kBf16BlockQ;
+  *block_kv = dtype == SPLASH_F32 ? splash::kF32BlockKV : splash::kBf16BlockKV;
+  return SPLASH_OK;
+}
+
+extern "C" int splash_attn_fwd(const splash_fwd_args* args, void* stream) {
+  splash::clear_error();
+  if (!args) return splash::fail(SPLASH_EINVAL, "splash_attn_fwd: NULL args");
+  const splash_fwd_args& a = *args;
+  if (a.dtype != SPLASH_F32 && a.dtype != SPLASH_BF16)
+    return splash::fail(SPLASH_EDTYPE, "splash_attn_fwd: unknown dtype %d", a.dtype);
+  if (a.B < 0 || a.Hq < 0 || a.L < 0 || a.Hkv <= 0)
+    return splash::fail(SPLASH_EINVAL, "splash_attn_fwd: bad sizes B=%d Hq=%d Hkv=%d L=%d", a.B,
+                        a.Hq, a.Hkv, a.L);
+  if (a.Hq % a.Hkv != 0)
+    return splash::fail(SPLASH_ESHAPE, "splash_attn_fwd: Hq=%d is not a multiple of Hkv=%d", a.Hq,
+                        a.Hkv);
+  if (!dims_supported(a.dtype, a.d_qk, a.d_v))
+    return splash::fail(SPLASH_EUNSUPPORTED,
+                        "splash_attn_fwd: head dims (%d, %d) not built for dtype %d", a.d_qk,
+                        a.d_v, a.dtype);
+  if (a.causal != 0 && a.causal != 1)
+    return splash::fail(SPLASH_EINVAL, "splash_attn_fwd: causal must be 0 or 1");
+  if (a.window_left < -1 || a.window_right < -1)
+    return splash::fail(SPLASH_EINVAL, "splash_attn_fwd: window must be -1 or >= 0");
+  if (a.mask_mode != SPLASH_MASK_COMPUTED && a.mask_mode != SPLASH_MASK_STORED)
+    return splash::fail(SPLASH_EINVAL, "splash_attn_fwd: unknown mask_mode %d", a.mask_mode);
+  if (!std::isfinite(a.scale) || !(a.scale > 0.0f))
+    return splash::fail(SPLASH_EINVAL, "splash_attn_fwd: scale must be finite and > 0");
+  if (std::isnan(a.soft_cap) || std::isinf(a.soft_cap))
+    return splash::fail(SPLASH_EINVAL, "splash_attn_fwd: soft_cap must be finite");
+  if (!a.seg_q && a.seg_kv)
+    return splash::fail(SPLASH_EINVAL, "splash_attn_fwd: seg_kv given without seg_q");
+
+  int32_t bq = 0, bkv = 0;
+  splash_fwd_tile(a.dtype, a.d_qk, a.d_v, &bq, &bkv);
+  if (a.block_q != bq || a.block_kv != bkv)
+    return splash::fail(SPLASH_ESHAPE,
+                        "splash_attn_fwd: tables built for blocks %dx%d, kernel uses %dx%d",
+                        a.block_q, a.block_kv, bq, bkv);
+  const int64_t nq = (static_cast<int64_t>(a.L) + bq - 1) / bq;
+  if (a.n_q_blocks != nq)
+    return splash::fail(SPLASH_ESHAPE, "splash_attn_fwd: n_q_blocks=%d but L=%d needs %lld",
+                        a.n_q_blocks, a.L, static_cast<long long>(nq));
+  if (a.n_active < 0 || a.n_patterns < 0)
+    return splash::fail(SPLASH_EINVAL, "splash_attn_fwd: negative table size");
+
+  const int64_t n_heads = static_cast<int64_t>(a.B) * a.Hq;
+  if (n_heads == 0 || a.L == 0) return SPLASH_OK;  // nothing to compute
+  const int64_t n_wg = n_heads * nq;
+  const int64_t max_d = a.d_qk > a.d_v ? a.d_qk : a.d_v;
+  if (n_wg > INT32_MAX || n_heads * a.L > (int64_t{1} << 46) / max_d)
+    return splash::fail(SPLASH_ESHAPE, "splash_attn_fwd: problem too large");
+
+  if (!a.q || !a.k || !a.v || !a.o)
+    return splash::fail(SPLASH_EINVAL, "splash_attn_fwd: NULL q/k/v/o");
+  if (!aligned16(a.q) || !aligned16(a.k) || !aligned16(a.v) || !aligned16(a.o))
+    return splash::fail(SPLASH_EINVAL, "splash_attn_fwd: q/k/v/o must be 16-byte aligned");
+  if (!a.row_ptr || !a.row_order)
+    return splash::fail(SPLASH_EINVAL, "splash_attn_fwd: NULL row_ptr or row_order");
+  if (a.n_active > 0 && (!a.active_cols || !a.block_code))
+    return splash::fail(SPLASH_EINVAL, "splash_attn_fwd: NULL active_cols or block_code");
+  if (a.mask_mode == SPLASH_MASK_STORED && a.n_active > 0 &&
+      (!a.mask_next || (a.n_patterns > 0 && !a.partial_mask_blocks)))
+    return splash::fail(SPLASH_EINVAL, "splash_attn_fwd: stored mask mode needs mask_next and patterns");
+
+  splash::FwdParams p{};
+  p.q = a.q;
+  p.k = a.k;
+  p.v = a.v;
+  p.o = a.o;
+  p.lse = a.lse;
+  p.B = a.B;
+  p.Hq = a.Hq;
+  p.Hkv = a.Hkv;
+  p.L = a.L;
+  p.group = a.Hq / a.Hkv;
+  p.causal = a.causal;
+  p.window_left = a.window_left;
+  p.window_right = a.window_right;
+  p.seg_q = a.seg_q;
+  p.seg_kv = a.seg_kv;
+  p.mask_stored = a.mask_mode == SPLASH_MASK_STORED ? 1 : 0;
+  p.n_q_blocks = static_cast<int32_t>(nq);
+  p.row_ptr = a.row_ptr;
+  p.row_order = a.row_order;
+  p.active_cols = a.active_cols;
+  p.block_code = a.block_code;
+  p.mask_next = a.mask_next;
+  p.patterns = a.partial_mask_blocks;
+  p.scale = a.scale;
+  p.scale_log2 = a.scale * 1.4426950408889634f;
+  p.soft_cap = a.soft_cap > 0.0f ? a.soft_cap : 0.0f;
+  choose_xcd_units(a, &p);
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = a.dtype == SPLASH_F32 ? splash::launch_fwd_f32(p, a.d_qk, a.d_v, s)
+                                             : splash::launch_fwd_bf16(p, a.d_qk, a.d_v, s);
+  if (e != hipSuccess)
+    return splash::fail(SPLASH_EHIP, "splash_attn_fwd: launch failed: %s", hipGetErrorString(e));
+  return SPLASH_OK;
+}

@@ -1,0 +1,221 @@
+/*
+ * splash.h - C ABI of the block-sparse (Splash) attention forward for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Two operations cross this boundary:
+ *
+ *   attn_mask_compile  host-side preprocessing of a causal / local-window /
+ *                      segment-id mask (and their AND) into the MaskInfo
+ *                      block-sparse execution table.  Defined by "Lecture 13 -
+ *                      Pallas Kernels and Splash Attention" (CMU 11-868
+ *                      notes), sections 6.1 (empty / full / partial blocks),
+ *                      6.2 (block_mask, active rows and columns,
+ *                      partial_mask_blocks, mask_next, bounds_start /
+ *                      bounds_end), 6.4 (segment ids, AND of masks) and 6.6
+ *                      (one byte per pattern element).
+ *
+ *   splash_attn_fwd    the attention forward over the active blocks only:
+ *                      running max m, running sum l and output accumulator o
+ *                      per query row, the alpha = e^(m_old - m_new) rescale,
+ *                      and a single divide o / l after the last block
+ *                      (deferred normalisation), returning o and the
+ *                      log-sum-exp residual lse = m + ln l.  Defined by
+ *                      Lecture 13 sections 5.1-5.2 (online softmax, kernel
+ *                      body), 5.2 (MHA / GQA heads), 5.4 (logit soft cap
+ *                      cap * tanh(x / cap)), 6.3 (Splash kernel: inputs q, k,
+ *                      v, segment ids, patterns; outputs O and logsumexp), and
+ *                      by the joto.ai page on core LLM operators, section
+ *                      "LSE and online softmax" (lse = m + log l).
+ *
+ * Conventions for every call:
+ *   - Return value: SPLASH_OK (0) or one of the SPLASH_E* codes below.  On an
+ *     error nothing is written to any output and no kernel is launched;
+ *     splash_last_error() returns a message for the calling thread.
+ *   - No call allocates memory that outlives it, keeps global state between
+ *     calls (other than the per-thread error message) or throws across the
+ *     ABI.  The caller owns every buffer.
+ *   - "host" pointers are CPU memory; "device" pointers are HIP device memory
+ *     on the current device.
+ */
+#ifndef SPLASH_H_
+#define SPLASH_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPLASH_VERSION 100
+
+enum splash_status {
+  SPLASH_OK = 0,
+  SPLASH_EINVAL = 1,        /* NULL pointer, negative size, bad flag value */
+  SPLASH_ESHAPE = 2,        /* inconsistent shapes or tables */
+  SPLASH_EDTYPE = 3,        /* unknown dtype */
+  SPLASH_EUNSUPPORTED = 4,  /* head dimension not built for this dtype */
+  SPLASH_ENOMEM = 5,        /* host scratch allocation failed */
+  SPLASH_EHIP = 6,          /* the HIP runtime reported an error */
+  SPLASH_EINTERNAL = 7      /* unexpected internal failure */
+};
+
+enum splash_dtype {
+  SPLASH_F32 = 0,   /* float32 storage, float32 arithmetic */
+  SPLASH_BF16 = 1   /* bfloat16 storage, bf16 MFMA with float32 accumulation */
+};
+
+enum splash_mask_mode {
+  /* Partial blocks build their element mask in the kernel from the query and
+   * key positions and the segment ids (Lecture 13 section 6.6 suggests this
+   * in place of stored patterns). */
+  SPLASH_MASK_COMPUTED = 0,
+  /* Partial blocks read partial_mask_blocks[mask_next[g]] (section 6.3). */
+  SPLASH_MASK_STORED = 1
+};
+
+/* Library version (SPLASH_VERSION of the build). */
+int splash_version(void);
+
+/* Message describing the last error on the calling thread ("" if none).
+ * The string is owned by the library and valid until the next call made by
+ * the same thread. */
+const char* splash_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * Mask preprocessing (MaskInfo).
+ * ---------------------------------------------------------------------- */
+
+/* The mask: element (i, j) (query position i, key position j) is allowed iff
+ *   i < L_q and j < L_kv                      (padding of ragged blocks)
+ *   and (!causal or j <= i)
+ *   and (window_left  < 0 or i - j <= window_left)
+ *   and (window_right < 0 or j - i <= window_right)
+ *   and (seg_q == NULL or seg_q[i] == seg_kv[j]).
+ * The blocks are block_q x block_kv; the last block row / column may hang
+ * over the sequence end (ragged L), its padded elements count as masked. */
+typedef struct splash_mask_desc {
+  int32_t L_q;            /* number of query positions, >= 0 */
+  int32_t L_kv;           /* number of key positions, >= 0 */
+  int32_t block_q;        /* > 0 */
+  int32_t block_kv;       /* > 0 */
+  int32_t causal;         /* 0 or 1 */
+  int32_t window_left;    /* -1 (unbounded) or >= 0 */
+  int32_t window_right;   /* -1 (unbounded) or >= 0 */
+  const int32_t* seg_q;   /* host [L_q] segment ids, or NULL: no segment mask */
+  const int32_t* seg_kv;  /* host [L_kv], or NULL: same array as seg_q
+                             (then L_kv must equal L_q) */
+} splash_mask_desc;
+
+typedef struct splash_mask_sizes {
+  int32_t n_q_blocks;     /* ceil(L_q / block_q) */
+  int32_t n_kv_blocks;    /* ceil(L_kv / block_kv) */
+  int32_t n_active;       /* blocks with at least one allowed element */
+  int32_t n_partial;      /* active blocks that are not full */
+  int32_t n_patterns;     /* distinct partial patterns */
+} splash_mask_sizes;
+
+/* Host output arrays, all caller-owned.  Any pointer may be NULL to skip
+ * that array.  Active blocks are listed in row-major order (q-block row, then
+ * kv-block column ascending). */
+typedef struct splash_mask_tables {
+  int8_t* block_mask;        /* [n_q_blocks * n_kv_blocks] 0 empty, 1 partial,
+                                2 full; row-major */
+  int32_t* active_rows;      /* [n_active] q-block row of each active block */
+  int32_t* active_cols;      /* [n_active] kv-block column */
+  int8_t* block_code;        /* [n_active] 1 partial, 2 full */
+  int32_t* mask_next;        /* [n_active] pattern index of a partial block
+                                (patterns numbered by first appearance in
+                                active order), -1 for a full block */
+  uint8_t* bounds;           /* [n_active] bit0 = bounds_start (first active
+                                block of its row), bit1 = bounds_end (last) */
+  int32_t* row_ptr;          /* [n_q_blocks + 1] CSR offsets into the active
+                                list */
+  int32_t* row_order;        /* [n_q_blocks] rows sorted by active count,
+                                longest first, ties by ascending row: the
+                                launch order of the forward */
+  uint8_t* partial_mask_blocks; /* [n_patterns * block_q * block_kv] 1 =
+                                allowed, one byte per element, each pattern
+                                row-major [block_q][block_kv] */
+} splash_mask_tables;
+
+/* Two-phase call.  With tables == NULL: validates desc and fills *sizes.
+ * With tables != NULL: *sizes must hold the values of the first phase for
+ * the same desc (SPLASH_ESHAPE otherwise), and the non-NULL arrays are
+ * filled.  Deterministic; thread-safe; touches no device.
+ * Errors: SPLASH_EINVAL (NULL desc/sizes, negative length, block <= 0,
+ * window < -1, seg_kv NULL with L_kv != L_q), SPLASH_ESHAPE (sizes do not
+ * match), SPLASH_ENOMEM. */
+int attn_mask_compile(const splash_mask_desc* desc, splash_mask_sizes* sizes,
+                      splash_mask_tables* tables);
+
+/* ------------------------------------------------------------------------
+ * Forward.
+ * ---------------------------------------------------------------------- */
+
+/* Block sizes (block_q, block_kv) that the forward kernel for this dtype and
+ * head dimensions uses; the tables passed to splash_attn_fwd must be
+ * compiled with exactly these.  Errors: SPLASH_EDTYPE, SPLASH_EUNSUPPORTED,
+ * SPLASH_EINVAL (NULL outputs). */
+int splash_fwd_tile(int32_t dtype, int32_t d_qk, int32_t d_v,
+                    int32_t* block_q, int32_t* block_kv);
+
+typedef struct splash_fwd_args {
+  int32_t dtype;         /* SPLASH_F32 or SPLASH_BF16: q, k, v and o */
+  int32_t B;             /* batch, >= 0 */
+  int32_t Hq;            /* query heads, >= 0 */
+  int32_t Hkv;           /* key/value heads, >= 1, divides Hq; query head h
+                            reads kv head h / (Hq / Hkv) */
+  int32_t L;             /* sequence length (queries = keys), >= 0 */
+  int32_t d_qk;          /* q/k head dim: f32 {64, 128}; bf16 {64, 128, 192} */
+  int32_t d_v;           /* v head dim:   f32 {64, 128}; bf16 {64, 128} */
+  const void* q;         /* device [B, Hq,  L, d_qk] contiguous, 16-B aligned */
+  const void* k;         /* device [B, Hkv, L, d_qk] contiguous, 16-B aligned */
+  const void* v;         /* device [B, Hkv, L, d_v]  contiguous, 16-B aligned */
+  void* o;               /* device [B, Hq,  L, d_v]  output, same dtype as q,
+                            16-B aligned; rows with no allowed key get 0 */
+  float* lse;            /* device [B, Hq, L] float32 natural-log lse of the
+                            scaled (and capped) logits, -inf for rows with no
+                            allowed key; or NULL */
+  /* Mask parameters (as in splash_mask_desc) used by SPLASH_MASK_COMPUTED
+   * for the element mask of partial blocks.  They must describe the same
+   * mask the tables were compiled from, for every batch element. */
+  int32_t causal;
+  int32_t window_left;
+  int32_t window_right;
+  const int32_t* seg_q;  /* device [B, L] or NULL */
+  const int32_t* seg_kv; /* device [B, L] or NULL (NULL: same as seg_q) */
+  /* Execution table (device copies of attn_mask_compile output for
+   * L_q = L_kv = L and this call's block sizes). */
+  int32_t block_q;       /* must equal splash_fwd_tile's block_q */
+  int32_t block_kv;      /* must equal splash_fwd_tile's block_kv */
+  int32_t n_q_blocks;    /* ceil(L / block_q) */
+  int32_t n_active;
+  int32_t n_patterns;
+  const int32_t* row_ptr;      /* device [n_q_blocks + 1] */
+  const int32_t* row_order;    /* device [n_q_blocks] */
+  const int32_t* active_cols;  /* device [n_active] */
+  const int8_t* block_code;    /* device [n_active] */
+  const int32_t* mask_next;    /* device [n_active] (SPLASH_MASK_STORED) */
+  const uint8_t* partial_mask_blocks; /* device [n_patterns, block_q,
+                                         block_kv] (SPLASH_MASK_STORED) */
+  int32_t mask_mode;     /* splash_mask_mode */
+  float scale;           /* softmax scale, finite and > 0 (e.g. 1/sqrt(d_qk)) */
+  float soft_cap;        /* logit soft cap; <= 0 disables it; logits are
+                            cap * tanh(scale * q.k / cap) */
+} splash_fwd_args;
+
+/* Enqueue the forward on `stream` (a hipStream_t; NULL = the default
+ * stream) and return without waiting.  Validation errors are returned
+ * synchronously: SPLASH_EINVAL (NULL args or buffers, misaligned pointer,
+ * bad flag, scale <= 0 or not finite, soft_cap NaN), SPLASH_ESHAPE
+ * (Hq % Hkv != 0, block sizes or n_q_blocks not matching, size overflow),
+ * SPLASH_EDTYPE, SPLASH_EUNSUPPORTED (head dims), SPLASH_EHIP (the launch
+ * failed).  B, Hq or L equal to 0 is a no-op.  Device-side faults surface at
+ * the caller's next synchronisation. */
+int splash_attn_fwd(const splash_fwd_args* args, void* stream);
+
+#ifdef __cplusplus
+}  /* extern "C" */
+#endif
+
+#endif  /* SPLASH_H_ */

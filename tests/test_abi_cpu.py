@@ -1,0 +1,203 @@
+"""CPU tests of the C ABI: exported symbols, bit-exact mask tables against
+the oracle, and the documented error codes (no GPU needed: validation runs
+before any device call and attn_mask_compile is host code)."""
+
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+from block_sparse_flash_amd import _lib, compile_mask, fwd_tile
+from block_sparse_flash_amd.inputs import WORKLOADS, segment_ids
+from oracle import mask_tables_ref
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+TABLE_FIELDS = ["block_mask", "active_rows", "active_cols", "block_code",
+                "mask_next", "bounds", "row_ptr", "row_order",
+                "partial_mask_blocks"]
+
+
+def _declared_functions():
+    names = []
+    for h in os.listdir(os.path.join(ROOT, "include")):
+        if not h.endswith(".h"):
+            continue
+        text = open(os.path.join(ROOT, "include", h)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, re.M):
+            if not m.group(0).lstrip().startswith(("typedef", "#", "enum", "struct")):
+                names.append(m.group(1))
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    declared = _declared_functions()
+    assert set(declared) == set(_lib.EXPORTED), declared
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert lib.splash_version() == 100
+
+
+def _assert_tables_equal(t, ref):
+    for key in ("n_q_blocks", "n_kv_blocks", "n_active", "n_partial", "n_patterns"):
+        assert getattr(t, key) == ref[key], key
+    for name in TABLE_FIELDS:
+        a, b = getattr(t, name), ref[name]
+        assert a.dtype == b.dtype and a.shape == b.shape, name
+        assert np.array_equal(a, b), name
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_tables_bit_exact_on_workloads(name):
+    w = WORKLOADS[name]
+    bq, bkv = fwd_tile(w.dtype, w.d_qk, w.d_v)
+    seg = segment_ids(w.L, w.seed, w.seg_min, w.seg_max) if w.segments else None
+    kw = dict(causal=w.causal, window_left=w.window_left,
+              window_right=w.window_right, seg_q=seg, seg_kv=seg)
+    t = compile_mask(w.L, bq, bkv, **kw)
+    _assert_tables_equal(t, mask_tables_ref(w.L, w.L, bq, bkv, **kw))
+
+
+@settings(max_examples=150, deadline=None)
+@given(Lq=st.integers(0, 150), dL=st.integers(-20, 20),
+       bq=st.sampled_from([1, 2, 3, 8, 16, 64]), bkv=st.sampled_from([1, 4, 5, 16, 64]),
+       causal=st.booleans(), wl=st.integers(-1, 40), wr=st.integers(-1, 40),
+       seg_mode=st.sampled_from(["none", "same", "split", "noncontig"]),
+       seed=st.integers(0, 10_000))
+def test_tables_bit_exact_random(Lq, dL, bq, bkv, causal, wl, wr, seg_mode, seed):
+    rng = np.random.default_rng(seed)
+    Lkv = Lq if seg_mode in ("same",) else max(0, Lq + dL)
+    sq = skv = None
+    if seg_mode == "same" and Lq > 0:
+        sq = np.sort(rng.integers(0, 5, size=Lq)).astype(np.int32)
+    elif seg_mode == "split" and Lq > 0 and Lkv > 0:
+        sq = np.sort(rng.integers(0, 4, size=Lq)).astype(np.int32)
+        skv = np.sort(rng.integers(0, 4, size=Lkv)).astype(np.int32)
+    elif seg_mode == "noncontig" and Lq > 0 and Lkv > 0:
+        sq = rng.integers(0, 3, size=Lq).astype(np.int32)
+        skv = rng.integers(0, 3, size=Lkv).astype(np.int32)
+    kw = dict(causal=causal, window_left=wl, window_right=wr, seg_q=sq, seg_kv=skv)
+    t = compile_mask(Lq, bq, bkv, L_kv=Lkv, **kw)
+    _assert_tables_equal(t, mask_tables_ref(Lq, Lkv, bq, bkv, **kw))
+
+
+def test_empty_and_no_allowed_mask():
+    t = compile_mask(0, 64, 64, causal=True)
+    assert t.n_q_blocks == 0 and t.n_active == 0 and t.row_ptr.tolist() == [0]
+    # Every query in its own segment, keys in another: nothing is allowed.
+    t = compile_mask(100, 16, 16, seg_q=np.zeros(100, np.int32),
+                     seg_kv=np.ones(100, np.int32))
+    assert t.n_active == 0 and t.row_ptr.tolist() == [0] * (t.n_q_blocks + 1)
+
+
+# ---------------------------------------------------------------- errors
+
+
+def _compile_raw(desc, tables=False, sizes=None):
+    lib = _lib.load()
+    sz = sizes or _lib.MaskSizes()
+    tabs = _lib.MaskTablesC() if tables else None
+    return lib.attn_mask_compile(ctypes.byref(desc) if desc else None,
+                                 ctypes.byref(sz), ctypes.byref(tabs) if tabs else None)
+
+
+def test_mask_compile_errors():
+    lib = _lib.load()
+    assert lib.attn_mask_compile(None, None, None) == 1
+    bad = [
+        _lib.MaskDesc(-1, 10, 4, 4, 0, -1, -1, None, None),
+        _lib.MaskDesc(10, 10, 0, 4, 0, -1, -1, None, None),
+        _lib.MaskDesc(10, 10, 4, -3, 0, -1, -1, None, None),
+        _lib.MaskDesc(10, 10, 4, 4, 2, -1, -1, None, None),
+        _lib.MaskDesc(10, 10, 4, 4, 0, -2, -1, None, None),
+        _lib.MaskDesc(10, 10, 4, 4, 0, -1, -7, None, None),
+    ]
+    for d in bad:
+        assert _compile_raw(d) == 1
+        assert lib.splash_last_error()
+    seg = np.zeros(10, np.int32)
+    d = _lib.MaskDesc(10, 12, 4, 4, 0, -1, -1, seg.ctypes.data_as(ctypes.c_void_p), None)
+    assert _compile_raw(d) == 1     # seg_kv NULL needs L_kv == L_q
+    d = _lib.MaskDesc(10, 10, 4, 4, 0, -1, -1, None, seg.ctypes.data_as(ctypes.c_void_p))
+    assert _compile_raw(d) == 1     # seg_kv without seg_q
+    # Phase 2 with sizes that do not belong to this mask.
+    d = _lib.MaskDesc(64, 64, 8, 8, 1, -1, -1, None, None)
+    sizes = _lib.MaskSizes(8, 8, 1, 1, 1)
+    assert _compile_raw(d, tables=True, sizes=sizes) == 2
+    assert b"do not match" in lib.splash_last_error()
+
+
+def test_fwd_tile_errors_and_values():
+    lib = _lib.load()
+    a, b = ctypes.c_int32(), ctypes.c_int32()
+    assert lib.splash_fwd_tile(7, 128, 128, ctypes.byref(a), ctypes.byref(b)) == 3
+    assert lib.splash_fwd_tile(1, 96, 128, ctypes.byref(a), ctypes.byref(b)) == 4
+    assert lib.splash_fwd_tile(0, 192, 128, ctypes.byref(a), ctypes.byref(b)) == 4
+    assert lib.splash_fwd_tile(1, 128, 128, None, ctypes.byref(b)) == 1
+    assert fwd_tile("bf16", 128, 128) == (128, 64)
+    assert fwd_tile("bf16", 192, 128) == (128, 64)
+    assert fwd_tile("f32", 64, 64) == (64, 64)
+
+
+def _good_args(**over):
+    """Arguments that pass validation (with fake, aligned device pointers);
+    each test changes one field so that validation must reject it before
+    any pointer is used."""
+    fake = 0x10000
+    a = dict(dtype=1, B=1, Hq=2, Hkv=1, L=256, d_qk=128, d_v=128,
+             q=fake, k=fake, v=fake, o=fake, lse=None,
+             causal=1, window_left=-1, window_right=-1, seg_q=None, seg_kv=None,
+             block_q=128, block_kv=64, n_q_blocks=2, n_active=3, n_patterns=1,
+             row_ptr=fake, row_order=fake, active_cols=fake, block_code=fake,
+             mask_next=fake, partial_mask_blocks=fake, mask_mode=0,
+             scale=0.088, soft_cap=0.0)
+    a.update(over)
+    return _lib.FwdArgs(**a)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(dtype=5), 3),
+    (dict(B=-1), 1),
+    (dict(Hkv=0), 1),
+    (dict(Hq=3, Hkv=2), 2),
+    (dict(d_qk=96), 4),
+    (dict(dtype=0, d_qk=192), 4),
+    (dict(causal=3), 1),
+    (dict(window_left=-2), 1),
+    (dict(mask_mode=9), 1),
+    (dict(scale=0.0), 1),
+    (dict(scale=-1.0), 1),
+    (dict(scale=math.nan), 1),
+    (dict(scale=math.inf), 1),
+    (dict(soft_cap=math.nan), 1),
+    (dict(soft_cap=math.inf), 1),
+    (dict(block_kv=32), 2),
+    (dict(n_q_blocks=3), 2),
+    (dict(q=None), 1),
+    (dict(o=0x10008), 1),
+    (dict(row_ptr=None), 1),
+    (dict(active_cols=None), 1),
+    (dict(mask_mode=1, mask_next=None), 1),
+    (dict(seg_kv=0x10000), 1),
+    (dict(n_active=-1), 1),
+])
+def test_forward_validation_errors(over, code):
+    lib = _lib.load()
+    args = _good_args(**over)
+    assert lib.splash_attn_fwd(ctypes.byref(args), None) == code
+    assert len(lib.splash_last_error()) > 0
+
+
+def test_forward_null_args_and_noops():
+    lib = _lib.load()
+    assert lib.splash_attn_fwd(None, None) == 1
+    # B == 0, Hq == 0 or L == 0 is valid and launches nothing.
+    assert lib.splash_attn_fwd(ctypes.byref(_good_args(B=0)), None) == 0
+    assert lib.splash_attn_fwd(ctypes.byref(_good_args(Hq=0)), None) == 0
+    assert lib.splash_attn_fwd(ctypes.byref(_good_args(L=0, n_q_blocks=0)), None) == 0
+    assert lib.splash_last_error() == b""
