@@ -48,9 +48,17 @@ def common_flags():
     ]
 
 
+# Per-source extra flags.  The bf16 kernel never produces NaN inside the
+# softmax (masked scores are -inf, all other values finite), so it is built
+# without IEEE NaN canonicalisation: fmaxf becomes a bare v_max3_f32.
+EXTRA_FLAGS = {
+    "splash_fwd_bf16.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
+}
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *common_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *common_flags(), *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".hip"):
         cmd[1:1] = ["-x", "hip"]
     if verbose:

@@ -111,11 +111,11 @@ extern "C" int splash_attn_fwd(const splash_fwd_args* args, void* stream) {
     return splash::fail(SPLASH_EINVAL, "splash_attn_fwd: q/k/v/o must be 16-byte aligned");
   if (!a.row_ptr || !a.row_order)
     return splash::fail(SPLASH_EINVAL, "splash_attn_fwd: NULL row_ptr or row_order");
-  if (a.n_active > 0 && (!a.active_cols || !a.block_code))
-    return splash::fail(SPLASH_EINVAL, "splash_attn_fwd: NULL active_cols or block_code");
-  if (a.mask_mode == SPLASH_MASK_STORED && a.n_active > 0 &&
-      (!a.mask_next || (a.n_patterns > 0 && !a.partial_mask_blocks)))
-    return splash::fail(SPLASH_EINVAL, "splash_attn_fwd: stored mask mode needs mask_next and patterns");
+  if (a.n_active > 0 && (!a.active_cols || !a.block_code || !a.mask_next))
+    return splash::fail(SPLASH_EINVAL, "splash_attn_fwd: NULL active_cols, block_code or mask_next");
+  if (a.mask_mode == SPLASH_MASK_STORED && a.n_active > 0 && a.n_patterns > 0 &&
+      !a.partial_mask_blocks)
+    return splash::fail(SPLASH_EINVAL, "splash_attn_fwd: stored mask mode needs partial_mask_blocks");
 
   splash::FwdParams p{};
   p.q = a.q;

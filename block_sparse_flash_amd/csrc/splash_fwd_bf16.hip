@@ -90,7 +90,10 @@ struct Cfg {
   static constexpr int VTILE = BN * VROW;      // bytes per V tile
   static constexpr int KCHUNKS = KTILE / 16;   // 16-byte chunks per K tile
   static constexpr int VCHUNKS = VTILE / 16;
-  static constexpr int LDS_BYTES = 2 * (KTILE + VTILE);
+  static constexpr int NBUF = 3;                // tile buffers per operand
+  static constexpr int LDS_BYTES = NBUF * (KTILE + VTILE);
+  static constexpr int KLOADS = KCHUNKS / NT;   // tile-load instructions per wave
+  static constexpr int VLOADS = VCHUNKS / NT;
   static_assert(KCHUNKS % NT == 0 && VCHUNKS % NT == 0, "tile chunks split over 256 threads");
 };
 
@@ -115,6 +118,54 @@ __device__ __forceinline__ void sfor(F&& f) {
 }
 #define SIDX(tag) decltype(tag)::value
 
+// One 16-byte-per-lane HBM -> LDS copy: lane i's 16 bytes at byte offset
+// voff of the buffer land at LDS address lds_addr + 16 i.  Issued as inline
+// assembly so that the compiler does not treat later LDS reads of *other*
+// buffers as dependent on it; completion is tracked explicitly with vmcnt.
+// M0 (the LDS base of the copy) is saved and restored around it.
+__device__ __forceinline__ void dma16(u32x4 rsrc, uint32_t lds_addr, int voff) {
+  const uint32_t base = (uint32_t)__builtin_amdgcn_readfirstlane(lds_addr);
+  const u32x4 rs = {(uint32_t)__builtin_amdgcn_readfirstlane(rsrc[0]),
+                    (uint32_t)__builtin_amdgcn_readfirstlane(rsrc[1]),
+                    (uint32_t)__builtin_amdgcn_readfirstlane(rsrc[2]),
+                    (uint32_t)__builtin_amdgcn_readfirstlane(rsrc[3])};
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(base), "v"(voff), "s"(rs)
+      : "memory");
+}
+
+// Wait until at most N tile copies of this wave are in flight and all LDS
+// reads are done, then synchronise the work-group.
+template <int N>
+__device__ __forceinline__ void wait_copies_and_barrier() {
+  static_assert(N >= 0 && N <= 6, "vmcnt immediate");
+  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  if constexpr (N == 1) asm volatile("s_waitcnt vmcnt(1) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  if constexpr (N == 2) asm volatile("s_waitcnt vmcnt(2) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  if constexpr (N == 3) asm volatile("s_waitcnt vmcnt(3) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  if constexpr (N == 5) asm volatile("s_waitcnt vmcnt(5) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  if constexpr (N == 6) asm volatile("s_waitcnt vmcnt(6) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Read-only table entry through the constant address space: with a
+// wave-uniform index this is a scalar load (lgkmcnt, not vmcnt).
+template <typename T>
+__device__ __forceinline__ T ld_table(const T* base, int i) {
+  return ((const __attribute__((address_space(4))) T*)base)[__builtin_amdgcn_readfirstlane(i)];
+}
+
+__device__ __forceinline__ u32x4 make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return u32x4{(uint32_t)a, (uint32_t)(a >> 32), bytes, (uint32_t)kRsrcWord3};
+}
+
 template <int DQK, int DV, bool CAP>
 __global__ __launch_bounds__(NT) void splash_fwd_bf16_kernel(FwdParams p) {
   using C = Cfg<DQK, DV>;
@@ -122,9 +173,9 @@ __global__ __launch_bounds__(NT) void splash_fwd_bf16_kernel(FwdParams p) {
   constexpr int DT = C::DT;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   lds_u8* lds = (lds_u8*)smem;  // address-space cast to LDS
-  // Layout: [K buf 0][K buf 1][V buf 0][V buf 1]
+  // Layout: [K buf 0..2][V buf 0..2]; block x lives in buffer x % 3.
   auto kbuf = [&](int i) { return lds + i * C::KTILE; };
-  auto vbuf = [&](int i) { return lds + 2 * C::KTILE + i * C::VTILE; };
+  auto vbuf = [&](int i) { return lds + C::NBUF * C::KTILE + i * C::VTILE; };
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -138,7 +189,7 @@ __global__ __launch_bounds__(NT) void splash_fwd_bf16_kernel(FwdParams p) {
   const int hq = head - b * p.Hq;
   const int kvh = b * p.Hkv + hq / p.group;
   const int L = p.L;
-  const int r = p.row_order[rank];
+  const int r = ld_table(p.row_order, rank);
   const int qw = r * BM + wave * 64;  // first query row of this wave
 
   const uint16_t* qg = static_cast<const uint16_t*>(p.q) + (int64_t)head * L * DQK;
@@ -147,10 +198,8 @@ __global__ __launch_bounds__(NT) void splash_fwd_bf16_kernel(FwdParams p) {
   // Buffer resources: reads past the sequence end return zero.
   const __amdgpu_buffer_rsrc_t qrs =
       __builtin_amdgcn_make_buffer_rsrc((void*)qg, (short)0, L * DQK * 2, kRsrcWord3);
-  const __amdgpu_buffer_rsrc_t krs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)kg, (short)0, L * DQK * 2, kRsrcWord3);
-  const __amdgpu_buffer_rsrc_t vrs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)vg, (short)0, L * DV * 2, kRsrcWord3);
+  const u32x4 krs = make_rsrc(kg, (uint32_t)(L * DQK * 2));
+  const u32x4 vrs = make_rsrc(vg, (uint32_t)(L * DV * 2));
 
   // Zero both tile buffers once so that a stale buffer read by the
   // pipeline's edge steps holds finite values.
@@ -179,7 +228,7 @@ __global__ __launch_bounds__(NT) void splash_fwd_bf16_kernel(FwdParams p) {
       const int row = slot / (DQK / 8);
       const int pc = slot - row * (DQK / 8);
       const int off = ((k0 + row) * DQK + kswz(row, pc) * 8) * 2;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(kbuf(buf) + slot0 * 16), 16, off, 0, 0, 0);
+      dma16(krs, (uint32_t)(uintptr_t)(kbuf(buf) + slot0 * 16), off);
     }
   };
   auto load_v = [&](int c, int buf) __attribute__((always_inline)) {
@@ -191,7 +240,7 @@ __global__ __launch_bounds__(NT) void splash_fwd_bf16_kernel(FwdParams p) {
       const int row = slot / (DV / 8);
       const int pc = slot - row * (DV / 8);
       const int off = ((k0 + row) * DV + vswz(row, pc) * 8) * 2;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(vbuf(buf) + slot0 * 16), 16, off, 0, 0, 0);
+      dma16(vrs, (uint32_t)(uintptr_t)(vbuf(buf) + slot0 * 16), off);
     }
   };
 
@@ -221,8 +270,8 @@ __global__ __launch_bounds__(NT) void splash_fwd_bf16_kernel(FwdParams p) {
   const int qa = qw;
   const int qb = min(qw + 63, L - 1);
 
-  const int g0 = p.row_ptr[r];
-  const int n = p.row_ptr[r + 1] - g0;
+  const int g0 = ld_table(p.row_ptr, r);
+  const int n = ld_table(p.row_ptr, r + 1) - g0;
   const int32_t* cols = p.active_cols + g0;
 
   // V^T transposed reads: lane j of 16-lane group G supplies row
@@ -278,7 +327,7 @@ __global__ __launch_bounds__(NT) void splash_fwd_bf16_kernel(FwdParams p) {
     const int ka = c * BN;
     const int kz = ka + BN - 1;
     if (p.mask_stored) {
-      const uint8_t* pat = p.patterns + (int64_t)p.mask_next[g0 + g] * (BM * BN);
+      const uint8_t* pat = p.patterns + (int64_t)ld_table(p.mask_next, g0 + g) * (BM * BN);
       sfor<0, 8>([&](auto i_) {
         constexpr int a = SIDX(i_) / 4;
         constexpr int q4 = SIDX(i_) % 4;
@@ -322,15 +371,26 @@ __global__ __launch_bounds__(NT) void splash_fwd_bf16_kernel(FwdParams p) {
   };
 
 
-  if (n > 0) {
-    load_k(cols[0], 0);
-    if (n > 1) load_k(cols[1], 1);
-  }
+  // Block x's K and V tiles live in buffer x % 3.  Copies run two steps
+  // ahead: step j issues K_{j+3} and V_{j+1} and, before its closing barrier,
+  // waits only for the copies issued one step earlier (K_{j+2}, V_j).
+  // Past the end of the row the copies repeat the last block (same count
+  // every step, landing in a buffer nobody reads).
+  constexpr int NL = C::KLOADS + C::VLOADS;  // copy instructions per wave per step
+  // Column of block x (clamped); the index is made provably wave-uniform so
+  // the read is a scalar load, which does not wait behind the tile copies.
+  auto colc = [&](int x) { return ld_table(cols, min(x, n - 1)); };
   // P of the (non-existent) block before the first: zero.
   sfor<0, 4>([&](auto i_) { pb[1][SIDX(i_) / 2][SIDX(i_) % 2] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u}); });
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (n > 0) compute_s(sacc[0], 0);
+  if (n > 0) {
+    load_k(cols[0], 0);
+    load_k(colc(1), 1);
+    wait_copies_and_barrier<0>();
+    compute_s(sacc[0], 0);
+    wait_copies_and_barrier<0>();  // every wave is done with K buffer 0
+    load_k(colc(2), 2);
+    load_v(cols[0], 0);
+  }
 
   // Iteration j: issue loads of K_{j+2} (buffer j%2) and V_j (buffer j%2);
   // softmax(S_j) on the vector unit while the matrix unit computes S_{j+1}
@@ -346,60 +406,73 @@ __global__ __launch_bounds__(NT) void splash_fwd_bf16_kernel(FwdParams p) {
   auto step = [&](int j, auto cur_tag) __attribute__((always_inline)) {
     constexpr int cur = decltype(cur_tag)::value;
     constexpr int nxt = cur ^ 1;
-    const int c = cols[j];
-    if (j + 2 < n) load_k(cols[j + 2], j & 1);
-    load_v(c, j & 1);
-    if (p.block_code[g0 + j] == 1) apply_mask(sacc[cur], j, c);
+    const int c = colc(j);
+    // Partial block <=> it has a pattern (mask_next >= 0); int32, so a scalar load.
+    if (ld_table(p.mask_next, g0 + j) >= 0) apply_mask(sacc[cur], j, c);
+    const int jm = j % 3;
+    const int jm1 = jm == 2 ? 0 : jm + 1;   // (j + 1) % 3
+    const int jm2 = jm1 == 2 ? 0 : jm1 + 1; // (j + 2) % 3 == (j - 1) % 3
+    load_k(colc(j + 3), jm);
+    load_v(colc(j + 1), jm1);
 
-    const lds_u8* kb = kbuf((j + 1) & 1);
-    const lds_u8* vb = vbuf((j + 1) & 1);
-    bf16x8 kf[KS];
-    sfor<0, KS>([&](auto s_) {
-      constexpr int s = SIDX(s_);
-      kf[s] = *reinterpret_cast<const lds_bf16x8*>(kb + l32 * C::KROW + kswz(l32, 2 * s + hi) * 16);
-    });
-    bf16x8 vf[2 * DT];
-    sfor<0, 2 * DT>([&](auto i_) {
-      constexpr int dt = SIDX(i_) / 2;
-      constexpr int c2 = SIDX(i_) % 2;
-      const int row = 16 * c2 + vrow0;
-      const int row2 = row + 8;
-      const int lc = 4 * dt + 2 * (grp & 1) + ((jj & 3) >> 1);
-      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_i16x4*)(vb + row * C::VROW + vswz(row, lc) * 16 + 8 * (jj & 1)));
-      const i16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_i16x4*)(vb + row2 * C::VROW + vswz(row2, lc) * 16 + 8 * (jj & 1)));
-      const u32x2 lo2 = __builtin_bit_cast(u32x2, lo);
-      const u32x2 up2 = __builtin_bit_cast(u32x2, up);
-      vf[SIDX(i_)] = __builtin_bit_cast(bf16x8, u32x4{lo2[0], lo2[1], up2[0], up2[1]});
-    });
+    const lds_u8* kb = kbuf(jm1);   // K_{j+1}
+    const lds_u8* vb = vbuf(jm2);   // V_{j-1}
+
+    // Operand fragments: frag f < KS is K k-step f (B of S^T); frag KS + i is
+    // V^T for (d-tile i/2, key half i%2).  Frag f feeds MFMAs 2f and 2f+1
+    // (one per q-tile) and is read from LDS LA frags (2 LA MFMAs) ahead.
+    constexpr int NF = KS + 2 * DT;
+    constexpr int LA = 2;
+    bf16x8 frag[NF];
+    auto read_frag = [&](auto f_) __attribute__((always_inline)) {
+      constexpr int f = SIDX(f_);
+      if constexpr (f < KS) {
+        frag[f] = *reinterpret_cast<const lds_bf16x8*>(kb + l32 * C::KROW + kswz(l32, 2 * f + hi) * 16);
+      } else {
+        constexpr int dt = (f - KS) / 2;
+        constexpr int c2 = (f - KS) % 2;
+        const int row = 16 * c2 + vrow0;
+        const int row2 = row + 8;
+        const int lc = 4 * dt + 2 * (grp & 1) + ((jj & 3) >> 1);
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(vb + row * C::VROW + vswz(row, lc) * 16 + 8 * (jj & 1)));
+        const i16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(vb + row2 * C::VROW + vswz(row2, lc) * 16 + 8 * (jj & 1)));
+        const u32x2 lo2 = __builtin_bit_cast(u32x2, lo);
+        const u32x2 up2 = __builtin_bit_cast(u32x2, up);
+        frag[f] = __builtin_bit_cast(bf16x8, u32x4{lo2[0], lo2[1], up2[0], up2[1]});
+      }
+    };
+    sfor<0, LA>(read_frag);
 
     // MFMA m: S_{j+1} for m < 2 KS (k-step m/2, q-tile m%2), then
-    // P_{j-1} V_{j-1} (d-tile, key half c2, q-tile).
+    // P_{j-1} V_{j-1} (d-tile, key half c2, q-tile).  Before the first MFMA
+    // of a frag, the frag LA ahead is requested from LDS.
     auto issue = [&](auto m_) __attribute__((always_inline)) {
       constexpr int m = SIDX(m_);
+      constexpr int f = m / 2;
+      if constexpr (m % 2 == 0 && f + LA < NF) read_frag(Idx<f + LA>{});
       if constexpr (m < 2 * KS) {
-        constexpr int s = m / 2;
         constexpr int a = m % 2;
-        if constexpr (s == 0) {
+        if constexpr (f == 0) {
           const f32x16 zero = {};
-          sacc[nxt][a] = mfma(kf[0], qf[a][0], zero);
+          sacc[nxt][a] = mfma(frag[0], qf[a][0], zero);
         } else {
-          sacc[nxt][a] = mfma(kf[s], qf[a][s], sacc[nxt][a]);
+          sacc[nxt][a] = mfma(frag[f], qf[a][f], sacc[nxt][a]);
         }
       } else {
         constexpr int mm = m - 2 * KS;
         constexpr int dt = mm / 4;
         constexpr int c2 = (mm / 2) % 2;
         constexpr int a = mm % 2;
-        oacc[a][dt] = mfma(vf[2 * dt + c2], pb[nxt][a][c2], oacc[a][dt]);
+        oacc[a][dt] = mfma(frag[f], pb[nxt][a][c2], oacc[a][dt]);
       }
     };
 
     f32x16* sv = sacc[cur];
     float alpha[2], mx[2], mc[2];
     float ps[2] = {0.0f, 0.0f};
-    u32x4 w[2][2];
+    u32x4 w[2][2];  // packed bf16 pairs of P, per q-tile and key half
     auto slice = [&](auto i_) __attribute__((always_inline)) {
       constexpr int i0 = SIDX(i_);
       constexpr int cap_slices = CAP ? 4 : 0;
@@ -472,8 +545,7 @@ __global__ __launch_bounds__(NT) void splash_fwd_bf16_kernel(FwdParams p) {
         oacc[a][dt] *= alpha[a];
       });
     }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    wait_copies_and_barrier<NL>();
   };
 
   for (int j = 0; j < n; j += 2) {
@@ -483,10 +555,11 @@ __global__ __launch_bounds__(NT) void splash_fwd_bf16_kernel(FwdParams p) {
   // Last block's P V (V_{n-1} landed before the final barrier).
   if (n > 0) {
     if ((n - 1) & 1)
-      compute_pv(pb[1], 1);
+      compute_pv(pb[1], (n - 1) % 3);
     else
-      compute_pv(pb[0], 0);
+      compute_pv(pb[0], (n - 1) % 3);
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the trailing copies
 
   // Epilogue: o = O / l, lse = (m zc + log2 l) ln 2.
   sfor<0, 2>([&](auto a_) {

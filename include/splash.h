@@ -195,7 +195,8 @@ typedef struct splash_fwd_args {
   const int32_t* row_order;    /* device [n_q_blocks] */
   const int32_t* active_cols;  /* device [n_active] */
   const int8_t* block_code;    /* device [n_active] */
-  const int32_t* mask_next;    /* device [n_active] (SPLASH_MASK_STORED) */
+  const int32_t* mask_next;    /* device [n_active]; also marks partial blocks
+                                  (>= 0) for the kernels */
   const uint8_t* partial_mask_blocks; /* device [n_patterns, block_q,
                                          block_kv] (SPLASH_MASK_STORED) */
   int32_t mask_mode;     /* splash_mask_mode */

@@ -182,7 +182,8 @@ def _good_args(**over):
     (dict(o=0x10008), 1),
     (dict(row_ptr=None), 1),
     (dict(active_cols=None), 1),
-    (dict(mask_mode=1, mask_next=None), 1),
+    (dict(mask_next=None), 1),
+    (dict(mask_mode=1, partial_mask_blocks=None), 1),
     (dict(seg_kv=0x10000), 1),
     (dict(n_active=-1), 1),
 ])
