@@ -109,6 +109,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--mask-mode", default="computed", choices=["computed", "stored"])
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after timing, run one device-to-device copy of this many MiB "
+                         "(a plain copy of known size, for scaling HBM counters)")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for cpu_baseline (0: skip)")
     args = ap.parse_args()
@@ -196,6 +199,14 @@ def main():
                      "frac": round(tflops / peak, 4), "traffic": traffic},
         "cpu_baseline": cpu,
     }
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib * (1 << 20)
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        rec["copy_calibration_bytes"] = n
     print(json.dumps(rec), flush=True)
 
 

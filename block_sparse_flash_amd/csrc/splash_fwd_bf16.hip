@@ -316,7 +316,6 @@ void splash_fwd_bf16_kernel(FwdParams p) {
     }
   };
 
-  constexpr int NL = C::KLOADS + C::VLOADS;  // copy instructions per wave per block
   if (n > 0) {
     load_k(cols[0], 0);
     load_v(cols[0], 0);
@@ -324,12 +323,14 @@ void splash_fwd_bf16_kernel(FwdParams p) {
 
   for (int j = 0; j < n; ++j) {
     const int buf = j & 1;
-    // Copy block j+1 into the other buffers (the last block is repeated past
-    // the end so every iteration issues the same number of copies), then wait
-    // for block j's copies and make them visible to the work-group.
-    load_k(colc(j + 1), buf ^ 1);
-    load_v(colc(j + 1), buf ^ 1);
-    wait_copies_and_barrier<NL>();
+    // Block j's copies (issued one iteration earlier) have landed and every
+    // wave is past iteration j-1, so buffer buf^1 is free: copy block j+1
+    // into it while block j is computed.
+    wait_copies_and_barrier<0>();
+    if (j + 1 < n) {
+      load_k(colc(j + 1), buf ^ 1);
+      load_v(colc(j + 1), buf ^ 1);
+    }
 
     const lds_u8* kb = kbuf(buf);
     const lds_u8* vb = vbuf(buf);
@@ -419,11 +420,7 @@ void splash_fwd_bf16_kernel(FwdParams p) {
         oacc[dt] = mfma(vf, pb[t][c2], oacc[dt]);
       });
     });
-    // Every wave is done reading buffer `buf` before the next iteration's
-    // copies overwrite it.
-    wait_copies_and_barrier<NL>();
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the trailing copies
 
   // Epilogue: o = O / l, lse = (m zc + log2 l) ln 2.
   const float lt = lsum + __shfl_xor(lsum, 32);
