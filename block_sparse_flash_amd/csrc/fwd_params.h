@@ -42,7 +42,7 @@ hipError_t launch_fwd_bf16(const FwdParams& p, int d_qk, int d_v, hipStream_t s)
 // Block sizes used by each kernel family.
 constexpr int kF32BlockQ = 64;
 constexpr int kF32BlockKV = 64;
-constexpr int kBf16BlockQ = 128;
+constexpr int kBf16BlockQ = 256;
 constexpr int kBf16BlockKV = 64;
 
 // Number of XCDs of an MI355X; consecutive work-group ids are dispatched

@@ -12,11 +12,18 @@
 // page, "LSE and online softmax").
 //
 // gfx950 design (this file's own; the pages' TPU kernel is prior art):
-//   * One work-group = 4 waves = a 128-query block of one head; each wave owns
-//     32 query rows.  Registers stay within 256 per lane and LDS within 80 KiB
-//     per work-group, so two work-groups share a CU and each SIMD runs two
-//     waves: the matrix pipe of one wave overlaps the softmax of the other
-//     (section 5.3: the vector work must hide behind the matrix work).
+//   * One work-group = 8 waves = a 256-query block of one head; each wave owns
+//     32 query rows.  Registers stay within 256 per lane, so the work-group
+//     fills a CU with two waves per SIMD (waves w and w + 4 share a SIMD).
+//     Every K/V tile copied into LDS serves 256 queries.
+//   * Ping-pong schedule (default loop): waves 0-3 and 4-7 form two groups
+//     with one wave per SIMD each.  They alternate, one barrier apart, between
+//     a matrix phase (O += P V of the previous block, S = Q K^T of this one)
+//     and a softmax phase, so on every SIMD one wave feeds the matrix pipe
+//     while the other uses the vector unit (section 5.3: the vector work must
+//     hide behind the matrix work).  On gfx950 a matrix-only wave and a
+//     vector-only wave overlap almost perfectly, while one wave mixing both
+//     does not.
 //   * The work-group walks its row's active blocks (CSR list), 64 keys per
 //     block.  Scores are computed transposed, S^T = K Q^T, on
 //     v_mfma_f32_32x32x16_bf16 as two 32-key tiles (two independent
@@ -29,19 +36,20 @@
 //     which returns four consecutive keys of one head dim per lane - the key
 //     grouping the accumulator layout implies.
 //   * K/V tiles stream HBM -> LDS with buffer_load ... lds (rows past the
-//     sequence end read as zero) one block ahead into the other of two
-//     buffers (section 3.1), waited with vmcnt before one barrier per block.
-//     LDS rows are XOR-swizzled in 16-byte chunks so both the K operand reads
-//     and the transposing V reads are bank-conflict free.
+//     sequence end read as zero) into double buffers (section 3.1).  LDS rows
+//     are XOR-swizzled in 16-byte chunks so that both the K operand reads and
+//     the transposing V reads are bank-conflict free at 256 bytes per clock.
 //   * exp is the hardware exp2 with log2(e) folded into the scale (6.6
 //     "use_base2_exp").  The reference max used in the exponent only moves
 //     when a row's block max exceeds it by more than 2^8; the constant cancels
 //     in o / l (section 5.4: any constant that keeps exp in range gives the
-//     same softmax), so almost every block skips the O rescale.
+//     same softmax), so almost every block skips the O rescale, and P is
+//     computed with the current reference while the block max is reduced.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include "fwd_params.h"
 
@@ -60,9 +68,10 @@ typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int BM = kBf16BlockQ;   // 128 queries per work-group
+constexpr int BM = kBf16BlockQ;   // 256 queries per work-group
 constexpr int BN = kBf16BlockKV;  // 64 keys per block
-constexpr int NT = 256;           // 4 waves
+constexpr int NW = BM / 32;       // 8 waves of 32 query rows
+constexpr int NT = 64 * NW;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kTau = 8.0f;      // log2 of the largest p allowed before a rescale
@@ -93,13 +102,35 @@ struct Cfg {
   static constexpr int LDS_BYTES = NBUF * (KTILE + VTILE);
   static constexpr int KLOADS = KCHUNKS / NT;  // tile-copy instructions per wave
   static constexpr int VLOADS = VCHUNKS / NT;
-  static_assert(KCHUNKS % NT == 0 && VCHUNKS % NT == 0, "tile chunks split over 256 threads");
-  static_assert(LDS_BYTES <= 81920, "two work-groups per CU");
+  static_assert(KCHUNKS % NT == 0 && VCHUNKS % NT == 0, "tile chunks split evenly over the work-group");
+  static_assert(LDS_BYTES <= 163840, "fits the LDS of a CU");
 };
 
-// Physical 16-byte chunk of logical chunk c in LDS row r.
-__device__ __forceinline__ int kswz(int r, int c) { return c ^ (r & 7); }
-__device__ __forceinline__ int vswz(int r, int c) { return c ^ (2 * (r & 3)); }
+// Physical 16-byte chunk of logical chunk c in LDS row r (an involution
+// that stays inside the row).  The gfx950 LDS serves 256 bytes (64 banks)
+// per clock: a ds_read_b128 takes 16 lanes per clock, which read 16
+// consecutive K rows at one logical chunk, and a ds_read_b64_tr_b16 takes
+// 32 lanes, which read 64 bytes from each of 4 consecutive V rows.  The XOR
+// spreads each of those groups over all 64 banks:
+//   K, 256-byte rows: chunk ^ (r & 15);   K, 128/384-byte rows: rows pair up
+//   in bank halves, chunk ^ ((r >> 1) & 7);
+//   V, 256-byte rows: 64-byte group ^ (r & 3);  V, 128-byte rows: chunk ^ 2(r & 3).
+template <int ROWB>
+__device__ __forceinline__ int kswz(int r, int c) {
+  static_assert(ROWB % 128 == 0 && ROWB >= 128, "K rows are 128-byte multiples");
+  if constexpr (ROWB % 256 == 0)
+    return c ^ (r & 15);
+  else
+    return c ^ ((r >> 1) & 7);
+}
+template <int ROWB>
+__device__ __forceinline__ int vswz(int r, int c) {
+  static_assert(ROWB == 128 || ROWB == 256, "V rows are 128 or 256 bytes");
+  if constexpr (ROWB == 256)
+    return c ^ (4 * (r & 3));
+  else
+    return c ^ (2 * (r & 3));
+}
 
 // Compile-time register-buffer index (keeps the double-buffered accumulator
 // arrays statically indexed).
@@ -155,12 +186,34 @@ __device__ __forceinline__ T ld_table(const T* base, int i) {
   return ((const __attribute__((address_space(4))) T*)base)[__builtin_amdgcn_readfirstlane(i)];
 }
 
+// The value of lane 0 in every lane, held in scalar registers.
+__device__ __forceinline__ u32x4 uniform(u32x4 v) {
+  return u32x4{(uint32_t)__builtin_amdgcn_readfirstlane((int)v[0]), (uint32_t)__builtin_amdgcn_readfirstlane((int)v[1]),
+               (uint32_t)__builtin_amdgcn_readfirstlane((int)v[2]), (uint32_t)__builtin_amdgcn_readfirstlane((int)v[3])};
+}
+
 __device__ __forceinline__ u32x4 make_rsrc(const void* base, uint32_t bytes) {
   const uint64_t a = reinterpret_cast<uint64_t>(base);
   return u32x4{(uint32_t)a, (uint32_t)(a >> 32), bytes, (uint32_t)kRsrcWord3};
 }
 
-template <int DQK, int DV, bool CAP>
+// Issue order of the matrix phase: the O MFMAs (NP of them) and the score
+// MFMAs (NQ) alternate, score first, so consecutive MFMAs never feed the
+// same accumulator; the longer list finishes the sequence.
+template <int NP, int NQ>
+struct MatOrder {
+  static constexpr int NMIN = NP < NQ ? NP : NQ;
+  static constexpr int N = NP + NQ;
+  static constexpr bool is_s(int m) { return m < 2 * NMIN ? (m % 2 == 0) : (NQ > NP); }
+  static constexpr int idx(int m) { return m < 2 * NMIN ? m / 2 : NMIN + (m - 2 * NMIN); }
+};
+
+// Wait for this wave's LDS reads, then synchronise the work-group.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int DQK, int DV, bool CAP, int LOOP>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void splash_fwd_bf16_kernel(FwdParams p) {
   using C = Cfg<DQK, DV>;
@@ -173,7 +226,7 @@ void splash_fwd_bf16_kernel(FwdParams p) {
   auto vbuf = [&](int i) { return lds + C::NBUF * C::KTILE + i * C::VTILE; };
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
@@ -192,10 +245,13 @@ void splash_fwd_bf16_kernel(FwdParams p) {
   const uint16_t* kg = static_cast<const uint16_t*>(p.k) + (int64_t)kvh * L * DQK;
   const uint16_t* vg = static_cast<const uint16_t*>(p.v) + (int64_t)kvh * L * DV;
   // Buffer resources: reads past the sequence end return zero.
-  const __amdgpu_buffer_rsrc_t qrs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)qg, (short)0, L * DQK * 2, kRsrcWord3);
-  const u32x4 krs = make_rsrc(kg, (uint32_t)(L * DQK * 2));
-  const u32x4 vrs = make_rsrc(vg, (uint32_t)(L * DV * 2));
+  const uint64_t qaddr = reinterpret_cast<uint64_t>(qg);
+  const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(qaddr >> 32)) << 32) |
+              (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)qaddr)),
+      (short)0, __builtin_amdgcn_readfirstlane(L * DQK * 2), kRsrcWord3);
+  const u32x4 krs = uniform(make_rsrc(kg, (uint32_t)(L * DQK * 2)));
+  const u32x4 vrs = uniform(make_rsrc(vg, (uint32_t)(L * DV * 2)));
 
   // Zero the tile buffers once: a tile that hangs over the sequence end is
   // then finite everywhere (its masked keys get zero weight).
@@ -218,11 +274,11 @@ void splash_fwd_bf16_kernel(FwdParams p) {
     const int k0 = c * BN;
 #pragma unroll
     for (int t = 0; t < C::KLOADS; ++t) {
-      const int slot0 = (t * 4 + wave) * 64;
+      const int slot0 = (t * NW + wave) * 64;
       const int slot = slot0 + lane;
       const int row = slot / (DQK / 8);
       const int pc = slot - row * (DQK / 8);
-      const int off = ((k0 + row) * DQK + kswz(row, pc) * 8) * 2;
+      const int off = ((k0 + row) * DQK + kswz<C::KROW>(row, pc) * 8) * 2;
       dma16(krs, (uint32_t)(uintptr_t)(kbuf(buf) + slot0 * 16), off);
     }
   };
@@ -230,11 +286,11 @@ void splash_fwd_bf16_kernel(FwdParams p) {
     const int k0 = c * BN;
 #pragma unroll
     for (int t = 0; t < C::VLOADS; ++t) {
-      const int slot0 = (t * 4 + wave) * 64;
+      const int slot0 = (t * NW + wave) * 64;
       const int slot = slot0 + lane;
       const int row = slot / (DV / 8);
       const int pc = slot - row * (DV / 8);
-      const int off = ((k0 + row) * DV + vswz(row, pc) * 8) * 2;
+      const int off = ((k0 + row) * DV + vswz<C::VROW>(row, pc) * 8) * 2;
       dma16(vrs, (uint32_t)(uintptr_t)(vbuf(buf) + slot0 * 16), off);
     }
   };
@@ -316,110 +372,612 @@ void splash_fwd_bf16_kernel(FwdParams p) {
     }
   };
 
-  if (n > 0) {
-    load_k(cols[0], 0);
-    load_v(cols[0], 0);
-  }
-
-  for (int j = 0; j < n; ++j) {
-    const int buf = j & 1;
-    // Block j's copies (issued one iteration earlier) have landed and every
-    // wave is past iteration j-1, so buffer buf^1 is free: copy block j+1
-    // into it while block j is computed.
-    wait_copies_and_barrier<0>();
-    if (j + 1 < n) {
-      load_k(colc(j + 1), buf ^ 1);
-      load_v(colc(j + 1), buf ^ 1);
-    }
-
-    const lds_u8* kb = kbuf(buf);
-    const lds_u8* vb = vbuf(buf);
-
-    // S^T for the two 32-key tiles (two independent accumulation chains).
-    f32x16 sv[2];
-    sfor<0, KS>([&](auto s_) {
-      constexpr int s = SIDX(s_);
-      sfor<0, 2>([&](auto t_) {
-        constexpr int t = SIDX(t_);
-        const int key = 32 * t + l32;
-        const bf16x8 kf = *reinterpret_cast<const lds_bf16x8*>(kb + key * C::KROW + kswz(key, 2 * s + hi) * 16);
-        if constexpr (s == 0) {
-          const f32x16 zero = {};
-          sv[t] = mfma(kf, qf[0], zero);
-        } else {
-          sv[t] = mfma(kf, qf[s], sv[t]);
-        }
-      });
-    });
-
-    if constexpr (CAP) {
-      const float k2 = 2.0f * kLog2e * p.scale / p.soft_cap;
-      const float A = p.soft_cap * kLog2e;
-      sfor<0, 32>([&](auto i_) {
-        constexpr int t = SIDX(i_) / 16;
-        constexpr int e = SIDX(i_) % 16;
-        const float ex = fast_exp2(sv[t][e] * k2);
-        sv[t][e] = A - 2.0f * A * __builtin_amdgcn_rcpf(ex + 1.0f);
-      });
-    }
-    // Partial block <=> it has a pattern (mask_next >= 0); int32 scalar load.
-    if (ld_table(p.mask_next, g0 + j) >= 0) apply_mask(sv, j, colc(j));
-
-    // Row max: in-lane over 32 keys, then across the two half-waves.
-    float mx = sv[0][0];
-    sfor<1, 32>([&](auto i_) { mx = fmaxf(mx, sv[SIDX(i_) / 16][SIDX(i_) % 16]); });
-    {
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-    }
-    // Lazy reference update: move only when the block max exceeds it by > 2^kTau.
-    const bool need = mx * zc > mref * zc + kTau;
-    const float mnew = need ? mx : mref;
-    const float alpha = (mnew == mref) ? 1.0f : fast_exp2((mref - mnew) * zc);
-    mref = mnew;
-    const float mc = (mnew == -INFINITY) ? 0.0f : mnew * zc;
-
-    // p = 2^(z zc - m zc), packed as bf16 B operands: tile t, key half c2.
-    bf16x8 pb[2][2];
-    float ps = 0.0f;
-    sfor<0, 4>([&](auto i_) {
-      constexpr int t = SIDX(i_) / 2;
-      constexpr int c2 = SIDX(i_) % 2;
-      u32x4 w;
-      sfor<0, 4>([&](auto e_) {
-        constexpr int e2 = SIDX(e_);
-        const float p0 = fast_exp2(fmaf(sv[t][8 * c2 + 2 * e2], zc, -mc));
-        const float p1 = fast_exp2(fmaf(sv[t][8 * c2 + 2 * e2 + 1], zc, -mc));
-        ps += p0 + p1;
-        w[e2] = pack_bf16(p0, p1);
-      });
-      pb[t][c2] = __builtin_bit_cast(bf16x8, w);
-    });
-    lsum = lsum * alpha + ps;
-    if (__any(alpha != 1.0f)) {
-      sfor<0, DT>([&](auto i_) { oacc[SIDX(i_)] *= alpha; });
-    }
-
-    // O^T += V^T P^T; key-half-major order keeps the DT accumulators
-    // independent between consecutive MFMAs.
-    sfor<0, 4>([&](auto tc_) {
-      constexpr int t = SIDX(tc_) / 2;
-      constexpr int c2 = SIDX(tc_) % 2;
+  // ---------------------------------------------------------------------
+  // Software-pipelined loop: iteration j runs softmax(S_j) on the vector
+  // unit while the matrix unit computes O += P_{j-1} V_{j-1} and then
+  // S_{j+1} = Q K_{j+1}^T.  Block x's K and V tiles live in buffer x % 2;
+  // iteration j copies K_{j+2} and V_j (into the buffers of K_j and V_{j-2},
+  // both finished before the barrier that opens iteration j).  P_{j-1} is
+  // consumed by the first MFMAs of the iteration before P_j is written, so
+  // one register set holds P.
+  auto pipelined_loop = [&]() __attribute__((always_inline)) {
+    f32x16 sacc[2][2];   // [register buffer][key tile]: S^T of block j / j+1
+    bf16x8 pb[2][2];     // [key tile][key half]: P^T, B operands of O^T += V^T P^T
+    auto read_kfrag = [&](const lds_u8* kb, int s, int t) __attribute__((always_inline)) {
+      const int key = 32 * t + l32;
+      return *reinterpret_cast<const lds_bf16x8*>(kb + key * C::KROW + kswz<C::KROW>(key, 2 * s + hi) * 16);
+    };
+    auto read_vfrag = [&](const lds_u8* vb, int t, int c2, int dt) __attribute__((always_inline)) {
       const int row = 32 * t + 16 * c2 + vrow0;
       const int row2 = row + 8;
-      sfor<0, DT>([&](auto dt_) {
-        constexpr int dt = SIDX(dt_);
-        const int lc = 4 * dt + vcol0;
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4*)(vb + row * C::VROW + vswz(row, lc) * 16 + 8 * (jj & 1)));
-        const i16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4*)(vb + row2 * C::VROW + vswz(row2, lc) * 16 + 8 * (jj & 1)));
-        const u32x2 lo2 = __builtin_bit_cast(u32x2, lo);
-        const u32x2 up2 = __builtin_bit_cast(u32x2, up);
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{lo2[0], lo2[1], up2[0], up2[1]});
-        oacc[dt] = mfma(vf, pb[t][c2], oacc[dt]);
+      const int lc = 4 * dt + vcol0;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4*)(vb + row * C::VROW + vswz<C::VROW>(row, lc) * 16 + 8 * (jj & 1)));
+      const i16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4*)(vb + row2 * C::VROW + vswz<C::VROW>(row2, lc) * 16 + 8 * (jj & 1)));
+      const u32x2 lo2 = __builtin_bit_cast(u32x2, lo);
+      const u32x2 up2 = __builtin_bit_cast(u32x2, up);
+      return __builtin_bit_cast(bf16x8, u32x4{lo2[0], lo2[1], up2[0], up2[1]});
+    };
+
+    if (n > 0) {
+      load_k(cols[0], 0);
+      load_k(colc(1), 1);
+      wait_copies_and_barrier<0>();
+      sfor<0, KS>([&](auto s_) {
+        sfor<0, 2>([&](auto t_) {
+          constexpr int s = SIDX(s_), t = SIDX(t_);
+          const bf16x8 kf = read_kfrag(kbuf(0), s, t);
+          if constexpr (s == 0) {
+            const f32x16 zero = {};
+            sacc[0][t] = mfma(kf, qf[0], zero);
+          } else {
+            sacc[0][t] = mfma(kf, qf[s], sacc[0][t]);
+          }
+        });
       });
-    });
+    }
+
+    constexpr int NPV = 4 * DT;                // O MFMAs per iteration
+    constexpr int NS = 2 * KS;                 // S MFMAs per iteration
+    constexpr int NCAP = CAP ? 4 : 0;
+    constexpr int NSLICE = NCAP + 3 + 8;
+    constexpr int DIST = 2;                    // operand reads run this many MFMAs ahead
+
+    // One iteration; FIRST skips the O MFMAs (there is no P_{-1}).
+    auto step = [&](int j, auto cur_tag, auto first_tag) __attribute__((always_inline)) {
+      constexpr int cur = SIDX(cur_tag);
+      constexpr int nxt = cur ^ 1;
+      constexpr bool FIRST = SIDX(first_tag) != 0;
+      constexpr int M0 = FIRST ? NPV : 0;      // first MFMA index issued
+      constexpr int NM = NPV + NS;
+      wait_copies_and_barrier<0>();
+      if (j + 2 < n) load_k(colc(j + 2), j & 1);
+      load_v(colc(j), j & 1);
+      f32x16* sv = sacc[cur];
+      // Partial block <=> it has a pattern (mask_next >= 0).
+      const bool partial = ld_table(p.mask_next, g0 + j) >= 0;
+
+      const lds_u8* kb = kbuf((j + 1) & 1);   // K_{j+1}
+      const lds_u8* vb = vbuf((j + 1) & 1);   // V_{j-1}
+      // MFMA m < NPV: O^T += V^T P^T for (key tile, key half) m / DT and
+      // d-tile m % DT; m >= NPV: S^T_{j+1} for k-step (m - NPV) / 2, key
+      // tile (m - NPV) % 2.
+      bf16x8 opnd[NM];
+      auto read_opnd = [&](auto m_) __attribute__((always_inline)) {
+        constexpr int m = SIDX(m_);
+        if constexpr (m < NPV) {
+          constexpr int tc = m / DT, dt = m % DT;
+          opnd[m] = read_vfrag(vb, tc / 2, tc % 2, dt);
+        } else {
+          constexpr int mm = m - NPV;
+          opnd[m] = read_kfrag(kb, mm / 2, mm % 2);
+        }
+      };
+      auto issue = [&](auto m_) __attribute__((always_inline)) {
+        constexpr int m = SIDX(m_);
+        if constexpr (m + DIST < NM) read_opnd(Idx<m + DIST>{});
+        if constexpr (m < NPV) {
+          constexpr int tc = m / DT, dt = m % DT;
+          oacc[dt] = mfma(opnd[m], pb[tc / 2][tc % 2], oacc[dt]);
+        } else {
+          constexpr int mm = m - NPV;
+          constexpr int s = mm / 2, t = mm % 2;
+          if constexpr (s == 0) {
+            const f32x16 zero = {};
+            sacc[nxt][t] = mfma(opnd[m], qf[0], zero);
+          } else {
+            sacc[nxt][t] = mfma(opnd[m], qf[s], sacc[nxt][t]);
+          }
+        }
+      };
+
+      float alpha = 1.0f, mc = 0.0f, ps = 0.0f;
+      float mxt[2];
+      auto slice = [&](auto i_) __attribute__((always_inline)) {
+        constexpr int i0 = SIDX(i_);
+        if constexpr (i0 < NCAP) {
+          // z = log2(e) cap tanh(scale q.k / cap), tanh y = 1 - 2 / (e^{2y} + 1).
+          constexpr int t = i0 / 2;
+          constexpr int e0 = (i0 % 2) * 8;
+          const float k2 = 2.0f * kLog2e * p.scale / p.soft_cap;
+          const float A = p.soft_cap * kLog2e;
+          sfor<e0, e0 + 8>([&](auto e_) {
+            constexpr int e = SIDX(e_);
+            const float ex = fast_exp2(sv[t][e] * k2);
+            sv[t][e] = A - 2.0f * A * __builtin_amdgcn_rcpf(ex + 1.0f);
+          });
+        } else {
+          constexpr int i = i0 - NCAP;
+          // The element mask comes after the cap (which maps -inf to -cap).
+          if constexpr (i == 0) {
+            if (partial) apply_mask(sv, j, colc(j));
+          }
+          if constexpr (i < 2) {
+            float m0 = sv[i][0];
+            sfor<1, 16>([&](auto e_) { m0 = fmaxf(m0, sv[i][SIDX(e_)]); });
+            mxt[i] = m0;
+          } else if constexpr (i == 2) {
+            // Row max across the two half-waves, then the lazy reference
+            // update: move only when the block max exceeds it by > 2^kTau.
+            const float m0 = fmaxf(mxt[0], mxt[1]);
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(m0), __float_as_uint(m0), false, false);
+            const float mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+            const bool need = mx * zc > mref * zc + kTau;
+            const float mnew = need ? mx : mref;
+            alpha = (mnew == mref) ? 1.0f : fast_exp2((mref - mnew) * zc);
+            mref = mnew;
+            mc = (mnew == -INFINITY) ? 0.0f : mnew * zc;
+          } else {
+            // p = 2^(z zc - m zc) for items 4(k%2) .. +3 of (tile, key half).
+            constexpr int k = i - 3;           // 0..7
+            constexpr int t = k / 4;
+            constexpr int c2 = (k / 2) % 2;
+            constexpr int h = k % 2;
+            u32x2 w;
+            sfor<0, 2>([&](auto e_) {
+              constexpr int e2 = 2 * h + SIDX(e_);
+              const float p0 = fast_exp2(fmaf(sv[t][8 * c2 + 2 * e2], zc, -mc));
+              const float p1 = fast_exp2(fmaf(sv[t][8 * c2 + 2 * e2 + 1], zc, -mc));
+              ps += p0 + p1;
+              w[SIDX(e_)] = pack_bf16(p0, p1);
+            });
+            u32x4 cur4 = __builtin_bit_cast(u32x4, pb[t][c2]);
+            cur4[2 * h] = w[0];
+            cur4[2 * h + 1] = w[1];
+            pb[t][c2] = __builtin_bit_cast(bf16x8, cur4);
+            if constexpr (k == 7) lsum = lsum * alpha + ps;
+          }
+        }
+      };
+
+      sfor<M0, M0 + DIST>([&](auto m_) { read_opnd(m_); });
+      sfor<0, NSLICE>([&](auto i_) {
+        constexpr int i = SIDX(i_);
+        constexpr int m0 = M0 + i * (NM - M0) / NSLICE;
+        constexpr int m1 = M0 + (i + 1) * (NM - M0) / NSLICE;
+        sfor<m0, m1>(issue);
+        slice(i_);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      // Keep P and l computed here, beside the MFMAs, rather than sunk past
+      // the branch and barrier below.
+      {
+        const bf16x8 q00 = pb[0][0], q01 = pb[0][1], q10 = pb[1][0], q11 = pb[1][1];
+        const float l0 = lsum;
+        asm volatile("" ::"v"(q00), "v"(q01), "v"(q10), "v"(q11), "v"(l0));
+      }
+      // O holds P_{j-1} V_{j-1}; move it to the new reference.
+      if (__any(alpha != 1.0f)) {
+        sfor<0, DT>([&](auto i_) { oacc[SIDX(i_)] *= alpha; });
+      }
+    };
+
+    if (n > 0) step(0, Idx<0>{}, Idx<1>{});
+    int j = 1;
+    for (; j + 1 < n; j += 2) {
+      step(j, Idx<1>{}, Idx<0>{});
+      step(j + 1, Idx<0>{}, Idx<0>{});
+    }
+    if (j < n) step(j, Idx<1>{}, Idx<0>{});
+    // Last block's P V (V_{n-1} was copied in the last iteration).
+    wait_copies_and_barrier<0>();
+    if (n > 0) {
+      const lds_u8* vb = vbuf((n - 1) & 1);
+      sfor<0, 4>([&](auto tc_) {
+        constexpr int tc = SIDX(tc_);
+        sfor<0, DT>([&](auto dt_) {
+          constexpr int dt = SIDX(dt_);
+          oacc[dt] = mfma(read_vfrag(vb, tc / 2, tc % 2, dt), pb[tc / 2][tc % 2], oacc[dt]);
+        });
+      });
+    }
+  };
+
+  // ---------------------------------------------------------------------
+  // Ping-pong loop.  Waves w and w + NW/2 run on the same SIMD, so waves
+  // [0, NW/2) (group 0) and [NW/2, NW) (group 1) each hold one wave per SIMD.
+  // Both groups run the same sequence MM(0) SM(0) MM(1) SM(1) ... MM(n), a
+  // work-group barrier after every phase, but group 1 starts one barrier
+  // later.  MM(i) is the matrix phase (O += P_{i-1} V_{i-1} for i >= 1,
+  // S_i = Q K_i^T for i < n), SM(i) the softmax phase (S_i -> P_i, l, lazy O
+  // rescale).  So in every half-step one wave of each SIMD feeds the matrix
+  // pipe while the other works on the vector unit:
+  //   half-step 2i:     group 0 MM(i)      group 1 SM(i-1)
+  //   half-step 2i+1:   group 0 SM(i)      group 1 MM(i)
+  // Group 1 also moves the tiles: at the start of SM(i) (half-step 2i+2) it
+  // issues K_{i+2} and V_{i+1} into the buffers of K_i and V_{i-1}, last read
+  // by MM(i) in half-steps 2i and 2i+1; it waits for them at the end of
+  // MM(i+1) (half-step 2i+3), and MM(i+2) reads them from half-step 2i+4.
+  auto pingpong_loop = [&]() __attribute__((always_inline)) {
+    static_assert(NW % 2 == 0, "two wave groups");
+    if (n == 0) return;
+    constexpr int GW = NW / 2;               // waves per group
+    const bool grp1 = wave >= GW;
+    const int gw = wave - (grp1 ? GW : 0);   // wave index inside its group
+    float mc = 0.0f;              // reference exponent offset m zc (0 while m = -inf)
+    float mthr = -INFINITY;       // m + kTau / zc: block maxima above it move m
+    f32x16 sacc[2];   // S^T of the current block: two 32-key tiles
+    bf16x8 pb[2][2];  // P^T of the previous block: [key tile][key half]
+    sfor<0, 4>([&](auto i_) { pb[SIDX(i_) / 2][SIDX(i_) % 2] = bf16x8{}; });
+
+    // Tile copies split over the 4 waves of group 1.
+    auto g1_load_k = [&](int c, int buf) __attribute__((always_inline)) {
+      const int k0 = c * BN;
+#pragma unroll
+      for (int t = 0; t < C::KCHUNKS / (64 * GW); ++t) {
+        const int slot0 = (t * GW + gw) * 64;
+        const int slot = slot0 + lane;
+        const int row = slot / (DQK / 8);
+        const int pc = slot - row * (DQK / 8);
+        const int off = ((k0 + row) * DQK + kswz<C::KROW>(row, pc) * 8) * 2;
+        dma16(krs, (uint32_t)(uintptr_t)(kbuf(buf) + slot0 * 16), off);
+      }
+    };
+    auto g1_load_v = [&](int c, int buf) __attribute__((always_inline)) {
+      const int k0 = c * BN;
+#pragma unroll
+      for (int t = 0; t < C::VCHUNKS / (64 * GW); ++t) {
+        const int slot0 = (t * GW + gw) * 64;
+        const int slot = slot0 + lane;
+        const int row = slot / (DV / 8);
+        const int pc = slot - row * (DV / 8);
+        const int off = ((k0 + row) * DV + vswz<C::VROW>(row, pc) * 8) * 2;
+        dma16(vrs, (uint32_t)(uintptr_t)(vbuf(buf) + slot0 * 16), off);
+      }
+    };
+    static_assert(C::KCHUNKS % (64 * GW) == 0 && C::VCHUNKS % (64 * GW) == 0, "tile split");
+
+    // Operand addresses.  With 256-byte rows the swizzle is an XOR of the
+    // address bits below 256, so every read is one base register XOR a
+    // constant (tiles and rows start at multiples of 256 bytes).
+    auto kfrag = [&](const lds_u8* kb, int s, int t) __attribute__((always_inline)) {
+      if constexpr (C::KROW % 256 == 0) {
+        const uint32_t base = (uint32_t)(uintptr_t)kb + l32 * C::KROW + 16 * (hi ^ (l32 & 15));
+        const uint32_t a = (base ^ (uint32_t)(32 * s)) + (uint32_t)(32 * t * C::KROW);
+        return *reinterpret_cast<const lds_bf16x8*>((lds_u8*)(uintptr_t)a);
+      } else {
+        const int key = 32 * t + l32;
+        return *reinterpret_cast<const lds_bf16x8*>(kb + key * C::KROW + kswz<C::KROW>(key, 2 * s + hi) * 16);
+      }
+    };
+    auto vfrag = [&](const lds_u8* vb, int t, int c2, int dt) __attribute__((always_inline)) {
+      const int row = 32 * t + 16 * c2 + vrow0;
+      const int row2 = row + 8;
+      i16x4 lo, up;
+      if constexpr (C::VROW == 256) {
+        // chunk 4dt + vcol0 of row r sits at chunk 4(dt ^ (r & 3)) + vcol0.
+        const uint32_t base = (uint32_t)(uintptr_t)vb + vrow0 * C::VROW +
+                              ((64 * (vrow0 & 3)) | (16 * vcol0) | (8 * (jj & 1)));
+        const uint32_t a = (base ^ (uint32_t)(64 * dt)) + (uint32_t)((32 * t + 16 * c2) * C::VROW);
+        lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)a);
+        up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(a + 8 * C::VROW));
+      } else {
+        const int lc = 4 * dt + vcol0;
+        lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(vb + row * C::VROW + vswz<C::VROW>(row, lc) * 16 + 8 * (jj & 1)));
+        up = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(vb + row2 * C::VROW + vswz<C::VROW>(row2, lc) * 16 + 8 * (jj & 1)));
+      }
+      const u32x2 lo2 = __builtin_bit_cast(u32x2, lo);
+      const u32x2 up2 = __builtin_bit_cast(u32x2, up);
+      return __builtin_bit_cast(bf16x8, u32x4{lo2[0], lo2[1], up2[0], up2[1]});
+    };
+
+    // Matrix phase MM(i); the tags select the O product and the scores.
+    auto mm = [&](int i, auto pv_tag, auto sc_tag) __attribute__((always_inline)) {
+      constexpr int NP = SIDX(pv_tag) ? 4 * DT : 0;
+      constexpr int NQ = SIDX(sc_tag) ? 2 * KS : 0;
+      using O = MatOrder<NP, NQ>;
+      constexpr int DIST = 3;  // operand reads run this many MFMAs ahead
+      const lds_u8* kb = kbuf(i & 1);         // K_i
+      const lds_u8* vb = vbuf((i + 1) & 1);   // V_{i-1}
+      bf16x8 opnd[O::N];
+      auto read_opnd = [&](auto m_) __attribute__((always_inline)) {
+        constexpr int m = SIDX(m_);
+        constexpr int x = O::idx(m);
+        if constexpr (O::is_s(m)) {
+          opnd[m] = kfrag(kb, x / 2, x % 2);
+        } else {
+          constexpr int tc = x / DT;
+          opnd[m] = vfrag(vb, tc / 2, tc % 2, x % DT);
+        }
+      };
+      auto issue = [&](auto m_) __attribute__((always_inline)) {
+        constexpr int m = SIDX(m_);
+        if constexpr (m + DIST < O::N) read_opnd(Idx<m + DIST>{});
+        constexpr int x = O::idx(m);
+        if constexpr (O::is_s(m)) {
+          constexpr int s = x / 2, t = x % 2;
+          if constexpr (s == 0) {
+            const f32x16 zero = {};
+            sacc[t] = mfma(opnd[m], qf[0], zero);
+          } else {
+            sacc[t] = mfma(opnd[m], qf[s], sacc[t]);
+          }
+        } else {
+          constexpr int tc = x / DT, dt = x % DT;
+          oacc[dt] = mfma(opnd[m], pb[tc / 2][tc % 2], oacc[dt]);
+        }
+      };
+      sfor<0, (DIST < O::N ? DIST : O::N)>([&](auto m_) { read_opnd(m_); });
+      sfor<0, O::N>(issue);
+      // The scores stay in this half-step (not sunk past the barrier).
+      if constexpr (NQ > 0) {
+        const f32x16 a0 = sacc[0], a1 = sacc[1];
+        asm volatile("" ::"v"(a0), "v"(a1));
+      }
+    };
+
+    // Softmax phase SM(i): S_i -> P_i (bf16), l, lazy reference and O rescale.
+    // copy(Idx<k>) issues tile-copy instruction k of NCOPY; they are spread
+    // between the exponentials so that the vector-memory queue drains while
+    // the wave keeps computing.  With the lazy reference the exponent offset
+    // almost never moves, so P is computed with the current offset while the
+    // block max is reduced (a tree, in parallel); only when some row's max
+    // passes its threshold does the wave move the reference and recompute.
+    auto exps = [&](f32x16* sv, float mcv, auto copy, auto ncopy_tag) __attribute__((always_inline)) {
+      constexpr int NCOPY = SIDX(ncopy_tag);
+      float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      sfor<0, 4>([&](auto i_) {
+        constexpr int t = SIDX(i_) / 2;
+        constexpr int c2 = SIDX(i_) % 2;
+        u32x4 w;
+        sfor<0, 4>([&](auto e_) {
+          constexpr int e2 = SIDX(e_);
+          constexpr int q = 4 * SIDX(i_) + e2;   // pair index 0..15
+          const float p0 = fast_exp2(fmaf(sv[t][8 * c2 + 2 * e2], zc, -mcv));
+          const float p1 = fast_exp2(fmaf(sv[t][8 * c2 + 2 * e2 + 1], zc, -mcv));
+          ps[q & 3] += p0 + p1;
+          w[e2] = pack_bf16(p0, p1);
+          if constexpr ((q + 1) * NCOPY / 16 > q * NCOPY / 16) {
+            // Keep each copy at its place between the exponentials.
+            __builtin_amdgcn_sched_barrier(0);
+            sfor<q * NCOPY / 16, (q + 1) * NCOPY / 16>(copy);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        });
+        pb[t][c2] = __builtin_bit_cast(bf16x8, w);
+      });
+      return (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    };
+    auto sm = [&](int i, auto copy, auto ncopy_tag) __attribute__((always_inline)) {
+      f32x16* sv = sacc;
+      if constexpr (CAP) {
+        // z = log2(e) cap tanh(scale q.k / cap), tanh y = 1 - 2 / (e^{2y} + 1).
+        const float k2 = 2.0f * kLog2e * p.scale / p.soft_cap;
+        const float A = p.soft_cap * kLog2e;
+        sfor<0, 32>([&](auto i_) {
+          constexpr int t = SIDX(i_) / 16;
+          constexpr int e = SIDX(i_) % 16;
+          const float ex = fast_exp2(sv[t][e] * k2);
+          sv[t][e] = A - 2.0f * A * __builtin_amdgcn_rcpf(ex + 1.0f);
+        });
+      }
+      // Partial block <=> it has a pattern (mask_next >= 0); after the cap,
+      // which would map -inf to -cap.
+      if (ld_table(p.mask_next, g0 + i) >= 0) apply_mask(sv, i, colc(i));
+      float ps = exps(sv, mc, copy, ncopy_tag);
+      {
+        // Computed here, overlapping the max below (not sunk into its branch).
+        const bf16x8 q00 = pb[0][0], q01 = pb[0][1], q10 = pb[1][0], q11 = pb[1][1];
+        asm volatile("" ::"v"(q00), "v"(q01), "v"(q10), "v"(q11), "v"(ps));
+      }
+      // Row max: a tree over the lane's 32 scores, then the other half-wave.
+      // 32 -> 11 -> 4 -> 2 -> 1 with three-input maxima (16 instructions).
+      auto max3 = [](float a, float b, float c) __attribute__((always_inline)) {
+        return __builtin_fmaxf(__builtin_fmaxf(a, b), c);
+      };
+      auto el = [&](int k) __attribute__((always_inline)) { return sv[k / 16][k % 16]; };
+      float m11[11];
+      sfor<0, 10>([&](auto j_) {
+        constexpr int j = SIDX(j_);
+        m11[j] = max3(el(3 * j), el(3 * j + 1), el(3 * j + 2));
+      });
+      m11[10] = __builtin_fmaxf(el(30), el(31));
+      const float m4a = max3(m11[0], m11[1], m11[2]), m4b = max3(m11[3], m11[4], m11[5]);
+      const float m4c = max3(m11[6], m11[7], m11[8]), m4d = __builtin_fmaxf(m11[9], m11[10]);
+      float mx = __builtin_fmaxf(max3(m4a, m4b, m4c), m4d);
+      {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      }
+      // Lazy reference: a row moves only when its block max exceeds the
+      // reference by more than 2^kTau in the exponent (mthr = m + kTau / zc).
+      if (__any(mx > mthr)) {
+        const float mnew = (mx > mthr) ? mx : mref;
+        const float alpha = (mnew == mref) ? 1.0f : fast_exp2((mref - mnew) * zc);
+        mref = mnew;
+        mc = (mnew == -INFINITY) ? 0.0f : mnew * zc;
+        mthr = mnew + kTau / zc;
+        ps = exps(sv, mc, [&](auto) __attribute__((always_inline)) {}, Idx<0>{});
+        lsum *= alpha;
+        sfor<0, DT>([&](auto i_) { oacc[SIDX(i_)] *= alpha; });
+      }
+      lsum += ps;
+      // P and l stay in this half-step (not sunk past the barrier).
+      {
+        const bf16x8 q00 = pb[0][0], q01 = pb[0][1], q10 = pb[1][0], q11 = pb[1][1];
+        const float l0 = lsum;
+        asm volatile("" ::"v"(q00), "v"(q01), "v"(q10), "v"(q11), "v"(l0));
+      }
+    };
+
+    // One tile-copy instruction of group 1's share: k < KL copies part of a
+    // K tile, the rest part of a V tile.
+    constexpr int KL = C::KCHUNKS / (64 * GW);
+    constexpr int VL = C::VCHUNKS / (64 * GW);
+    auto copy_part = [&](auto k_, int ck, int kbf, int cv, int vbf) __attribute__((always_inline)) {
+      constexpr int k = SIDX(k_);
+      if constexpr (k < KL) {
+        const int slot0 = (k * GW + gw) * 64;
+        const int slot = slot0 + lane;
+        const int row = slot / (DQK / 8);
+        const int pc = slot - row * (DQK / 8);
+        const int off = ((ck * BN + row) * DQK + kswz<C::KROW>(row, pc) * 8) * 2;
+        dma16(krs, (uint32_t)(uintptr_t)(kbuf(kbf) + slot0 * 16), off);
+      } else {
+        const int slot0 = ((k - KL) * GW + gw) * 64;
+        const int slot = slot0 + lane;
+        const int row = slot / (DV / 8);
+        const int pc = slot - row * (DV / 8);
+        const int off = ((cv * BN + row) * DV + vswz<C::VROW>(row, pc) * 8) * 2;
+        dma16(vrs, (uint32_t)(uintptr_t)(vbuf(vbf) + slot0 * 16), off);
+      }
+    };
+    auto no_copy = [&](auto) __attribute__((always_inline)) {};
+
+    // Each group runs its own copy of the sequence (no per-phase branches).
+    auto run = [&](auto g1_tag) __attribute__((always_inline)) {
+      constexpr bool G1 = SIDX(g1_tag) != 0;
+      if constexpr (G1) {
+        g1_load_k(cols[0], 0);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
+      lds_barrier();
+      if constexpr (G1) {
+        if (n > 1) g1_load_k(colc(1), 1);
+        g1_load_v(cols[0], 0);
+        lds_barrier();   // group 1 starts one half-step late
+      }
+      mm(0, Idx<0>{}, Idx<1>{});
+      for (int i = 0; i + 1 < n; ++i) {
+        wait_copies_and_barrier<0>();
+        if constexpr (G1) {
+          // K_{i+2} (past the end: a repeat of K_{n-1} into the free buffer)
+          // and V_{i+1}.
+          const int ck = colc(i + 2), cv = colc(i + 1);
+          const int kbf = i & 1, vbf = (i + 1) & 1;
+          sm(i, [&](auto k_) __attribute__((always_inline)) { copy_part(k_, ck, kbf, cv, vbf); },
+             Idx<KL + VL>{});
+        } else {
+          sm(i, no_copy, Idx<0>{});
+        }
+        lds_barrier();
+        mm(i + 1, Idx<1>{}, Idx<1>{});
+      }
+      wait_copies_and_barrier<0>();
+      sm(n - 1, no_copy, Idx<0>{});
+      lds_barrier();
+      mm(n, Idx<1>{}, Idx<0>{});
+      if constexpr (!G1) lds_barrier();   // matches group 1's extra barrier
+    };
+    if (grp1)
+      run(Idx<1>{});
+    else
+      run(Idx<0>{});
+  };
+
+  if constexpr (LOOP == 0) {
+    if (n > 0) {
+      load_k(cols[0], 0);
+      load_v(cols[0], 0);
+    }
+
+    for (int j = 0; j < n; ++j) {
+      const int buf = j & 1;
+      // Block j's copies (issued one iteration earlier) have landed and every
+      // wave is past iteration j-1, so buffer buf^1 is free: copy block j+1
+      // into it while block j is computed.
+      wait_copies_and_barrier<0>();
+      if (j + 1 < n) {
+        load_k(colc(j + 1), buf ^ 1);
+        load_v(colc(j + 1), buf ^ 1);
+      }
+
+      const lds_u8* kb = kbuf(buf);
+      const lds_u8* vb = vbuf(buf);
+
+      // S^T for the two 32-key tiles (two independent accumulation chains).
+      f32x16 sv[2];
+      sfor<0, KS>([&](auto s_) {
+        constexpr int s = SIDX(s_);
+        sfor<0, 2>([&](auto t_) {
+          constexpr int t = SIDX(t_);
+          const int key = 32 * t + l32;
+          const bf16x8 kf = *reinterpret_cast<const lds_bf16x8*>(kb + key * C::KROW + kswz<C::KROW>(key, 2 * s + hi) * 16);
+          if constexpr (s == 0) {
+            const f32x16 zero = {};
+            sv[t] = mfma(kf, qf[0], zero);
+          } else {
+            sv[t] = mfma(kf, qf[s], sv[t]);
+          }
+        });
+      });
+
+      if constexpr (CAP) {
+        const float k2 = 2.0f * kLog2e * p.scale / p.soft_cap;
+        const float A = p.soft_cap * kLog2e;
+        sfor<0, 32>([&](auto i_) {
+          constexpr int t = SIDX(i_) / 16;
+          constexpr int e = SIDX(i_) % 16;
+          const float ex = fast_exp2(sv[t][e] * k2);
+          sv[t][e] = A - 2.0f * A * __builtin_amdgcn_rcpf(ex + 1.0f);
+        });
+      }
+      // Partial block <=> it has a pattern (mask_next >= 0); int32 scalar load.
+      if (ld_table(p.mask_next, g0 + j) >= 0) apply_mask(sv, j, colc(j));
+
+      // Row max: in-lane over 32 keys, then across the two half-waves.
+      float mx = sv[0][0];
+      sfor<1, 32>([&](auto i_) { mx = fmaxf(mx, sv[SIDX(i_) / 16][SIDX(i_) % 16]); });
+      {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      }
+      // Lazy reference update: move only when the block max exceeds it by > 2^kTau.
+      const bool need = mx * zc > mref * zc + kTau;
+      const float mnew = need ? mx : mref;
+      const float alpha = (mnew == mref) ? 1.0f : fast_exp2((mref - mnew) * zc);
+      mref = mnew;
+      const float mc = (mnew == -INFINITY) ? 0.0f : mnew * zc;
+
+      // p = 2^(z zc - m zc), packed as bf16 B operands: tile t, key half c2.
+      bf16x8 pb[2][2];
+      float ps = 0.0f;
+      sfor<0, 4>([&](auto i_) {
+        constexpr int t = SIDX(i_) / 2;
+        constexpr int c2 = SIDX(i_) % 2;
+        u32x4 w;
+        sfor<0, 4>([&](auto e_) {
+          constexpr int e2 = SIDX(e_);
+          const float p0 = fast_exp2(fmaf(sv[t][8 * c2 + 2 * e2], zc, -mc));
+          const float p1 = fast_exp2(fmaf(sv[t][8 * c2 + 2 * e2 + 1], zc, -mc));
+          ps += p0 + p1;
+          w[e2] = pack_bf16(p0, p1);
+        });
+        pb[t][c2] = __builtin_bit_cast(bf16x8, w);
+      });
+      lsum = lsum * alpha + ps;
+      if (__any(alpha != 1.0f)) {
+        sfor<0, DT>([&](auto i_) { oacc[SIDX(i_)] *= alpha; });
+      }
+
+      // O^T += V^T P^T; key-half-major order keeps the DT accumulators
+      // independent between consecutive MFMAs.
+      sfor<0, 4>([&](auto tc_) {
+        constexpr int t = SIDX(tc_) / 2;
+        constexpr int c2 = SIDX(tc_) % 2;
+        const int row = 32 * t + 16 * c2 + vrow0;
+        const int row2 = row + 8;
+        sfor<0, DT>([&](auto dt_) {
+          constexpr int dt = SIDX(dt_);
+          const int lc = 4 * dt + vcol0;
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_i16x4*)(vb + row * C::VROW + vswz<C::VROW>(row, lc) * 16 + 8 * (jj & 1)));
+          const i16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_i16x4*)(vb + row2 * C::VROW + vswz<C::VROW>(row2, lc) * 16 + 8 * (jj & 1)));
+          const u32x2 lo2 = __builtin_bit_cast(u32x2, lo);
+          const u32x2 up2 = __builtin_bit_cast(u32x2, up);
+          const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{lo2[0], lo2[1], up2[0], up2[1]});
+          oacc[dt] = mfma(vf, pb[t][c2], oacc[dt]);
+        });
+      });
+    }
+  } else if constexpr (LOOP == 1) {
+    pipelined_loop();
+  } else {
+    pingpong_loop();
   }
 
   // Epilogue: o = O / l, lse = (m zc + log2 l) ln 2.
@@ -439,11 +997,11 @@ void splash_fwd_bf16_kernel(FwdParams p) {
   }
 }
 
-template <int DQK, int DV, bool CAP>
+template <int DQK, int DV, bool CAP, int LOOP>
 hipError_t launch(const FwdParams& p, hipStream_t s) {
   const int64_t n_wg = (int64_t)p.B * p.Hq * p.n_q_blocks;
   const int bytes = Cfg<DQK, DV>::LDS_BYTES;
-  auto fn = splash_fwd_bf16_kernel<DQK, DV, CAP>;
+  auto fn = splash_fwd_bf16_kernel<DQK, DV, CAP, LOOP>;
   if (bytes > 65536) {
     // Opt in to more than 64 KiB of dynamic LDS (gfx950 has 160 KiB per CU).
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
@@ -454,9 +1012,26 @@ hipError_t launch(const FwdParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+int loop_mode() {
+  static const int v = [] {
+    const char* e = getenv("SPLASH_BF16_LOOP");
+    return e ? atoi(e) : 2;
+  }();
+  return v;
+}
+
+template <int DQK, int DV, bool CAP>
+hipError_t launch_loop(const FwdParams& p, hipStream_t s) {
+  switch (loop_mode()) {
+    case 0: return launch<DQK, DV, CAP, 0>(p, s);
+    case 1: return launch<DQK, DV, CAP, 1>(p, s);
+    default: return launch<DQK, DV, CAP, 2>(p, s);
+  }
+}
+
 template <int DQK, int DV>
 hipError_t launch_cap(const FwdParams& p, hipStream_t s) {
-  return p.soft_cap > 0.0f ? launch<DQK, DV, true>(p, s) : launch<DQK, DV, false>(p, s);
+  return p.soft_cap > 0.0f ? launch_loop<DQK, DV, true>(p, s) : launch_loop<DQK, DV, false>(p, s);
 }
 
 }  // namespace

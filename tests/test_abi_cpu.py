@@ -139,8 +139,8 @@ def test_fwd_tile_errors_and_values():
     assert lib.splash_fwd_tile(1, 96, 128, ctypes.byref(a), ctypes.byref(b)) == 4
     assert lib.splash_fwd_tile(0, 192, 128, ctypes.byref(a), ctypes.byref(b)) == 4
     assert lib.splash_fwd_tile(1, 128, 128, None, ctypes.byref(b)) == 1
-    assert fwd_tile("bf16", 128, 128) == (128, 64)
-    assert fwd_tile("bf16", 192, 128) == (128, 64)
+    assert fwd_tile("bf16", 128, 128) == (256, 64)
+    assert fwd_tile("bf16", 192, 128) == (256, 64)
     assert fwd_tile("f32", 64, 64) == (64, 64)
 
 
@@ -152,7 +152,7 @@ def _good_args(**over):
     a = dict(dtype=1, B=1, Hq=2, Hkv=1, L=256, d_qk=128, d_v=128,
              q=fake, k=fake, v=fake, o=fake, lse=None,
              causal=1, window_left=-1, window_right=-1, seg_q=None, seg_kv=None,
-             block_q=128, block_kv=64, n_q_blocks=2, n_active=3, n_patterns=1,
+             block_q=256, block_kv=64, n_q_blocks=1, n_active=3, n_patterns=1,
              row_ptr=fake, row_order=fake, active_cols=fake, block_code=fake,
              mask_next=fake, partial_mask_blocks=fake, mask_mode=0,
              scale=0.088, soft_cap=0.0)
@@ -177,7 +177,7 @@ def _good_args(**over):
     (dict(soft_cap=math.nan), 1),
     (dict(soft_cap=math.inf), 1),
     (dict(block_kv=32), 2),
-    (dict(n_q_blocks=3), 2),
+    (dict(n_q_blocks=2), 2),
     (dict(q=None), 1),
     (dict(o=0x10008), 1),
     (dict(row_ptr=None), 1),
