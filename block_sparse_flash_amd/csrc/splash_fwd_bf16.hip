@@ -99,7 +99,9 @@ struct Cfg {
   static constexpr int KCHUNKS = KTILE / 16;   // 16-byte chunks per K tile
   static constexpr int VCHUNKS = VTILE / 16;
   static constexpr int NBUF = 2;               // tile buffers per operand
-  static constexpr int LDS_BYTES = NBUF * (KTILE + VTILE);
+  static constexpr int SEG_OFF = NBUF * (KTILE + VTILE);  // key segment-id ring
+  static constexpr int SEG_SLOTS = 3;          // ids of one block per slot
+  static constexpr int LDS_BYTES = SEG_OFF + SEG_SLOTS * BN * 4;
   static constexpr int KLOADS = KCHUNKS / NT;  // tile-copy instructions per wave
   static constexpr int VLOADS = VCHUNKS / NT;
   static_assert(KCHUNKS % NT == 0 && VCHUNKS % NT == 0, "tile chunks split evenly over the work-group");
@@ -165,6 +167,25 @@ __device__ __forceinline__ void dma16(u32x4 rsrc, uint32_t lds_addr, int voff) {
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %1\n\t"
       "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(base), "v"(voff), "s"(rs)
+      : "memory");
+}
+
+// One 4-byte-per-lane HBM -> LDS copy (lane i's dword lands at
+// lds_addr + 4 i); otherwise as dma16.
+__device__ __forceinline__ void dma4(u32x4 rsrc, uint32_t lds_addr, int voff) {
+  const uint32_t base = (uint32_t)__builtin_amdgcn_readfirstlane(lds_addr);
+  const u32x4 rs = {(uint32_t)__builtin_amdgcn_readfirstlane(rsrc[0]),
+                    (uint32_t)__builtin_amdgcn_readfirstlane(rsrc[1]),
+                    (uint32_t)__builtin_amdgcn_readfirstlane(rsrc[2]),
+                    (uint32_t)__builtin_amdgcn_readfirstlane(rsrc[3])};
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "buffer_load_dword %2, %3, 0 offen lds\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
       : "s"(base), "v"(voff), "s"(rs)
@@ -362,11 +383,14 @@ void splash_fwd_bf16_kernel(FwdParams p) {
         sv[t][i] = ok ? sv[t][i] : -INFINITY;
       });
     } else {
+      // Key offset minus 4 hi against the shifted interval (constants on one side).
+      const int base = ka + 4 * hi;
+      const int lo = klo - base, up = khi - base;
       sfor<0, 32>([&](auto i_) {
         constexpr int t = SIDX(i_) / 16;
         constexpr int i = SIDX(i_) % 16;
-        const int key = ka + 32 * t + 8 * (i / 4) + 4 * hi + (i % 4);
-        const bool ok = (key >= klo) & (key <= khi);
+        constexpr int r = 32 * t + 8 * (i / 4) + (i % 4);
+        const bool ok = (r >= lo) & (r <= up);
         sv[t][i] = ok ? sv[t][i] : -INFINITY;
       });
     }
@@ -597,6 +621,38 @@ void splash_fwd_bf16_kernel(FwdParams p) {
     const int gw = wave - (grp1 ? GW : 0);   // wave index inside its group
     float mc = 0.0f;              // reference exponent offset m zc (0 while m = -inf)
     float mthr = -INFINITY;       // m + kTau / zc: block maxima above it move m
+
+    // Key segment ids of a block, for the element mask of partial blocks,
+    // are copied into an LDS ring (slot = block index mod 3) by one wave of
+    // group 1 together with the block's K tile; the mask then reads them
+    // with four-key LDS loads instead of one global load per key.
+    const bool seg_lds = has_seg && !p.mask_stored;
+    const u32x4 srs = uniform(make_rsrc(segk, (uint32_t)(has_seg ? L * 4 : 0)));
+    auto segbuf = [&](int slot) { return lds + C::SEG_OFF + slot * (BN * 4); };
+    auto seg_copy = [&](int c, int slot) __attribute__((always_inline)) {
+      if (seg_lds && gw == 0) dma4(srs, (uint32_t)(uintptr_t)segbuf(slot), (c * BN + lane) * 4);
+    };
+    // Element mask of a partial block with segments: item E of tile t is key
+    // k0 + 32t + 8(E/4) + 4hi + E%4 of query qi.
+    auto apply_mask_seg_lds = [&](f32x16* sv, int c, int slot) __attribute__((always_inline)) {
+      // Key offset inside the block minus this half-wave's 4 hi, against the
+      // lane's allowed interval shifted the same way: compile-time constants
+      // on one side.
+      const int base = c * BN + 4 * hi;
+      const int lo = klo - base, up = khi - base;
+      const lds_u8* st = segbuf(slot) + 16 * hi;
+      sfor<0, 8>([&](auto j_) {
+        constexpr int t = SIDX(j_) / 4;
+        constexpr int q4 = SIDX(j_) % 4;
+        const u32x4 ids = *reinterpret_cast<const lds_u32x4*>(st + (32 * t + 8 * q4) * 4);
+        sfor<0, 4>([&](auto e_) {
+          constexpr int e = SIDX(e_);
+          constexpr int r = 32 * t + 8 * q4 + e;
+          const bool ok = (r >= lo) & (r <= up) & ((int)ids[e] == my_seg);
+          sv[t][4 * q4 + e] = ok ? sv[t][4 * q4 + e] : -INFINITY;
+        });
+      });
+    };
     f32x16 sacc[2];   // S^T of the current block: two 32-key tiles
     bf16x8 pb[2][2];  // P^T of the previous block: [key tile][key half]
     sfor<0, 4>([&](auto i_) { pb[SIDX(i_) / 2][SIDX(i_) % 2] = bf16x8{}; });
@@ -756,7 +812,12 @@ void splash_fwd_bf16_kernel(FwdParams p) {
       }
       // Partial block <=> it has a pattern (mask_next >= 0); after the cap,
       // which would map -inf to -cap.
-      if (ld_table(p.mask_next, g0 + i) >= 0) apply_mask(sv, i, colc(i));
+      if (ld_table(p.mask_next, g0 + i) >= 0) {
+        if (seg_lds)
+          apply_mask_seg_lds(sv, colc(i), i % 3);
+        else
+          apply_mask(sv, i, colc(i));
+      }
       float ps = exps(sv, mc, copy, ncopy_tag);
       {
         // Computed here, overlapping the max below (not sunk into its branch).
@@ -807,8 +868,9 @@ void splash_fwd_bf16_kernel(FwdParams p) {
     // K tile, the rest part of a V tile.
     constexpr int KL = C::KCHUNKS / (64 * GW);
     constexpr int VL = C::VCHUNKS / (64 * GW);
-    auto copy_part = [&](auto k_, int ck, int kbf, int cv, int vbf) __attribute__((always_inline)) {
+    auto copy_part = [&](auto k_, int ck, int kbf, int cv, int vbf, int sslot) __attribute__((always_inline)) {
       constexpr int k = SIDX(k_);
+      if constexpr (k == 0) seg_copy(ck, sslot);
       if constexpr (k < KL) {
         const int slot0 = (k * GW + gw) * 64;
         const int slot = slot0 + lane;
@@ -832,11 +894,15 @@ void splash_fwd_bf16_kernel(FwdParams p) {
       constexpr bool G1 = SIDX(g1_tag) != 0;
       if constexpr (G1) {
         g1_load_k(cols[0], 0);
+        seg_copy(cols[0], 0);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       }
       lds_barrier();
       if constexpr (G1) {
-        if (n > 1) g1_load_k(colc(1), 1);
+        if (n > 1) {
+          g1_load_k(colc(1), 1);
+          seg_copy(colc(1), 1);
+        }
         g1_load_v(cols[0], 0);
         lds_barrier();   // group 1 starts one half-step late
       }
@@ -846,9 +912,11 @@ void splash_fwd_bf16_kernel(FwdParams p) {
         if constexpr (G1) {
           // K_{i+2} (past the end: a repeat of K_{n-1} into the free buffer)
           // and V_{i+1}.
+          // Segment ids of block i+2 go to ring slot (i+2) % 3, last read by
+          // SM(i-1) in half-step 2i.
           const int ck = colc(i + 2), cv = colc(i + 1);
-          const int kbf = i & 1, vbf = (i + 1) & 1;
-          sm(i, [&](auto k_) __attribute__((always_inline)) { copy_part(k_, ck, kbf, cv, vbf); },
+          const int kbf = i & 1, vbf = (i + 1) & 1, sslot = (i + 2) % 3;
+          sm(i, [&](auto k_) __attribute__((always_inline)) { copy_part(k_, ck, kbf, cv, vbf, sslot); },
              Idx<KL + VL>{});
         } else {
           sm(i, no_copy, Idx<0>{});
