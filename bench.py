@@ -111,6 +111,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--mask-mode", default="computed", choices=["computed", "stored"])
+    ap.add_argument("--max-logit", type=float, default=None,
+                    help="Max Logit Estimate constant (logit units) in place of the running "
+                         "row max; the default is the running max")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run one device-to-device copy of this many MiB "
                          "(a plain copy of known size, for scaling HBM counters)")
@@ -140,7 +143,7 @@ def main():
     out = torch.empty((w.B, w.Hq, w.L, w.d_v), dtype=qd.dtype, device=dev)
     lse = torch.empty((w.B, w.Hq, w.L), dtype=torch.float32, device=dev)
     kw = dict(scale=w.softmax_scale, soft_cap=w.soft_cap, seg_q=seg, tables=tabs,
-              mask_mode=args.mask_mode, out=out, lse=lse, **mask_kw)
+              mask_mode=args.mask_mode, out=out, lse=lse, max_logit=args.max_logit, **mask_kw)
 
     for _ in range(args.warmup):
         splash_fwd(qd, kd, vd, **kw)
@@ -190,7 +193,8 @@ def main():
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "L": w.L,
                    "d_qk": w.d_qk, "d_v": w.d_v, "mask": mask, "soft_cap": w.soft_cap,
                    "scale": w.softmax_scale, "block_q": bq, "block_kv": bkv,
-                   "mask_mode": args.mask_mode, "parallelism": "single GPU"},
+                   "mask_mode": args.mask_mode, "max_logit": args.max_logit,
+                   "parallelism": "single GPU"},
         "pct_of_peak": round(100.0 * tflops / peak, 2),
         "unmasked_tflop_per_step": flop_per_step / 1e12,
         "active_blocks": tabs.n_active, "partial_blocks": tabs.n_partial,

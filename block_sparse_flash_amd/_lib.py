@@ -64,7 +64,8 @@ class FwdArgs(ctypes.Structure):
                 ("block_code", c_ptr), ("mask_next", c_ptr),
                 ("partial_mask_blocks", c_ptr),
                 ("mask_mode", c_i32), ("scale", ctypes.c_float),
-                ("soft_cap", ctypes.c_float)]
+                ("soft_cap", ctypes.c_float),
+                ("use_max_logit", c_i32), ("max_logit", ctypes.c_float)]
 
 
 class SplashError(RuntimeError):

@@ -129,15 +129,17 @@ def splash_fwd(q, k, v, *, scale: Optional[float] = None, soft_cap: float = 0.0,
                causal: bool = False, window_left: int = -1, window_right: int = -1,
                seg_q=None, seg_kv=None, tables: Optional[MaskTables] = None,
                mask_mode: str = "computed", out=None, lse=None, return_lse: bool = True,
-               stream=None):
+               max_logit: Optional[float] = None, stream=None):
     """Block-sparse attention forward on the GPU.
 
     q [B, Hq, L, d_qk], k [B, Hkv, L, d_qk], v [B, Hkv, L, d_v]: contiguous
     torch tensors on one GPU, all float32 or all bfloat16.  ``seg_q`` /
     ``seg_kv``: segment ids [L] (shared by the batch) or [B, L].  ``tables``:
     a MaskTables compiled for this mask at the kernel's block sizes
-    (``fwd_tile``); compiled here when omitted.  Returns (o, lse) with o like q
-    but with d_v, lse float32 [B, Hq, L] (None if ``return_lse`` is False).
+    (``fwd_tile``); compiled here when omitted.  ``max_logit``: the Max Logit
+    Estimate constant (logit units) used instead of the running row max, or
+    None.  Returns (o, lse) with o like q but with d_v, lse float32 [B, Hq, L]
+    (None if ``return_lse`` is False).
     """
     import torch
     lib = _lib.load()
@@ -219,6 +221,7 @@ def splash_fwd(q, k, v, *, scale: Optional[float] = None, soft_cap: float = 0.0,
             dev["row_ptr"].data_ptr(), dev["row_order"].data_ptr(),
             dev["active_cols"].data_ptr(), dev["block_code"].data_ptr(),
             dev["mask_next"].data_ptr(), dev["partial_mask_blocks"].data_ptr(),
-            _MASK_MODES[mask_mode], float(scale), float(soft_cap))
+            _MASK_MODES[mask_mode], float(scale), float(soft_cap),
+            0 if max_logit is None else 1, 0.0 if max_logit is None else float(max_logit))
         _lib.check(lib.splash_attn_fwd(ctypes.byref(args), ctypes.c_void_p(stream)))
     return out, (lse if return_lse else None)

@@ -30,6 +30,8 @@ struct FwdParams {
   float scale;        // softmax scale
   float scale_log2;   // scale * log2(e)
   float soft_cap;     // > 0 when the cap is on
+  int32_t mle;        // 1: constant max logit instead of the running max
+  float mle_log2;     // that constant times log2(e)
   // work-group -> (head, row) mapping
   int32_t xcd_units;      // number of units spread over XCDs (0: plain order)
   int32_t unit_heads;     // query heads per unit

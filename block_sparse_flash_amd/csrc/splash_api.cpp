@@ -82,6 +82,10 @@ extern "C" int splash_attn_fwd(const splash_fwd_args* args, void* stream) {
     return splash::fail(SPLASH_EINVAL, "splash_attn_fwd: scale must be finite and > 0");
   if (std::isnan(a.soft_cap) || std::isinf(a.soft_cap))
     return splash::fail(SPLASH_EINVAL, "splash_attn_fwd: soft_cap must be finite");
+  if (a.use_max_logit != 0 && a.use_max_logit != 1)
+    return splash::fail(SPLASH_EINVAL, "splash_attn_fwd: use_max_logit must be 0 or 1");
+  if (a.use_max_logit && !std::isfinite(a.max_logit))
+    return splash::fail(SPLASH_EINVAL, "splash_attn_fwd: max_logit must be finite");
   if (!a.seg_q && a.seg_kv)
     return splash::fail(SPLASH_EINVAL, "splash_attn_fwd: seg_kv given without seg_q");
 
@@ -144,6 +148,8 @@ extern "C" int splash_attn_fwd(const splash_fwd_args* args, void* stream) {
   p.scale = a.scale;
   p.scale_log2 = a.scale * 1.4426950408889634f;
   p.soft_cap = a.soft_cap > 0.0f ? a.soft_cap : 0.0f;
+  p.mle = a.use_max_logit;
+  p.mle_log2 = a.use_max_logit ? a.max_logit * 1.4426950408889634f : 0.0f;
   choose_xcd_units(a, &p);
 
   hipStream_t s = static_cast<hipStream_t>(stream);

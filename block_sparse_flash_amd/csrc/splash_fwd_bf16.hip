@@ -319,7 +319,10 @@ void splash_fwd_bf16_kernel(FwdParams p) {
   // Softmax state (z in log2 units after multiplying by zc):
   //   no cap: z = q.k, zc = scale log2(e);  cap: z = log2(e) cap tanh(scale q.k / cap), zc = 1.
   const float zc = CAP ? 1.0f : p.scale_log2;
-  float mref = -INFINITY;
+  // Reference max (z units).  With the max logit estimate (section 5.4) it
+  // is the given constant and never moves: no max reduction, no rescale.
+  const bool mle = p.mle != 0;
+  float mref = mle ? p.mle_log2 / zc : -INFINITY;
   float lsum = 0.0f;
   f32x16 oacc[DT];
   sfor<0, DT>([&](auto i_) { oacc[SIDX(i_)] = f32x16{}; });
@@ -527,7 +530,7 @@ void splash_fwd_bf16_kernel(FwdParams p) {
             const float m0 = fmaxf(mxt[0], mxt[1]);
             const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(m0), __float_as_uint(m0), false, false);
             const float mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-            const bool need = mx * zc > mref * zc + kTau;
+            const bool need = !mle && mx * zc > mref * zc + kTau;
             const float mnew = need ? mx : mref;
             alpha = (mnew == mref) ? 1.0f : fast_exp2((mref - mnew) * zc);
             mref = mnew;
@@ -619,7 +622,7 @@ void splash_fwd_bf16_kernel(FwdParams p) {
     constexpr int GW = NW / 2;               // waves per group
     const bool grp1 = wave >= GW;
     const int gw = wave - (grp1 ? GW : 0);   // wave index inside its group
-    float mc = 0.0f;              // reference exponent offset m zc (0 while m = -inf)
+    float mc = mle ? p.mle_log2 : 0.0f;  // reference exponent offset m zc (0 while m = -inf)
     float mthr = -INFINITY;       // m + kTau / zc: block maxima above it move m
 
     // Key segment ids of a block, for the element mask of partial blocks,
@@ -824,36 +827,39 @@ void splash_fwd_bf16_kernel(FwdParams p) {
         const bf16x8 q00 = pb[0][0], q01 = pb[0][1], q10 = pb[1][0], q11 = pb[1][1];
         asm volatile("" ::"v"(q00), "v"(q01), "v"(q10), "v"(q11), "v"(ps));
       }
-      // Row max: a tree over the lane's 32 scores, then the other half-wave.
-      // 32 -> 11 -> 4 -> 2 -> 1 with three-input maxima (16 instructions).
-      auto max3 = [](float a, float b, float c) __attribute__((always_inline)) {
-        return __builtin_fmaxf(__builtin_fmaxf(a, b), c);
-      };
-      auto el = [&](int k) __attribute__((always_inline)) { return sv[k / 16][k % 16]; };
-      float m11[11];
-      sfor<0, 10>([&](auto j_) {
-        constexpr int j = SIDX(j_);
-        m11[j] = max3(el(3 * j), el(3 * j + 1), el(3 * j + 2));
-      });
-      m11[10] = __builtin_fmaxf(el(30), el(31));
-      const float m4a = max3(m11[0], m11[1], m11[2]), m4b = max3(m11[3], m11[4], m11[5]);
-      const float m4c = max3(m11[6], m11[7], m11[8]), m4d = __builtin_fmaxf(m11[9], m11[10]);
-      float mx = __builtin_fmaxf(max3(m4a, m4b, m4c), m4d);
-      {
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-      }
-      // Lazy reference: a row moves only when its block max exceeds the
-      // reference by more than 2^kTau in the exponent (mthr = m + kTau / zc).
-      if (__any(mx > mthr)) {
-        const float mnew = (mx > mthr) ? mx : mref;
-        const float alpha = (mnew == mref) ? 1.0f : fast_exp2((mref - mnew) * zc);
-        mref = mnew;
-        mc = (mnew == -INFINITY) ? 0.0f : mnew * zc;
-        mthr = mnew + kTau / zc;
-        ps = exps(sv, mc, [&](auto) __attribute__((always_inline)) {}, Idx<0>{});
-        lsum *= alpha;
-        sfor<0, DT>([&](auto i_) { oacc[SIDX(i_)] *= alpha; });
+      // With the max logit estimate the reference is fixed: no max at all.
+      if (!mle) {
+        // Row max: a tree over the lane's 32 scores, then the other half-wave.
+        // 32 -> 11 -> 4 -> 2 -> 1 with three-input maxima (16 instructions).
+        auto max3 = [](float a, float b, float c) __attribute__((always_inline)) {
+          return __builtin_fmaxf(__builtin_fmaxf(a, b), c);
+        };
+        auto el = [&](int k) __attribute__((always_inline)) { return sv[k / 16][k % 16]; };
+        float m11[11];
+        sfor<0, 10>([&](auto j_) {
+          constexpr int j = SIDX(j_);
+          m11[j] = max3(el(3 * j), el(3 * j + 1), el(3 * j + 2));
+        });
+        m11[10] = __builtin_fmaxf(el(30), el(31));
+        const float m4a = max3(m11[0], m11[1], m11[2]), m4b = max3(m11[3], m11[4], m11[5]);
+        const float m4c = max3(m11[6], m11[7], m11[8]), m4d = __builtin_fmaxf(m11[9], m11[10]);
+        float mx = __builtin_fmaxf(max3(m4a, m4b, m4c), m4d);
+        {
+          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+          mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        }
+        // Lazy reference: a row moves only when its block max exceeds the
+        // reference by more than 2^kTau in the exponent (mthr = m + kTau / zc).
+        if (__any(mx > mthr)) {
+          const float mnew = (mx > mthr) ? mx : mref;
+          const float alpha = (mnew == mref) ? 1.0f : fast_exp2((mref - mnew) * zc);
+          mref = mnew;
+          mc = (mnew == -INFINITY) ? 0.0f : mnew * zc;
+          mthr = mnew + kTau / zc;
+          ps = exps(sv, mc, [&](auto) __attribute__((always_inline)) {}, Idx<0>{});
+          lsum *= alpha;
+          sfor<0, DT>([&](auto i_) { oacc[SIDX(i_)] *= alpha; });
+        }
       }
       lsum += ps;
       // P and l stay in this half-step (not sunk past the barrier).
@@ -994,7 +1000,7 @@ void splash_fwd_bf16_kernel(FwdParams p) {
         mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
       }
       // Lazy reference update: move only when the block max exceeds it by > 2^kTau.
-      const bool need = mx * zc > mref * zc + kTau;
+      const bool need = !mle && mx * zc > mref * zc + kTau;
       const float mnew = need ? mx : mref;
       const float alpha = (mnew == mref) ? 1.0f : fast_exp2((mref - mnew) * zc);
       mref = mnew;

@@ -65,7 +65,9 @@ __global__ __launch_bounds__(64) void splash_fwd_f32_kernel(FwdParams p) {
   float o[DV];
 #pragma unroll
   for (int d = 0; d < DV; ++d) o[d] = 0.0f;
-  float m = -INFINITY;  // running max of z (log2 units)
+  // Running max of z (log2 units); with the max logit estimate a constant.
+  const bool mle = p.mle != 0;
+  float m = mle ? p.mle_log2 : -INFINITY;
   float l = 0.0f;
 
   const int32_t* segq = p.seg_q ? p.seg_q + (int64_t)b * L : nullptr;
@@ -119,7 +121,7 @@ __global__ __launch_bounds__(64) void splash_fwd_f32_kernel(FwdParams p) {
         z[j] = zz;
         zmax = fmaxf(zmax, zz);
       }
-      const float m_new = fmaxf(m, zmax);
+      const float m_new = mle ? m : fmaxf(m, zmax);
       const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
       const float alpha = fast_exp2(m - m_use);
       float psum = 0.0f;

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define SPLASH_VERSION 100
+#define SPLASH_VERSION 101
 
 enum splash_status {
   SPLASH_OK = 0,
@@ -203,12 +203,24 @@ typedef struct splash_fwd_args {
   float scale;           /* softmax scale, finite and > 0 (e.g. 1/sqrt(d_qk)) */
   float soft_cap;        /* logit soft cap; <= 0 disables it; logits are
                             cap * tanh(scale * q.k / cap) */
+  /* Max Logit Estimate (Lecture 13 section 5.4).  use_max_logit = 1: the
+   * constant max_logit (logit units: after the scale and the cap) replaces
+   * the running row max, so p = e^(logit - max_logit) with no max reduction
+   * and no rescale.  The constant cancels in o = sum p v / sum p, so o and
+   * lse = max_logit + ln(sum p) are those of the exact softmax as long as
+   * no exponent leaves the float32 range: max_logit must exceed the largest
+   * logit minus 88.7 (else p overflows) and stay below every row's largest
+   * logit plus 87.3 (else that row underflows to o = 0, lse = -inf).  With a
+   * soft cap, max_logit = soft_cap can never overflow.  0 = running max. */
+  int32_t use_max_logit;
+  float max_logit;       /* finite when use_max_logit = 1 */
 } splash_fwd_args;
 
 /* Enqueue the forward on `stream` (a hipStream_t; NULL = the default
  * stream) and return without waiting.  Validation errors are returned
  * synchronously: SPLASH_EINVAL (NULL args or buffers, misaligned pointer,
- * bad flag, scale <= 0 or not finite, soft_cap NaN), SPLASH_ESHAPE
+ * bad flag, scale <= 0 or not finite, soft_cap not finite, max_logit not
+ * finite with use_max_logit = 1), SPLASH_ESHAPE
  * (Hq % Hkv != 0, block sizes or n_q_blocks not matching, size overflow),
  * SPLASH_EDTYPE, SPLASH_EUNSUPPORTED (head dims), SPLASH_EHIP (the launch
  * failed).  B, Hq or L equal to 0 is a no-op.  Device-side faults surface at

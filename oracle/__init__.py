@@ -30,6 +30,7 @@ from .attention import (
     attention_brute,
     online_softmax_steps,
     merge_partials,
+    mle_safe_range,
 )
 from .mask_tables import mask_tables_ref
 
@@ -39,5 +40,6 @@ __all__ = [
     "attention_brute",
     "online_softmax_steps",
     "merge_partials",
+    "mle_safe_range",
     "mask_tables_ref",
 ]

@@ -76,7 +76,7 @@ def attention_ref(q, k, v, *, scale: float, soft_cap: float = 0.0,
                   window_right: int = -1, seg_q=None, seg_kv=None,
                   rows: Optional[Sequence[int]] = None,
                   heads: Optional[Iterable[tuple]] = None,
-                  panel: int = 512):
+                  panel: int = 512, max_logit: Optional[float] = None):
     """Exact masked attention forward in float64.
 
     Shapes: ``q`` [B, Hq, L_q, d_qk], ``k`` [B, Hkv, L_kv, d_qk],
@@ -94,6 +94,12 @@ def attention_ref(q, k, v, *, scale: float, soft_cap: float = 0.0,
       A_i  = { j allowed by causal AND window AND segment };
       m_i  = max_{j in A_i} s_ij;  p_ij = exp(s_ij - m_i) on A_i, else 0;
       l_i  = sum_j p_ij;  o_i = sum_j p_ij v_j / l_i;  lse_i = m_i + ln l_i.
+
+    ``max_logit`` = c selects the Max Logit Estimate (Lecture 13 section
+    5.4): the constant c takes the place of m_i in every row (p_ij =
+    exp(s_ij - c), lse_i = c + ln l_i).  In exact arithmetic c cancels, so
+    the result equals the one above; float64 keeps every exp in range for
+    |s - c| < 700.
     """
     q = np.asarray(q)
     k = np.asarray(k)
@@ -129,9 +135,12 @@ def attention_ref(q, k, v, *, scale: float, soft_cap: float = 0.0,
                         causal=causal, window_left=window_left,
                         window_right=window_right, seg_q=sq, seg_kv=skv)
             s_a = np.where(a, s, -np.inf)
-            m = s_a.max(axis=1)
-            has = np.isfinite(m)
-            m_safe = np.where(has, m, 0.0)
+            has = a.any(axis=1)
+            if max_logit is None:
+                m = s_a.max(axis=1)
+                m_safe = np.where(has, m, 0.0)
+            else:
+                m_safe = np.full(sel.shape[0], float(max_logit))
             p = np.where(a, np.exp(s_a - m_safe[:, None]), 0.0)
             l = p.sum(axis=1)
             l_safe = np.where(has, l, 1.0)
@@ -140,6 +149,21 @@ def attention_ref(q, k, v, *, scale: float, soft_cap: float = 0.0,
             lse[b, h, p0:p0 + sel.shape[0]] = np.where(
                 has, m_safe + np.log(l_safe), -np.inf)
     return o, lse
+
+
+# float32 limits of exp: e^x overflows above ln(FLT_MAX) and leaves the
+# normal range below ln(FLT_MIN) = ln(2^-126).
+LN_FLT_MAX = math.log(3.4028234663852886e38)
+LN_FLT_MIN = math.log(2.0 ** -126)
+
+
+def mle_safe_range(max_logit: float, min_row_max: float):
+    """Open interval of Max Logit Estimate constants c that keep float32
+    exp(s - c) finite for the largest logit and keep at least each row's
+    largest term normal (Lecture 13 section 5.4, exercise 10): the largest
+    logit minus c stays below ln(FLT_MAX) (88.72), and c minus the smallest
+    row maximum stays below -ln(FLT_MIN) (87.34)."""
+    return (float(max_logit) - LN_FLT_MAX, float(min_row_max) - LN_FLT_MIN)
 
 
 def attention_brute(q, k, v, *, scale: float, soft_cap: float = 0.0,

@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
     assert set(declared) == set(_lib.EXPORTED), declared
     for name in declared:
         assert hasattr(lib, name), name
-    assert lib.splash_version() == 100
+    assert lib.splash_version() == 101
 
 
 def _assert_tables_equal(t, ref):
@@ -186,6 +186,9 @@ def _good_args(**over):
     (dict(mask_mode=1, partial_mask_blocks=None), 1),
     (dict(seg_kv=0x10000), 1),
     (dict(n_active=-1), 1),
+    (dict(use_max_logit=2), 1),
+    (dict(use_max_logit=1, max_logit=math.nan), 1),
+    (dict(use_max_logit=1, max_logit=math.inf), 1),
 ])
 def test_forward_validation_errors(over, code):
     lib = _lib.load()

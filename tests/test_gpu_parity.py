@@ -17,7 +17,7 @@ torch = pytest.importorskip("torch")
 from block_sparse_flash_amd import compile_mask, fwd_tile, splash_fwd
 from block_sparse_flash_amd.inputs import (WORKLOADS, as_f64, draw_qkv, make_inputs,
                                            segment_ids, stored)
-from oracle import attention_ref
+from oracle import allowed, attention_ref, mle_safe_range
 
 pytestmark = pytest.mark.gpu
 
@@ -86,6 +86,69 @@ def test_small_cases_every_element(case):
                                    soft_cap=cap, seg_q=seg, **mk)
     eo, el = _compare(o, lse, o_ref, lse_ref, dtype)
     _announce(f"  max-abs o {eo:.3g} lse {el:.3g}")
+
+
+def _logit_extremes(q, k, scale, cap, mk, seg):
+    """Largest allowed logit and smallest row maximum (float64)."""
+    qf, kf = as_f64(q), as_f64(k)
+    B, Hq, L, _ = qf.shape
+    group = Hq // kf.shape[1]
+    i = np.arange(L)[:, None]
+    j = np.arange(L)[None, :]
+    a = allowed(i, j, L_q=L, L_kv=L, causal=mk.get("causal", False),
+                window_left=mk.get("window_left", -1), window_right=mk.get("window_right", -1),
+                seg_q=seg)
+    smax, rmin = -np.inf, np.inf
+    for b in range(B):
+        for h in range(Hq):
+            s = scale * (qf[b, h] @ kf[b, h // group].T)
+            if cap > 0:
+                s = cap * np.tanh(s / cap)
+            s = np.where(a, s, -np.inf)
+            rm = s.max(axis=1)
+            rm = rm[np.isfinite(rm)]
+            smax, rmin = max(smax, rm.max()), min(rmin, rm.min())
+    return float(smax), float(rmin)
+
+
+MLE_CASES = [
+    # (dtype, L, d_qk, d_v, mask kwargs, soft_cap, how the constant is chosen)
+    ("bf16", 777, 128, 128, dict(causal=True, segs=(40, 300)), 0.0, "max"),
+    ("bf16", 777, 128, 128, dict(causal=True, segs=(40, 300)), 0.0, "low"),
+    ("bf16", 777, 128, 128, dict(causal=True, segs=(40, 300)), 0.0, "high"),
+    ("bf16", 600, 128, 128, dict(causal=True, window_left=100), 20.0, "cap"),
+    ("bf16", 520, 192, 128, dict(causal=True), 0.0, "max"),
+    ("bf16", 300, 64, 64, dict(window_left=70, window_right=33), 0.0, "low"),
+    ("f32", 333, 64, 128, dict(causal=True, segs=(20, 90)), 5.0, "cap"),
+    ("f32", 256, 128, 128, dict(causal=True), 0.0, "high"),
+]
+
+
+@pytest.mark.parametrize("case", MLE_CASES, ids=lambda c: f"{c[0]}-L{c[1]}-d{c[2]}x{c[3]}-{c[6]}")
+def test_max_logit_estimate(case):
+    """Lecture 13 section 5.4: a constant in place of the running max gives
+    the softmax of the oracle (its running-max definition) as long as the
+    constant is inside the float32 safe range; "low" / "high" sit 60 inside
+    the overflow / underflow edges."""
+    dtype, L, dqk, dv, mk, cap, how = case
+    _announce(f"max logit estimate {case}")
+    seed = 4000 + L + dqk
+    q, k, v = (stored(a, dtype) for a in draw_qkv(1, 4, 2, L, dqk, dv, seed, qk_std=1.5 if cap else 1.0))
+    mk = dict(mk)
+    seg = None
+    if "segs" in mk:
+        lo, hi = mk.pop("segs")
+        seg = segment_ids(L, seed, lo, hi)
+    scale = 1.0 / math.sqrt(dqk)
+    smax, rmin = _logit_extremes(q, k, scale, cap, mk, seg)
+    c = {"max": smax, "low": smax - 60.0, "high": rmin + 60.0, "cap": cap}[how]
+    lo_c, hi_c = mle_safe_range(smax, rmin)
+    assert lo_c < c < hi_c
+    o, lse = _run(q, k, v, scale=scale, soft_cap=cap, seg_q=seg, max_logit=c, **mk)
+    o_ref, lse_ref = attention_ref(as_f64(q), as_f64(k), as_f64(v), scale=scale,
+                                   soft_cap=cap, seg_q=seg, **mk)
+    eo, el = _compare(o, lse, o_ref, lse_ref, dtype)
+    _announce(f"  c {c:.3f} (safe {lo_c:.1f}..{hi_c:.1f}) max-abs o {eo:.3g} lse {el:.3g}")
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])

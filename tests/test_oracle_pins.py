@@ -9,7 +9,7 @@ import scipy.special
 from hypothesis import given, settings, strategies as st
 
 from oracle import (allowed, attention_brute, attention_ref, merge_partials,
-                    online_softmax_steps)
+                    mle_safe_range, online_softmax_steps)
 from tests.conftest import read_golden
 
 
@@ -193,3 +193,43 @@ def test_allowed_definition_examples():
     # right window only
     a = allowed(i, j, L_q=6, L_kv=6, window_right=1)
     assert a[0, 1] and not a[0, 2] and a[5, 0]
+
+
+# ---------------------------------------------------------- max logit estimate
+
+
+def test_mle_safe_range_exercise10():
+    """The safe interval of the Max Logit Estimate constant against the
+    worked answer of Lecture 13 exercise 10 (section 5.4)."""
+    g = read_golden("mle_exercise10.txt")
+    lo, hi = mle_safe_range(float(g["max_logit"]), float(g["min_row_max"]))
+    assert abs(lo - float(g["lower"])) < 0.05      # 40 - 88.72
+    assert abs(hi - float(g["upper"])) < 0.5       # -30 + 87.34 (page rounds to 87)
+    # The float32 limits it uses are those of numpy's float32.
+    assert abs((40 - lo) - math.log(float(np.finfo(np.float32).max))) < 1e-12
+    assert abs((hi + 30) + math.log(float(np.finfo(np.float32).tiny))) < 1e-12
+
+
+@pytest.mark.parametrize("c", [-20.0, 0.0, 3.0, 60.0])
+@pytest.mark.parametrize("mask", [dict(causal=True), dict(causal=True, window_left=5),
+                                  dict(causal=False, seg="split"), dict(causal=True, cap=2.5)])
+def test_mle_constant_cancels(c, mask):
+    """Section 5.4: any constant in place of the row max gives the same
+    softmax; lse carries the constant back (lse = c + ln l)."""
+    rng = np.random.default_rng(7)
+    B, H, L, d = 2, 2, 24, 8
+    q = rng.standard_normal((B, H, L, d))
+    k = rng.standard_normal((B, H, L, d))
+    v = rng.standard_normal((B, H, L, d))
+    kw = dict(scale=0.5, causal=mask.get("causal", False),
+              window_left=mask.get("window_left", -1), soft_cap=mask.get("cap", 0.0))
+    if mask.get("seg") == "split":
+        kw["seg_q"] = np.repeat(np.arange(3), 8).astype(np.int32)
+    o0, l0 = attention_ref(q, k, v, **kw)
+    o1, l1 = attention_ref(q, k, v, max_logit=c, **kw)
+    assert np.max(np.abs(o1 - o0)) < 1e-12
+    assert np.max(np.abs(l1 - l0)) < 1e-10
+    # The unshifted brute-force definition agrees too.
+    ob, lb = attention_brute(q, k, v, **kw)
+    assert np.max(np.abs(o1 - np.asarray(ob))) < 1e-12
+    assert np.max(np.abs(l1 - np.asarray(lb))) < 1e-10
