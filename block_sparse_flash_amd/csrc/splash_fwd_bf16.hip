@@ -274,11 +274,10 @@ void splash_fwd_bf16_kernel(FwdParams p) {
   const u32x4 krs = uniform(make_rsrc(kg, (uint32_t)(L * DQK * 2)));
   const u32x4 vrs = uniform(make_rsrc(vg, (uint32_t)(L * DV * 2)));
 
-  // Zero the tile buffers once: a tile that hangs over the sequence end is
-  // then finite everywhere (its masked keys get zero weight).
-  for (int i = tid; i < C::LDS_BYTES / 16; i += NT)
-    *reinterpret_cast<lds_u32x4*>(lds + 16 * i) = u32x4{0u, 0u, 0u, 0u};
-  __syncthreads();  // the zero stores land before any wave's tile copies
+  // No LDS initialisation: every tile copy covers its whole tile (rows past
+  // the sequence end read as zero through the buffer range check) and the
+  // segment-id ring is only read where it was copied.  Without a barrier
+  // here the Q loads below and the first tile copies are in flight together.
 
   // Q^T as B operands: k-step s -> Q[qi][16s + 8hi + 0..7].
   bf16x8 qf[KS];
