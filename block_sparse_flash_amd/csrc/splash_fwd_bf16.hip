@@ -727,7 +727,11 @@ void splash_fwd_bf16_kernel(FwdParams p) {
       constexpr int NP = SIDX(pv_tag) ? 4 * DT : 0;
       constexpr int NQ = SIDX(sc_tag) ? 2 * KS : 0;
       using O = MatOrder<NP, NQ>;
-      constexpr int DIST = 3;  // operand reads run this many MFMAs ahead
+      // Operand reads run this many MFMAs ahead.  Each step below is fenced
+      // with a scheduling barrier: left to itself the compiler sinks every LDS
+      // read to just before its MFMA, which exposes the LDS latency on most
+      // of the phase's MFMAs.
+      constexpr int DIST = 6;
       const lds_u8* kb = kbuf(i & 1);         // K_i
       const lds_u8* vb = vbuf((i + 1) & 1);   // V_{i-1}
       bf16x8 opnd[O::N];
@@ -759,7 +763,10 @@ void splash_fwd_bf16_kernel(FwdParams p) {
         }
       };
       sfor<0, (DIST < O::N ? DIST : O::N)>([&](auto m_) { read_opnd(m_); });
-      sfor<0, O::N>(issue);
+      sfor<0, O::N>([&](auto m_) __attribute__((always_inline)) {
+        issue(m_);
+        __builtin_amdgcn_sched_barrier(0);
+      });
       // The scores stay in this half-step (not sunk past the barrier).
       if constexpr (NQ > 0) {
         const f32x16 a0 = sacc[0], a1 = sacc[1];
