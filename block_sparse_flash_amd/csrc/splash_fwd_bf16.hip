@@ -102,9 +102,6 @@ struct Cfg {
   static constexpr int SEG_OFF = NBUF * (KTILE + VTILE);  // key segment-id ring
   static constexpr int SEG_SLOTS = 3;          // ids of one block per slot
   static constexpr int LDS_BYTES = SEG_OFF + SEG_SLOTS * BN * 4;
-  static constexpr int KLOADS = KCHUNKS / NT;  // tile-copy instructions per wave
-  static constexpr int VLOADS = VCHUNKS / NT;
-  static_assert(KCHUNKS % NT == 0 && VCHUNKS % NT == 0, "tile chunks split evenly over the work-group");
   static_assert(LDS_BYTES <= 163840, "fits the LDS of a CU");
 };
 
@@ -234,9 +231,10 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <int DQK, int DV, bool CAP, int LOOP>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void splash_fwd_bf16_kernel(FwdParams p) {
+// One item: the 256 query rows of q-block row r of query head `head`
+// (flattened b * Hq + h), over the row's active kv blocks.
+template <int DQK, int DV, bool CAP>
+__device__ __forceinline__ void item_fwd(const FwdParams& p, int head, int r) {
   using C = Cfg<DQK, DV>;
   constexpr int KS = C::KS;
   constexpr int DT = C::DT;
@@ -252,13 +250,10 @@ void splash_fwd_bf16_kernel(FwdParams p) {
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  int head, rank;
-  map_workgroup(p, blockIdx.x, &head, &rank);
   const int b = head / p.Hq;
   const int hq = head - b * p.Hq;
   const int kvh = b * p.Hkv + hq / p.group;
   const int L = p.L;
-  const int r = ld_table(p.row_order, rank);
   const int qw = r * BM + wave * 32;  // first query row of this wave
   const int qi = qw + l32;            // this lane's query row
 
@@ -286,34 +281,6 @@ void splash_fwd_bf16_kernel(FwdParams p) {
     const int off = (qi * DQK + 16 * s + 8 * hi) * 2;
     qf[s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qrs, off, 0, 0));
   });
-
-  // Tile copies HBM -> LDS.  Each wave instruction writes 64 consecutive
-  // 16-byte LDS chunks; lane i fetches the global chunk that belongs in
-  // physical slot i of the swizzled layout.
-  auto load_k = [&](int c, int buf) __attribute__((always_inline)) {
-    const int k0 = c * BN;
-#pragma unroll
-    for (int t = 0; t < C::KLOADS; ++t) {
-      const int slot0 = (t * NW + wave) * 64;
-      const int slot = slot0 + lane;
-      const int row = slot / (DQK / 8);
-      const int pc = slot - row * (DQK / 8);
-      const int off = ((k0 + row) * DQK + kswz<C::KROW>(row, pc) * 8) * 2;
-      dma16(krs, (uint32_t)(uintptr_t)(kbuf(buf) + slot0 * 16), off);
-    }
-  };
-  auto load_v = [&](int c, int buf) __attribute__((always_inline)) {
-    const int k0 = c * BN;
-#pragma unroll
-    for (int t = 0; t < C::VLOADS; ++t) {
-      const int slot0 = (t * NW + wave) * 64;
-      const int slot = slot0 + lane;
-      const int row = slot / (DV / 8);
-      const int pc = slot - row * (DV / 8);
-      const int off = ((k0 + row) * DV + vswz<C::VROW>(row, pc) * 8) * 2;
-      dma16(vrs, (uint32_t)(uintptr_t)(vbuf(buf) + slot0 * 16), off);
-    }
-  };
 
   // Softmax state (z in log2 units after multiplying by zc):
   //   no cap: z = q.k, zc = scale log2(e);  cap: z = log2(e) cap tanh(scale q.k / cap), zc = 1.
@@ -394,208 +361,6 @@ void splash_fwd_bf16_kernel(FwdParams p) {
         constexpr int r = 32 * t + 8 * (i / 4) + (i % 4);
         const bool ok = (r >= lo) & (r <= up);
         sv[t][i] = ok ? sv[t][i] : -INFINITY;
-      });
-    }
-  };
-
-  // ---------------------------------------------------------------------
-  // Software-pipelined loop: iteration j runs softmax(S_j) on the vector
-  // unit while the matrix unit computes O += P_{j-1} V_{j-1} and then
-  // S_{j+1} = Q K_{j+1}^T.  Block x's K and V tiles live in buffer x % 2;
-  // iteration j copies K_{j+2} and V_j (into the buffers of K_j and V_{j-2},
-  // both finished before the barrier that opens iteration j).  P_{j-1} is
-  // consumed by the first MFMAs of the iteration before P_j is written, so
-  // one register set holds P.
-  auto pipelined_loop = [&]() __attribute__((always_inline)) {
-    f32x16 sacc[2][2];   // [register buffer][key tile]: S^T of block j / j+1
-    bf16x8 pb[2][2];     // [key tile][key half]: P^T, B operands of O^T += V^T P^T
-    auto read_kfrag = [&](const lds_u8* kb, int s, int t) __attribute__((always_inline)) {
-      const int key = 32 * t + l32;
-      return *reinterpret_cast<const lds_bf16x8*>(kb + key * C::KROW + kswz<C::KROW>(key, 2 * s + hi) * 16);
-    };
-    auto read_vfrag = [&](const lds_u8* vb, int t, int c2, int dt) __attribute__((always_inline)) {
-      const int row = 32 * t + 16 * c2 + vrow0;
-      const int row2 = row + 8;
-      const int lc = 4 * dt + vcol0;
-      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_i16x4*)(vb + row * C::VROW + vswz<C::VROW>(row, lc) * 16 + 8 * (jj & 1)));
-      const i16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_i16x4*)(vb + row2 * C::VROW + vswz<C::VROW>(row2, lc) * 16 + 8 * (jj & 1)));
-      const u32x2 lo2 = __builtin_bit_cast(u32x2, lo);
-      const u32x2 up2 = __builtin_bit_cast(u32x2, up);
-      return __builtin_bit_cast(bf16x8, u32x4{lo2[0], lo2[1], up2[0], up2[1]});
-    };
-
-    if (n > 0) {
-      load_k(cols[0], 0);
-      load_k(colc(1), 1);
-      wait_copies_and_barrier<0>();
-      sfor<0, KS>([&](auto s_) {
-        sfor<0, 2>([&](auto t_) {
-          constexpr int s = SIDX(s_), t = SIDX(t_);
-          const bf16x8 kf = read_kfrag(kbuf(0), s, t);
-          if constexpr (s == 0) {
-            const f32x16 zero = {};
-            sacc[0][t] = mfma(kf, qf[0], zero);
-          } else {
-            sacc[0][t] = mfma(kf, qf[s], sacc[0][t]);
-          }
-        });
-      });
-    }
-
-    constexpr int NPV = 4 * DT;                // O MFMAs per iteration
-    constexpr int NS = 2 * KS;                 // S MFMAs per iteration
-    constexpr int NCAP = CAP ? 4 : 0;
-    constexpr int NSLICE = NCAP + 3 + 8;
-    constexpr int DIST = 2;                    // operand reads run this many MFMAs ahead
-
-    // One iteration; FIRST skips the O MFMAs (there is no P_{-1}).
-    auto step = [&](int j, auto cur_tag, auto first_tag) __attribute__((always_inline)) {
-      constexpr int cur = SIDX(cur_tag);
-      constexpr int nxt = cur ^ 1;
-      constexpr bool FIRST = SIDX(first_tag) != 0;
-      constexpr int M0 = FIRST ? NPV : 0;      // first MFMA index issued
-      constexpr int NM = NPV + NS;
-      wait_copies_and_barrier<0>();
-      if (j + 2 < n) load_k(colc(j + 2), j & 1);
-      load_v(colc(j), j & 1);
-      f32x16* sv = sacc[cur];
-      // Partial block <=> it has a pattern (mask_next >= 0).
-      const bool partial = ld_table(p.mask_next, g0 + j) >= 0;
-
-      const lds_u8* kb = kbuf((j + 1) & 1);   // K_{j+1}
-      const lds_u8* vb = vbuf((j + 1) & 1);   // V_{j-1}
-      // MFMA m < NPV: O^T += V^T P^T for (key tile, key half) m / DT and
-      // d-tile m % DT; m >= NPV: S^T_{j+1} for k-step (m - NPV) / 2, key
-      // tile (m - NPV) % 2.
-      bf16x8 opnd[NM];
-      auto read_opnd = [&](auto m_) __attribute__((always_inline)) {
-        constexpr int m = SIDX(m_);
-        if constexpr (m < NPV) {
-          constexpr int tc = m / DT, dt = m % DT;
-          opnd[m] = read_vfrag(vb, tc / 2, tc % 2, dt);
-        } else {
-          constexpr int mm = m - NPV;
-          opnd[m] = read_kfrag(kb, mm / 2, mm % 2);
-        }
-      };
-      auto issue = [&](auto m_) __attribute__((always_inline)) {
-        constexpr int m = SIDX(m_);
-        if constexpr (m + DIST < NM) read_opnd(Idx<m + DIST>{});
-        if constexpr (m < NPV) {
-          constexpr int tc = m / DT, dt = m % DT;
-          oacc[dt] = mfma(opnd[m], pb[tc / 2][tc % 2], oacc[dt]);
-        } else {
-          constexpr int mm = m - NPV;
-          constexpr int s = mm / 2, t = mm % 2;
-          if constexpr (s == 0) {
-            const f32x16 zero = {};
-            sacc[nxt][t] = mfma(opnd[m], qf[0], zero);
-          } else {
-            sacc[nxt][t] = mfma(opnd[m], qf[s], sacc[nxt][t]);
-          }
-        }
-      };
-
-      float alpha = 1.0f, mc = 0.0f, ps = 0.0f;
-      float mxt[2];
-      auto slice = [&](auto i_) __attribute__((always_inline)) {
-        constexpr int i0 = SIDX(i_);
-        if constexpr (i0 < NCAP) {
-          // z = log2(e) cap tanh(scale q.k / cap), tanh y = 1 - 2 / (e^{2y} + 1).
-          constexpr int t = i0 / 2;
-          constexpr int e0 = (i0 % 2) * 8;
-          const float k2 = 2.0f * kLog2e * p.scale / p.soft_cap;
-          const float A = p.soft_cap * kLog2e;
-          sfor<e0, e0 + 8>([&](auto e_) {
-            constexpr int e = SIDX(e_);
-            const float ex = fast_exp2(sv[t][e] * k2);
-            sv[t][e] = A - 2.0f * A * __builtin_amdgcn_rcpf(ex + 1.0f);
-          });
-        } else {
-          constexpr int i = i0 - NCAP;
-          // The element mask comes after the cap (which maps -inf to -cap).
-          if constexpr (i == 0) {
-            if (partial) apply_mask(sv, j, colc(j));
-          }
-          if constexpr (i < 2) {
-            float m0 = sv[i][0];
-            sfor<1, 16>([&](auto e_) { m0 = fmaxf(m0, sv[i][SIDX(e_)]); });
-            mxt[i] = m0;
-          } else if constexpr (i == 2) {
-            // Row max across the two half-waves, then the lazy reference
-            // update: move only when the block max exceeds it by > 2^kTau.
-            const float m0 = fmaxf(mxt[0], mxt[1]);
-            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(m0), __float_as_uint(m0), false, false);
-            const float mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-            const bool need = !mle && mx * zc > mref * zc + kTau;
-            const float mnew = need ? mx : mref;
-            alpha = (mnew == mref) ? 1.0f : fast_exp2((mref - mnew) * zc);
-            mref = mnew;
-            mc = (mnew == -INFINITY) ? 0.0f : mnew * zc;
-          } else {
-            // p = 2^(z zc - m zc) for items 4(k%2) .. +3 of (tile, key half).
-            constexpr int k = i - 3;           // 0..7
-            constexpr int t = k / 4;
-            constexpr int c2 = (k / 2) % 2;
-            constexpr int h = k % 2;
-            u32x2 w;
-            sfor<0, 2>([&](auto e_) {
-              constexpr int e2 = 2 * h + SIDX(e_);
-              const float p0 = fast_exp2(fmaf(sv[t][8 * c2 + 2 * e2], zc, -mc));
-              const float p1 = fast_exp2(fmaf(sv[t][8 * c2 + 2 * e2 + 1], zc, -mc));
-              ps += p0 + p1;
-              w[SIDX(e_)] = pack_bf16(p0, p1);
-            });
-            u32x4 cur4 = __builtin_bit_cast(u32x4, pb[t][c2]);
-            cur4[2 * h] = w[0];
-            cur4[2 * h + 1] = w[1];
-            pb[t][c2] = __builtin_bit_cast(bf16x8, cur4);
-            if constexpr (k == 7) lsum = lsum * alpha + ps;
-          }
-        }
-      };
-
-      sfor<M0, M0 + DIST>([&](auto m_) { read_opnd(m_); });
-      sfor<0, NSLICE>([&](auto i_) {
-        constexpr int i = SIDX(i_);
-        constexpr int m0 = M0 + i * (NM - M0) / NSLICE;
-        constexpr int m1 = M0 + (i + 1) * (NM - M0) / NSLICE;
-        sfor<m0, m1>(issue);
-        slice(i_);
-        __builtin_amdgcn_sched_barrier(0);
-      });
-      // Keep P and l computed here, beside the MFMAs, rather than sunk past
-      // the branch and barrier below.
-      {
-        const bf16x8 q00 = pb[0][0], q01 = pb[0][1], q10 = pb[1][0], q11 = pb[1][1];
-        const float l0 = lsum;
-        asm volatile("" ::"v"(q00), "v"(q01), "v"(q10), "v"(q11), "v"(l0));
-      }
-      // O holds P_{j-1} V_{j-1}; move it to the new reference.
-      if (__any(alpha != 1.0f)) {
-        sfor<0, DT>([&](auto i_) { oacc[SIDX(i_)] *= alpha; });
-      }
-    };
-
-    if (n > 0) step(0, Idx<0>{}, Idx<1>{});
-    int j = 1;
-    for (; j + 1 < n; j += 2) {
-      step(j, Idx<1>{}, Idx<0>{});
-      step(j + 1, Idx<0>{}, Idx<0>{});
-    }
-    if (j < n) step(j, Idx<1>{}, Idx<0>{});
-    // Last block's P V (V_{n-1} was copied in the last iteration).
-    wait_copies_and_barrier<0>();
-    if (n > 0) {
-      const lds_u8* vb = vbuf((n - 1) & 1);
-      sfor<0, 4>([&](auto tc_) {
-        constexpr int tc = SIDX(tc_);
-        sfor<0, DT>([&](auto dt_) {
-          constexpr int dt = SIDX(dt_);
-          oacc[dt] = mfma(read_vfrag(vb, tc / 2, tc % 2, dt), pb[tc / 2][tc % 2], oacc[dt]);
-        });
       });
     }
   };
@@ -727,11 +492,12 @@ void splash_fwd_bf16_kernel(FwdParams p) {
       constexpr int NP = SIDX(pv_tag) ? 4 * DT : 0;
       constexpr int NQ = SIDX(sc_tag) ? 2 * KS : 0;
       using O = MatOrder<NP, NQ>;
-      // Operand reads run this many MFMAs ahead.  Each step below is fenced
+      // Operand reads run this many MFMAs ahead (fewer with 192-wide heads,
+      // whose Q fragments leave fewer registers).  Each step below is fenced
       // with a scheduling barrier: left to itself the compiler sinks every LDS
       // read to just before its MFMA, which exposes the LDS latency on most
       // of the phase's MFMAs.
-      constexpr int DIST = 6;
+      constexpr int DIST = DQK > 128 ? 3 : 6;
       const lds_u8* kb = kbuf(i & 1);         // K_i
       const lds_u8* vb = vbuf((i + 1) & 1);   // V_{i-1}
       bf16x8 opnd[O::N];
@@ -948,117 +714,7 @@ void splash_fwd_bf16_kernel(FwdParams p) {
       run(Idx<0>{});
   };
 
-  if constexpr (LOOP == 0) {
-    if (n > 0) {
-      load_k(cols[0], 0);
-      load_v(cols[0], 0);
-    }
-
-    for (int j = 0; j < n; ++j) {
-      const int buf = j & 1;
-      // Block j's copies (issued one iteration earlier) have landed and every
-      // wave is past iteration j-1, so buffer buf^1 is free: copy block j+1
-      // into it while block j is computed.
-      wait_copies_and_barrier<0>();
-      if (j + 1 < n) {
-        load_k(colc(j + 1), buf ^ 1);
-        load_v(colc(j + 1), buf ^ 1);
-      }
-
-      const lds_u8* kb = kbuf(buf);
-      const lds_u8* vb = vbuf(buf);
-
-      // S^T for the two 32-key tiles (two independent accumulation chains).
-      f32x16 sv[2];
-      sfor<0, KS>([&](auto s_) {
-        constexpr int s = SIDX(s_);
-        sfor<0, 2>([&](auto t_) {
-          constexpr int t = SIDX(t_);
-          const int key = 32 * t + l32;
-          const bf16x8 kf = *reinterpret_cast<const lds_bf16x8*>(kb + key * C::KROW + kswz<C::KROW>(key, 2 * s + hi) * 16);
-          if constexpr (s == 0) {
-            const f32x16 zero = {};
-            sv[t] = mfma(kf, qf[0], zero);
-          } else {
-            sv[t] = mfma(kf, qf[s], sv[t]);
-          }
-        });
-      });
-
-      if constexpr (CAP) {
-        const float k2 = 2.0f * kLog2e * p.scale / p.soft_cap;
-        const float A = p.soft_cap * kLog2e;
-        sfor<0, 32>([&](auto i_) {
-          constexpr int t = SIDX(i_) / 16;
-          constexpr int e = SIDX(i_) % 16;
-          const float ex = fast_exp2(sv[t][e] * k2);
-          sv[t][e] = A - 2.0f * A * __builtin_amdgcn_rcpf(ex + 1.0f);
-        });
-      }
-      // Partial block <=> it has a pattern (mask_next >= 0); int32 scalar load.
-      if (ld_table(p.mask_next, g0 + j) >= 0) apply_mask(sv, j, colc(j));
-
-      // Row max: in-lane over 32 keys, then across the two half-waves.
-      float mx = sv[0][0];
-      sfor<1, 32>([&](auto i_) { mx = fmaxf(mx, sv[SIDX(i_) / 16][SIDX(i_) % 16]); });
-      {
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-      }
-      // Lazy reference update: move only when the block max exceeds it by > 2^kTau.
-      const bool need = !mle && mx * zc > mref * zc + kTau;
-      const float mnew = need ? mx : mref;
-      const float alpha = (mnew == mref) ? 1.0f : fast_exp2((mref - mnew) * zc);
-      mref = mnew;
-      const float mc = (mnew == -INFINITY) ? 0.0f : mnew * zc;
-
-      // p = 2^(z zc - m zc), packed as bf16 B operands: tile t, key half c2.
-      bf16x8 pb[2][2];
-      float ps = 0.0f;
-      sfor<0, 4>([&](auto i_) {
-        constexpr int t = SIDX(i_) / 2;
-        constexpr int c2 = SIDX(i_) % 2;
-        u32x4 w;
-        sfor<0, 4>([&](auto e_) {
-          constexpr int e2 = SIDX(e_);
-          const float p0 = fast_exp2(fmaf(sv[t][8 * c2 + 2 * e2], zc, -mc));
-          const float p1 = fast_exp2(fmaf(sv[t][8 * c2 + 2 * e2 + 1], zc, -mc));
-          ps += p0 + p1;
-          w[e2] = pack_bf16(p0, p1);
-        });
-        pb[t][c2] = __builtin_bit_cast(bf16x8, w);
-      });
-      lsum = lsum * alpha + ps;
-      if (__any(alpha != 1.0f)) {
-        sfor<0, DT>([&](auto i_) { oacc[SIDX(i_)] *= alpha; });
-      }
-
-      // O^T += V^T P^T; key-half-major order keeps the DT accumulators
-      // independent between consecutive MFMAs.
-      sfor<0, 4>([&](auto tc_) {
-        constexpr int t = SIDX(tc_) / 2;
-        constexpr int c2 = SIDX(tc_) % 2;
-        const int row = 32 * t + 16 * c2 + vrow0;
-        const int row2 = row + 8;
-        sfor<0, DT>([&](auto dt_) {
-          constexpr int dt = SIDX(dt_);
-          const int lc = 4 * dt + vcol0;
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_i16x4*)(vb + row * C::VROW + vswz<C::VROW>(row, lc) * 16 + 8 * (jj & 1)));
-          const i16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_i16x4*)(vb + row2 * C::VROW + vswz<C::VROW>(row2, lc) * 16 + 8 * (jj & 1)));
-          const u32x2 lo2 = __builtin_bit_cast(u32x2, lo);
-          const u32x2 up2 = __builtin_bit_cast(u32x2, up);
-          const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{lo2[0], lo2[1], up2[0], up2[1]});
-          oacc[dt] = mfma(vf, pb[t][c2], oacc[dt]);
-        });
-      });
-    }
-  } else if constexpr (LOOP == 1) {
-    pipelined_loop();
-  } else {
-    pingpong_loop();
-  }
+  pingpong_loop();
 
   // Epilogue: o = O / l, lse = (m zc + log2 l) ln 2.
   const float lt = lsum + __shfl_xor(lsum, 32);
@@ -1077,52 +733,87 @@ void splash_fwd_bf16_kernel(FwdParams p) {
   }
 }
 
-template <int DQK, int DV, bool CAP, int LOOP>
-hipError_t launch(const FwdParams& p, hipStream_t s) {
-  const int64_t n_wg = (int64_t)p.B * p.Hq * p.n_q_blocks;
+// Work-group schedule (persistent): the grid has at most one work-group per
+// CU; work-group w processes items w, w + G, w + 2G, ... (G = grid size) of
+// the XCD-aware, longest-row-first item order, one after another.  Odd
+// rounds run backwards inside each XCD, so that a work-group that took one
+// of the longest rows in one round takes one of the shortest in the next:
+// the per-CU sums of causal row lengths come out equal.  A CU thus never
+// waits for a work-group launch between items.
+__device__ __forceinline__ int item_of_round(int k, int w, int G, bool snake) {
+  if (snake && (k & 1)) {
+    const int S = G / kNumXcd;
+    return k * G + kNumXcd * (S - 1 - w / kNumXcd) + w % kNumXcd;
+  }
+  return k * G + w;
+}
+
+template <int DQK, int DV, bool CAP>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void splash_fwd_bf16_kernel(FwdParams p) {
+  const int w = blockIdx.x;
+  const int G = gridDim.x;
+  const int T = p.B * p.Hq * p.n_q_blocks;
+  const bool snake = (G % kNumXcd) == 0;
+  for (int k = 0; k * G < T; ++k) {
+    const int t = item_of_round(k, w, G, snake);
+    if (t >= T) continue;
+    int head, rank;
+    map_workgroup(p, t, &head, &rank);
+    item_fwd<DQK, DV, CAP>(p, head, ld_table(p.row_order, rank));
+  }
+}
+
+// Grid size: one work-group per CU for masks whose rows cost what their
+// block counts say (causal, windows), where the static round schedule is
+// balanced; with segment ids, rows mix partial and full blocks unevenly and
+// the hardware's dynamic dispatch of one work-group per item balances better
+// (a grid of one work-group per item is the same kernel with one round).
+template <int DQK, int DV, bool CAP>
+hipError_t launch(const FwdParams& p, int n_cu, hipStream_t s) {
+  const int64_t n_items = (int64_t)p.B * p.Hq * p.n_q_blocks;
+  const bool persistent = p.seg_q == nullptr;
+  const int64_t grid = (persistent && n_items > n_cu) ? n_cu : n_items;
   const int bytes = Cfg<DQK, DV>::LDS_BYTES;
-  auto fn = splash_fwd_bf16_kernel<DQK, DV, CAP, LOOP>;
+  auto fn = splash_fwd_bf16_kernel<DQK, DV, CAP>;
   if (bytes > 65536) {
     // Opt in to more than 64 KiB of dynamic LDS (gfx950 has 160 KiB per CU).
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                               hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
     (void)hipGetLastError();
   }
-  hipLaunchKernelGGL(fn, dim3((unsigned)n_wg), dim3(NT), bytes, s, p);
+  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(NT), bytes, s, p);
   return hipGetLastError();
 }
 
-int loop_mode() {
-  static const int v = [] {
-    const char* e = getenv("SPLASH_BF16_LOOP");
-    return e ? atoi(e) : 2;
-  }();
-  return v;
-}
-
-template <int DQK, int DV, bool CAP>
-hipError_t launch_loop(const FwdParams& p, hipStream_t s) {
-  switch (loop_mode()) {
-    case 0: return launch<DQK, DV, CAP, 0>(p, s);
-    case 1: return launch<DQK, DV, CAP, 1>(p, s);
-    default: return launch<DQK, DV, CAP, 2>(p, s);
-  }
-}
-
 template <int DQK, int DV>
-hipError_t launch_cap(const FwdParams& p, hipStream_t s) {
-  return p.soft_cap > 0.0f ? launch_loop<DQK, DV, true>(p, s) : launch_loop<DQK, DV, false>(p, s);
+hipError_t launch_cap(const FwdParams& p, int n_cu, hipStream_t s) {
+  return p.soft_cap > 0.0f ? launch<DQK, DV, true>(p, n_cu, s) : launch<DQK, DV, false>(p, n_cu, s);
+}
+
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
 }
 
 }  // namespace
 
 hipError_t launch_fwd_bf16(const FwdParams& p, int d_qk, int d_v, hipStream_t s) {
-  if (d_qk == 128 && d_v == 128) return launch_cap<128, 128>(p, s);
-  if (d_qk == 192 && d_v == 128) return launch_cap<192, 128>(p, s);
-  if (d_qk == 64 && d_v == 64) return launch_cap<64, 64>(p, s);
-  if (d_qk == 128 && d_v == 64) return launch_cap<128, 64>(p, s);
-  if (d_qk == 64 && d_v == 128) return launch_cap<64, 128>(p, s);
-  if (d_qk == 192 && d_v == 64) return launch_cap<192, 64>(p, s);
+  const int n_cu = device_cus();
+  if (d_qk == 128 && d_v == 128) return launch_cap<128, 128>(p, n_cu, s);
+  if (d_qk == 192 && d_v == 128) return launch_cap<192, 128>(p, n_cu, s);
+  if (d_qk == 64 && d_v == 64) return launch_cap<64, 64>(p, n_cu, s);
+  if (d_qk == 128 && d_v == 64) return launch_cap<128, 64>(p, n_cu, s);
+  if (d_qk == 64 && d_v == 128) return launch_cap<64, 128>(p, n_cu, s);
+  if (d_qk == 192 && d_v == 64) return launch_cap<192, 64>(p, n_cu, s);
   return hipErrorInvalidValue;
 }
 

@@ -177,6 +177,20 @@ def test_per_batch_segments_and_gqa():
     _compare(o, lse, o_ref, lse_ref, "bf16")
 
 
+def test_more_items_than_work_groups():
+    """288 (head, q-block row) items on at most one work-group per CU: two
+    rounds, the second partial and run in reverse order inside each XCD;
+    every output element is checked."""
+    _announce("persistent rounds: B=2 Hq=36 Hkv=6 L=1000 d=64, causal + window 300")
+    B, Hq, Hkv, L, d = 2, 36, 6, 1000, 64
+    q, k, v = (stored(a, "bf16") for a in draw_qkv(B, Hq, Hkv, L, d, d, 31))
+    mk = dict(causal=True, window_left=300)
+    o, lse = _run(q, k, v, **mk)
+    o_ref, lse_ref = attention_ref(as_f64(q), as_f64(k), as_f64(v), scale=d ** -0.5, **mk)
+    eo, el = _compare(o, lse, o_ref, lse_ref, "bf16")
+    _announce(f"  max-abs o {eo:.3g} lse {el:.3g}")
+
+
 def test_empty_problem_is_noop():
     _announce("empty problem")
     q = torch.zeros((1, 2, 0, 128), dtype=torch.bfloat16, device="cuda")
