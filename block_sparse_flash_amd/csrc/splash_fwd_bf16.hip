@@ -284,7 +284,11 @@ __device__ __forceinline__ void item_fwd(const FwdParams& p, int head, int r) {
 
   // Softmax state (z in log2 units after multiplying by zc):
   //   no cap: z = q.k, zc = scale log2(e);  cap: z = log2(e) cap tanh(scale q.k / cap), zc = 1.
+  // With the cap the score registers hold u = 1 / (e^{2y} + 1), y = scale q.k / cap,
+  // from which z = A - 2A u (A = log2(e) cap) is folded into later
+  // multiply-adds; z is decreasing in u, so a masked pair holds u = +inf.
   const float zc = CAP ? 1.0f : p.scale_log2;
+  constexpr float kMasked = CAP ? INFINITY : -INFINITY;
   // Reference max (z units).  With the max logit estimate (section 5.4) it
   // is the given constant and never moves: no max reduction, no rescale.
   const bool mle = p.mle != 0;
@@ -333,7 +337,7 @@ __device__ __forceinline__ void item_fwd(const FwdParams& p, int head, int r) {
         const uint32_t bits = *reinterpret_cast<const uint32_t*>(prow + 32 * t + 8 * q4 + 4 * hi);
         sfor<0, 4>([&](auto e_) {
           constexpr int e = SIDX(e_);
-          sv[t][4 * q4 + e] = ((bits >> (8 * e)) & 0xffu) ? sv[t][4 * q4 + e] : -INFINITY;
+          sv[t][4 * q4 + e] = ((bits >> (8 * e)) & 0xffu) ? sv[t][4 * q4 + e] : kMasked;
         });
       });
       return;
@@ -349,7 +353,7 @@ __device__ __forceinline__ void item_fwd(const FwdParams& p, int head, int r) {
         constexpr int i = SIDX(i_) % 16;
         const int key = ka + 32 * t + 8 * (i / 4) + 4 * hi + (i % 4);
         const bool ok = (key >= klo) & (key <= khi) & (segk[min(key, L - 1)] == my_seg);
-        sv[t][i] = ok ? sv[t][i] : -INFINITY;
+        sv[t][i] = ok ? sv[t][i] : kMasked;
       });
     } else {
       // Key offset minus 4 hi against the shifted interval (constants on one side).
@@ -360,7 +364,7 @@ __device__ __forceinline__ void item_fwd(const FwdParams& p, int head, int r) {
         constexpr int i = SIDX(i_) % 16;
         constexpr int r = 32 * t + 8 * (i / 4) + (i % 4);
         const bool ok = (r >= lo) & (r <= up);
-        sv[t][i] = ok ? sv[t][i] : -INFINITY;
+        sv[t][i] = ok ? sv[t][i] : kMasked;
       });
     }
   };
@@ -416,7 +420,7 @@ __device__ __forceinline__ void item_fwd(const FwdParams& p, int head, int r) {
           constexpr int e = SIDX(e_);
           constexpr int r = 32 * t + 8 * q4 + e;
           const bool ok = (r >= lo) & (r <= up) & ((int)ids[e] == my_seg);
-          sv[t][4 * q4 + e] = ok ? sv[t][4 * q4 + e] : -INFINITY;
+          sv[t][4 * q4 + e] = ok ? sv[t][4 * q4 + e] : kMasked;
         });
       });
     };
@@ -547,8 +551,12 @@ __device__ __forceinline__ void item_fwd(const FwdParams& p, int head, int r) {
     // almost never moves, so P is computed with the current offset while the
     // block max is reduced (a tree, in parallel); only when some row's max
     // passes its threshold does the wave move the reference and recompute.
+    // Exponent of an item: z zc - mc, as one multiply-add (cap: (A - mc) - 2A u).
+    const float capA = CAP ? p.soft_cap * kLog2e : 0.0f;
+    const float ea = CAP ? -2.0f * capA : zc;
     auto exps = [&](f32x16* sv, float mcv, auto copy, auto ncopy_tag) __attribute__((always_inline)) {
       constexpr int NCOPY = SIDX(ncopy_tag);
+      const float eb = CAP ? capA - mcv : -mcv;
       float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
       sfor<0, 4>([&](auto i_) {
         constexpr int t = SIDX(i_) / 2;
@@ -557,8 +565,8 @@ __device__ __forceinline__ void item_fwd(const FwdParams& p, int head, int r) {
         sfor<0, 4>([&](auto e_) {
           constexpr int e2 = SIDX(e_);
           constexpr int q = 4 * SIDX(i_) + e2;   // pair index 0..15
-          const float p0 = fast_exp2(fmaf(sv[t][8 * c2 + 2 * e2], zc, -mcv));
-          const float p1 = fast_exp2(fmaf(sv[t][8 * c2 + 2 * e2 + 1], zc, -mcv));
+          const float p0 = fast_exp2(fmaf(sv[t][8 * c2 + 2 * e2], ea, eb));
+          const float p1 = fast_exp2(fmaf(sv[t][8 * c2 + 2 * e2 + 1], ea, eb));
           ps[q & 3] += p0 + p1;
           w[e2] = pack_bf16(p0, p1);
           if constexpr ((q + 1) * NCOPY / 16 > q * NCOPY / 16) {
@@ -575,18 +583,16 @@ __device__ __forceinline__ void item_fwd(const FwdParams& p, int head, int r) {
     auto sm = [&](int i, auto copy, auto ncopy_tag) __attribute__((always_inline)) {
       f32x16* sv = sacc;
       if constexpr (CAP) {
-        // z = log2(e) cap tanh(scale q.k / cap), tanh y = 1 - 2 / (e^{2y} + 1).
+        // z = log2(e) cap tanh(y), tanh y = 1 - 2 / (e^{2y} + 1): keep u = 1 / (e^{2y} + 1).
         const float k2 = 2.0f * kLog2e * p.scale / p.soft_cap;
-        const float A = p.soft_cap * kLog2e;
         sfor<0, 32>([&](auto i_) {
           constexpr int t = SIDX(i_) / 16;
           constexpr int e = SIDX(i_) % 16;
-          const float ex = fast_exp2(sv[t][e] * k2);
-          sv[t][e] = A - 2.0f * A * __builtin_amdgcn_rcpf(ex + 1.0f);
+          sv[t][e] = __builtin_amdgcn_rcpf(fast_exp2(sv[t][e] * k2) + 1.0f);
         });
       }
       // Partial block <=> it has a pattern (mask_next >= 0); after the cap,
-      // which would map -inf to -cap.
+      // which would map a masked -inf to -cap.
       if (ld_table(p.mask_next, g0 + i) >= 0) {
         if (seg_lds)
           apply_mask_seg_lds(sv, colc(i), i % 3);
@@ -602,9 +608,13 @@ __device__ __forceinline__ void item_fwd(const FwdParams& p, int head, int r) {
       // With the max logit estimate the reference is fixed: no max at all.
       if (!mle) {
         // Row max: a tree over the lane's 32 scores, then the other half-wave.
-        // 32 -> 11 -> 4 -> 2 -> 1 with three-input maxima (16 instructions).
+        // 32 -> 11 -> 4 -> 2 -> 1 with three-input maxima (16 instructions);
+        // with the cap a tree of minima over u, z = A - 2A min u.
         auto max3 = [](float a, float b, float c) __attribute__((always_inline)) {
-          return __builtin_fmaxf(__builtin_fmaxf(a, b), c);
+          if constexpr (CAP)
+            return __builtin_fminf(__builtin_fminf(a, b), c);
+          else
+            return __builtin_fmaxf(__builtin_fmaxf(a, b), c);
         };
         auto el = [&](int k) __attribute__((always_inline)) { return sv[k / 16][k % 16]; };
         float m11[11];
@@ -612,10 +622,11 @@ __device__ __forceinline__ void item_fwd(const FwdParams& p, int head, int r) {
           constexpr int j = SIDX(j_);
           m11[j] = max3(el(3 * j), el(3 * j + 1), el(3 * j + 2));
         });
-        m11[10] = __builtin_fmaxf(el(30), el(31));
+        m11[10] = max3(el(30), el(31), el(31));
         const float m4a = max3(m11[0], m11[1], m11[2]), m4b = max3(m11[3], m11[4], m11[5]);
-        const float m4c = max3(m11[6], m11[7], m11[8]), m4d = __builtin_fmaxf(m11[9], m11[10]);
-        float mx = __builtin_fmaxf(max3(m4a, m4b, m4c), m4d);
+        const float m4c = max3(m11[6], m11[7], m11[8]);
+        float mx = max3(max3(m4a, m4b, m4c), m11[9], m11[10]);
+        if constexpr (CAP) mx = fmaf(mx, -2.0f * capA, capA);
         {
           const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
           mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
