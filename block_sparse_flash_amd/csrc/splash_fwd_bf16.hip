@@ -380,10 +380,10 @@ __device__ __forceinline__ void item_fwd(const FwdParams& p, int head, int r) {
   // pipe while the other works on the vector unit:
   //   half-step 2i:     group 0 MM(i)      group 1 SM(i-1)
   //   half-step 2i+1:   group 0 SM(i)      group 1 MM(i)
-  // Group 1 also moves the tiles: at the start of SM(i) (half-step 2i+2) it
-  // issues K_{i+2} and V_{i+1} into the buffers of K_i and V_{i-1}, last read
-  // by MM(i) in half-steps 2i and 2i+1; it waits for them at the end of
-  // MM(i+1) (half-step 2i+3), and MM(i+2) reads them from half-step 2i+4.
+  // The tiles of block i+2 (K) and i+1 (V) are copied in half-step 2i+2,
+  // into the buffers of K_i and V_{i-1} (last read by MM(i) in half-steps 2i
+  // and 2i+1), and MM(i+2) reads them from half-step 2i+4 (see run below for
+  // which group issues them).
   auto pingpong_loop = [&]() __attribute__((always_inline)) {
     static_assert(NW % 2 == 0, "two wave groups");
     if (n == 0) return;
@@ -491,10 +491,39 @@ __device__ __forceinline__ void item_fwd(const FwdParams& p, int head, int r) {
       return __builtin_bit_cast(bf16x8, u32x4{lo2[0], lo2[1], up2[0], up2[1]});
     };
 
+    // One tile-copy instruction of a group's share: k < KL copies part of a
+    // K tile (with the block's segment ids first), the rest part of a V tile.
+    constexpr int KL = C::KCHUNKS / (64 * GW);
+    constexpr int VL = C::VCHUNKS / (64 * GW);
+    auto copy_part = [&](auto k_, int ck, int kbf, int cv, int vbf, int sslot) __attribute__((always_inline)) {
+      constexpr int k = SIDX(k_);
+      if constexpr (k == 0) seg_copy(ck, sslot);
+      if constexpr (k < KL) {
+        const int slot0 = (k * GW + gw) * 64;
+        const int slot = slot0 + lane;
+        const int row = slot / (DQK / 8);
+        const int pc = slot - row * (DQK / 8);
+        const int off = ((ck * BN + row) * DQK + kswz<C::KROW>(row, pc) * 8) * 2;
+        dma16(krs, (uint32_t)(uintptr_t)(kbuf(kbf) + slot0 * 16), off);
+      } else {
+        const int slot0 = ((k - KL) * GW + gw) * 64;
+        const int slot = slot0 + lane;
+        const int row = slot / (DV / 8);
+        const int pc = slot - row * (DV / 8);
+        const int off = ((cv * BN + row) * DV + vswz<C::VROW>(row, pc) * 8) * 2;
+        dma16(vrs, (uint32_t)(uintptr_t)(vbuf(vbf) + slot0 * 16), off);
+      }
+    };
+    auto no_copy = [&](auto) __attribute__((always_inline)) {};
+
     // Matrix phase MM(i); the tags select the O product and the scores.
-    auto mm = [&](int i, auto pv_tag, auto sc_tag) __attribute__((always_inline)) {
+    // copy(Idx<k>) issues tile-copy instruction k of NCOPY, spread between
+    // the MFMAs: issuing a copy holds the wave for tens of cycles, which the
+    // matrix pipe spends on the MFMAs already issued.
+    auto mm = [&](int i, auto pv_tag, auto sc_tag, auto copy, auto ncopy_tag) __attribute__((always_inline)) {
       constexpr int NP = SIDX(pv_tag) ? 4 * DT : 0;
       constexpr int NQ = SIDX(sc_tag) ? 2 * KS : 0;
+      constexpr int NCOPY = SIDX(ncopy_tag);
       using O = MatOrder<NP, NQ>;
       // Operand reads run this many MFMAs ahead (fewer with 192-wide heads,
       // whose Q fragments leave fewer registers).  Each step below is fenced
@@ -534,8 +563,13 @@ __device__ __forceinline__ void item_fwd(const FwdParams& p, int head, int r) {
       };
       sfor<0, (DIST < O::N ? DIST : O::N)>([&](auto m_) { read_opnd(m_); });
       sfor<0, O::N>([&](auto m_) __attribute__((always_inline)) {
+        constexpr int m = SIDX(m_);
         issue(m_);
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr ((m + 1) * NCOPY / O::N > m * NCOPY / O::N) {
+          sfor<m * NCOPY / O::N, (m + 1) * NCOPY / O::N>(copy);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       });
       // The scores stay in this half-step (not sunk past the barrier).
       if constexpr (NQ > 0) {
@@ -653,32 +687,17 @@ __device__ __forceinline__ void item_fwd(const FwdParams& p, int head, int r) {
       }
     };
 
-    // One tile-copy instruction of group 1's share: k < KL copies part of a
-    // K tile, the rest part of a V tile.
-    constexpr int KL = C::KCHUNKS / (64 * GW);
-    constexpr int VL = C::VCHUNKS / (64 * GW);
-    auto copy_part = [&](auto k_, int ck, int kbf, int cv, int vbf, int sslot) __attribute__((always_inline)) {
-      constexpr int k = SIDX(k_);
-      if constexpr (k == 0) seg_copy(ck, sslot);
-      if constexpr (k < KL) {
-        const int slot0 = (k * GW + gw) * 64;
-        const int slot = slot0 + lane;
-        const int row = slot / (DQK / 8);
-        const int pc = slot - row * (DQK / 8);
-        const int off = ((ck * BN + row) * DQK + kswz<C::KROW>(row, pc) * 8) * 2;
-        dma16(krs, (uint32_t)(uintptr_t)(kbuf(kbf) + slot0 * 16), off);
-      } else {
-        const int slot0 = ((k - KL) * GW + gw) * 64;
-        const int slot = slot0 + lane;
-        const int row = slot / (DV / 8);
-        const int pc = slot - row * (DV / 8);
-        const int off = ((cv * BN + row) * DV + vswz<C::VROW>(row, pc) * 8) * 2;
-        dma16(vrs, (uint32_t)(uintptr_t)(vbuf(vbf) + slot0 * 16), off);
-      }
-    };
-    auto no_copy = [&](auto) __attribute__((always_inline)) {};
 
     // Each group runs its own copy of the sequence (no per-phase branches).
+    // Group 1 copies the first tiles (K_0, then K_1 and V_0).  From then on
+    // K_{i+2} and V_{i+1} are copied in half-step 2i+2 into the buffers of K_i
+    // and V_{i-1} (last read by MM(i) in half-steps 2i and 2i+1) and waited
+    // for before the barrier that opens MM(i+2) of group 0 (half-step 2i+4):
+    //   heads up to 128 wide: by group 0 during its MM(i+1), where issuing a
+    //     copy costs little (the matrix pipe works meanwhile);
+    //   192-wide heads: by group 1 during its SM(i), since the copy addresses
+    //     do not fit beside the wider Q fragments in the matrix phase.
+    constexpr bool kCopyInMM = DQK <= 128;
     auto run = [&](auto g1_tag) __attribute__((always_inline)) {
       constexpr bool G1 = SIDX(g1_tag) != 0;
       if constexpr (G1) {
@@ -695,28 +714,49 @@ __device__ __forceinline__ void item_fwd(const FwdParams& p, int head, int r) {
         g1_load_v(cols[0], 0);
         lds_barrier();   // group 1 starts one half-step late
       }
-      mm(0, Idx<0>{}, Idx<1>{});
+      mm(0, Idx<0>{}, Idx<1>{}, no_copy, Idx<0>{});
       for (int i = 0; i + 1 < n; ++i) {
-        wait_copies_and_barrier<0>();
-        if constexpr (G1) {
+        if constexpr (!kCopyInMM) {
+          wait_copies_and_barrier<0>();
+          if constexpr (G1) {
+            const int ck = colc(i + 2), cv = colc(i + 1);
+            const int kbf = i & 1, vbf = (i + 1) & 1, sslot = (i + 2) % 3;
+            sm(i, [&](auto k_) __attribute__((always_inline)) { copy_part(k_, ck, kbf, cv, vbf, sslot); },
+               Idx<KL + VL>{});
+          } else {
+            sm(i, no_copy, Idx<0>{});
+          }
+          lds_barrier();
+          mm(i + 1, Idx<1>{}, Idx<1>{}, no_copy, Idx<0>{});
+        } else if constexpr (G1) {
+          wait_copies_and_barrier<0>();
+          sm(i, no_copy, Idx<0>{});
+          lds_barrier();
+          mm(i + 1, Idx<1>{}, Idx<1>{}, no_copy, Idx<0>{});
+        } else {
+          lds_barrier();
+          sm(i, no_copy, Idx<0>{});
+          wait_copies_and_barrier<0>();
           // K_{i+2} (past the end: a repeat of K_{n-1} into the free buffer)
-          // and V_{i+1}.
-          // Segment ids of block i+2 go to ring slot (i+2) % 3, last read by
-          // SM(i-1) in half-step 2i.
+          // and V_{i+1}; the segment ids of block i+2 go to ring slot
+          // (i+2) % 3, last read by SM(i-1) in half-steps 2i-1 and 2i.
           const int ck = colc(i + 2), cv = colc(i + 1);
           const int kbf = i & 1, vbf = (i + 1) & 1, sslot = (i + 2) % 3;
-          sm(i, [&](auto k_) __attribute__((always_inline)) { copy_part(k_, ck, kbf, cv, vbf, sslot); },
+          mm(i + 1, Idx<1>{}, Idx<1>{},
+             [&](auto k_) __attribute__((always_inline)) { copy_part(k_, ck, kbf, cv, vbf, sslot); },
              Idx<KL + VL>{});
-        } else {
-          sm(i, no_copy, Idx<0>{});
         }
-        lds_barrier();
-        mm(i + 1, Idx<1>{}, Idx<1>{});
       }
-      wait_copies_and_barrier<0>();
+      if constexpr (G1 || !kCopyInMM)
+        wait_copies_and_barrier<0>();
+      else
+        lds_barrier();
       sm(n - 1, no_copy, Idx<0>{});
-      lds_barrier();
-      mm(n, Idx<1>{}, Idx<0>{});
+      if constexpr (G1 || !kCopyInMM)
+        lds_barrier();
+      else
+        wait_copies_and_barrier<0>();
+      mm(n, Idx<1>{}, Idx<0>{}, no_copy, Idx<0>{});
       if constexpr (!G1) lds_barrier();   // matches group 1's extra barrier
     };
     if (grp1)
