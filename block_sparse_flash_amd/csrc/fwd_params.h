@@ -51,21 +51,22 @@ constexpr int kBf16BlockKV = 64;
 // round-robin over them.
 constexpr int kNumXcd = 8;
 
-// Maps a linear work-group id to (flattened head b*Hq+h, q-block row rank).
-// When xcd_units > 0, all work-groups of one unit (a K/V head group or a
-// single query head) land on the same XCD so that they share its L2; within
-// an XCD, rows are taken longest-first across that XCD's units.
+// Maps a linear item id to (flattened head b*Hq+h, q-block row rank).
+// When xcd_units > 0, all items of one unit (a K/V head group or a single
+// query head) land on the same XCD so that they share its L2.  Within an
+// XCD the items go unit by unit, each unit's rows longest-first with the
+// query heads of a K/V group side by side: the few units in flight at a
+// time keep their K/V in the XCD's L2.
 __device__ __forceinline__ void map_workgroup(const FwdParams& p, int wg, int* head, int* rank) {
   const int n_heads = p.B * p.Hq;
   if (p.xcd_units > 0) {
     const int xcd = wg % kNumXcd;
     const int slot = wg / kNumXcd;
-    const int units_per_xcd = p.xcd_units / kNumXcd;
-    const int per_rank = units_per_xcd * p.unit_heads;
-    const int rk = slot / per_rank;
-    const int rem = slot - rk * per_rank;
-    const int unit_local = rem / p.unit_heads;
-    const int sub = rem - unit_local * p.unit_heads;
+    const int per_unit = p.n_q_blocks * p.unit_heads;
+    const int unit_local = slot / per_unit;
+    const int rem = slot - unit_local * per_unit;
+    const int rk = rem / p.unit_heads;
+    const int sub = rem - rk * p.unit_heads;
     *head = (unit_local * kNumXcd + xcd) * p.unit_heads + sub;
     *rank = rk;
   } else {

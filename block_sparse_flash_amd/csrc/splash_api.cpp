@@ -22,21 +22,26 @@ bool dims_supported(int32_t dtype, int32_t d_qk, int32_t d_v) {
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 
-// Work-group placement: a "unit" (one K/V head group, else one query head)
-// is kept on one XCD when the unit count divides evenly over the XCDs.
+// Work-group placement: a "unit" is a run of query heads that share one K/V
+// head (the whole group, or the largest part of it that still gives a unit
+// count divisible by the XCD count); each unit's items stay on one XCD so
+// that its K/V is read into that XCD's L2 once.  Without such a split the
+// items keep their plain order.
 void choose_xcd_units(const splash_fwd_args& a, splash::FwdParams* p) {
   p->xcd_units = 0;
   p->unit_heads = 1;
   const char* env = std::getenv("SPLASH_XCD_MAP");
   if (env && env[0] == '0') return;
-  const int64_t kv_units = static_cast<int64_t>(a.B) * a.Hkv;
-  const int64_t q_units = static_cast<int64_t>(a.B) * a.Hq;
-  if (kv_units % splash::kNumXcd == 0) {
-    p->xcd_units = static_cast<int32_t>(kv_units);
-    p->unit_heads = a.Hq / a.Hkv;
-  } else if (q_units % splash::kNumXcd == 0) {
-    p->xcd_units = static_cast<int32_t>(q_units);
-    p->unit_heads = 1;
+  const int group = a.Hq / a.Hkv;
+  const int64_t q_heads = static_cast<int64_t>(a.B) * a.Hq;
+  for (int d = group; d >= 1; --d) {
+    if (group % d != 0) continue;
+    const int64_t units = q_heads / d;
+    if (units % splash::kNumXcd == 0) {
+      p->xcd_units = static_cast<int32_t>(units);
+      p->unit_heads = d;
+      return;
+    }
   }
 }
 
