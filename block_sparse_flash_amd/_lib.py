@@ -27,7 +27,9 @@ SPLASH_MASK_STORED = 1
 
 # Every symbol include/splash.h declares.
 EXPORTED = ("splash_version", "splash_last_error", "attn_mask_compile",
-            "splash_fwd_tile", "splash_attn_fwd")
+            "splash_fwd_tile", "splash_attn_fwd", "splash_split_workspace_bytes",
+            "splash_attn_fwd_split")
+SPLASH_MAX_SPLIT = 64
 
 c_i32 = ctypes.c_int32
 c_ptr = ctypes.c_void_p
@@ -104,6 +106,12 @@ def load():
                                         ctypes.POINTER(c_i32), ctypes.POINTER(c_i32)]
         lib.splash_attn_fwd.restype = ctypes.c_int
         lib.splash_attn_fwd.argtypes = [ctypes.POINTER(FwdArgs), c_ptr]
+        lib.splash_split_workspace_bytes.restype = ctypes.c_int
+        lib.splash_split_workspace_bytes.argtypes = [c_i32, c_i32, c_i32, c_i32, c_i32,
+                                                     ctypes.POINTER(ctypes.c_int64)]
+        lib.splash_attn_fwd_split.restype = ctypes.c_int
+        lib.splash_attn_fwd_split.argtypes = [ctypes.POINTER(FwdArgs), c_i32, c_ptr,
+                                              ctypes.c_int64, c_ptr]
         _lib = lib
         return lib
 

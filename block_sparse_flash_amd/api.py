@@ -129,7 +129,7 @@ def splash_fwd(q, k, v, *, scale: Optional[float] = None, soft_cap: float = 0.0,
                causal: bool = False, window_left: int = -1, window_right: int = -1,
                seg_q=None, seg_kv=None, tables: Optional[MaskTables] = None,
                mask_mode: str = "computed", out=None, lse=None, return_lse: bool = True,
-               max_logit: Optional[float] = None, stream=None):
+               max_logit: Optional[float] = None, n_split: int = 1, workspace=None, stream=None):
     """Block-sparse attention forward on the GPU.
 
     q [B, Hq, L, d_qk], k [B, Hkv, L, d_qk], v [B, Hkv, L, d_v]: contiguous
@@ -139,7 +139,11 @@ def splash_fwd(q, k, v, *, scale: Optional[float] = None, soft_cap: float = 0.0,
     (``fwd_tile``); compiled here when omitted.  ``max_logit``: the Max Logit
     Estimate constant (logit units) used instead of the running row max, or
     None.  Returns (o, lse) with o like q but with d_v, lse float32 [B, Hq, L]
-    (None if ``return_lse`` is False).
+    (None if ``return_lse`` is False).  ``n_split`` > 1 (bf16 only): each
+    row's active kv blocks are cut into that many chunks computed as separate
+    items and merged through their log-sum-exp (``splash_attn_fwd_split``);
+    ``workspace`` is a device tensor of at least ``split_workspace_bytes``
+    bytes, allocated here when omitted.
     """
     import torch
     lib = _lib.load()
@@ -186,6 +190,16 @@ def splash_fwd(q, k, v, *, scale: Optional[float] = None, soft_cap: float = 0.0,
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
 
+    ws_ptr, ws_bytes = None, 0
+    if n_split != 1:
+        need = split_workspace_bytes(n_split, 1 if per_batch else B, Hq, L, d_v)
+        if workspace is None:
+            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        have = workspace.numel() * workspace.element_size()
+        if have < need:
+            raise ValueError(f"workspace holds {have} bytes, {need} needed")
+        ws_ptr, ws_bytes = workspace.data_ptr(), have
+
     batches = range(B) if per_batch else [None]
     for bsel in batches:
         if tables is None or per_batch:
@@ -223,5 +237,19 @@ def splash_fwd(q, k, v, *, scale: Optional[float] = None, soft_cap: float = 0.0,
             dev["mask_next"].data_ptr(), dev["partial_mask_blocks"].data_ptr(),
             _MASK_MODES[mask_mode], float(scale), float(soft_cap),
             0 if max_logit is None else 1, 0.0 if max_logit is None else float(max_logit))
-        _lib.check(lib.splash_attn_fwd(ctypes.byref(args), ctypes.c_void_p(stream)))
+        if n_split == 1:
+            _lib.check(lib.splash_attn_fwd(ctypes.byref(args), ctypes.c_void_p(stream)))
+        else:
+            _lib.check(lib.splash_attn_fwd_split(ctypes.byref(args), int(n_split),
+                                                 ctypes.c_void_p(ws_ptr), ctypes.c_int64(ws_bytes),
+                                                 ctypes.c_void_p(stream)))
     return out, (lse if return_lse else None)
+
+
+def split_workspace_bytes(n_split: int, B: int, Hq: int, L: int, d_v: int) -> int:
+    """Device workspace bytes of a split-KV forward (``splash_split_workspace_bytes``)."""
+    lib = _lib.load()
+    nb = ctypes.c_int64()
+    _lib.check(lib.splash_split_workspace_bytes(int(n_split), int(B), int(Hq), int(L), int(d_v),
+                                                ctypes.byref(nb)))
+    return nb.value

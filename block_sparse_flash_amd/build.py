@@ -26,6 +26,7 @@ SOURCES = [
     "splash_api.cpp",
     "splash_fwd_f32.hip",
     "splash_fwd_bf16.hip",
+    "splash_split_merge.hip",
 ]
 
 ARCH = "gfx950"

@@ -35,11 +35,21 @@ struct FwdParams {
   // work-group -> (head, row) mapping
   int32_t xcd_units;      // number of units spread over XCDs (0: plain order)
   int32_t unit_heads;     // query heads per unit
+  // split-KV: each row's active blocks are cut into n_split contiguous
+  // chunks, each an item of its own writing a partial o (float32, divided
+  // by its own l) and lse to ws_o [n_split, B*Hq, L, d_v] and
+  // ws_lse [n_split, B*Hq, L]; ws_o == null: plain forward (n_split = 1).
+  int32_t n_split;
+  float* ws_o;
+  float* ws_lse;
 };
 
 // Launchers (return the hipError_t of the launch).
 hipError_t launch_fwd_f32(const FwdParams& p, int d_qk, int d_v, hipStream_t s);
 hipError_t launch_fwd_bf16(const FwdParams& p, int d_qk, int d_v, hipStream_t s);
+// Merge of the split-KV partials of p.ws_o / p.ws_lse into p.o (bf16) and
+// p.lse.
+hipError_t launch_split_merge_bf16(const FwdParams& p, int d_v, hipStream_t s);
 
 // Block sizes used by each kernel family.
 constexpr int kF32BlockQ = 64;

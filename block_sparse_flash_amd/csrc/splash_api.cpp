@@ -61,70 +61,69 @@ extern "C" int splash_fwd_tile(int32_t dtype, int32_t d_qk, int32_t d_v, int32_t
   return SPLASH_OK;
 }
 
-extern "C" int splash_attn_fwd(const splash_fwd_args* args, void* stream) {
-  splash::clear_error();
-  if (!args) return splash::fail(SPLASH_EINVAL, "splash_attn_fwd: NULL args");
+namespace {
+
+// Validates *args (errors prefixed with `fn`) and fills *p for the launch.
+// Returns SPLASH_OK, an error code, or -1 for a problem with nothing to
+// compute (B, Hq or L equal to 0).
+int prepare(const splash_fwd_args* args, const char* fn, splash::FwdParams* out) {
+  if (!args) return splash::fail(SPLASH_EINVAL, "%s: NULL args", fn);
   const splash_fwd_args& a = *args;
   if (a.dtype != SPLASH_F32 && a.dtype != SPLASH_BF16)
-    return splash::fail(SPLASH_EDTYPE, "splash_attn_fwd: unknown dtype %d", a.dtype);
+    return splash::fail(SPLASH_EDTYPE, "%s: unknown dtype %d", fn, a.dtype);
   if (a.B < 0 || a.Hq < 0 || a.L < 0 || a.Hkv <= 0)
-    return splash::fail(SPLASH_EINVAL, "splash_attn_fwd: bad sizes B=%d Hq=%d Hkv=%d L=%d", a.B,
-                        a.Hq, a.Hkv, a.L);
+    return splash::fail(SPLASH_EINVAL, "%s: bad sizes B=%d Hq=%d Hkv=%d L=%d", fn, a.B, a.Hq,
+                        a.Hkv, a.L);
   if (a.Hq % a.Hkv != 0)
-    return splash::fail(SPLASH_ESHAPE, "splash_attn_fwd: Hq=%d is not a multiple of Hkv=%d", a.Hq,
-                        a.Hkv);
+    return splash::fail(SPLASH_ESHAPE, "%s: Hq=%d is not a multiple of Hkv=%d", fn, a.Hq, a.Hkv);
   if (!dims_supported(a.dtype, a.d_qk, a.d_v))
-    return splash::fail(SPLASH_EUNSUPPORTED,
-                        "splash_attn_fwd: head dims (%d, %d) not built for dtype %d", a.d_qk,
-                        a.d_v, a.dtype);
+    return splash::fail(SPLASH_EUNSUPPORTED, "%s: head dims (%d, %d) not built for dtype %d", fn,
+                        a.d_qk, a.d_v, a.dtype);
   if (a.causal != 0 && a.causal != 1)
-    return splash::fail(SPLASH_EINVAL, "splash_attn_fwd: causal must be 0 or 1");
+    return splash::fail(SPLASH_EINVAL, "%s: causal must be 0 or 1", fn);
   if (a.window_left < -1 || a.window_right < -1)
-    return splash::fail(SPLASH_EINVAL, "splash_attn_fwd: window must be -1 or >= 0");
+    return splash::fail(SPLASH_EINVAL, "%s: window must be -1 or >= 0", fn);
   if (a.mask_mode != SPLASH_MASK_COMPUTED && a.mask_mode != SPLASH_MASK_STORED)
-    return splash::fail(SPLASH_EINVAL, "splash_attn_fwd: unknown mask_mode %d", a.mask_mode);
+    return splash::fail(SPLASH_EINVAL, "%s: unknown mask_mode %d", fn, a.mask_mode);
   if (!std::isfinite(a.scale) || !(a.scale > 0.0f))
-    return splash::fail(SPLASH_EINVAL, "splash_attn_fwd: scale must be finite and > 0");
+    return splash::fail(SPLASH_EINVAL, "%s: scale must be finite and > 0", fn);
   if (std::isnan(a.soft_cap) || std::isinf(a.soft_cap))
-    return splash::fail(SPLASH_EINVAL, "splash_attn_fwd: soft_cap must be finite");
+    return splash::fail(SPLASH_EINVAL, "%s: soft_cap must be finite", fn);
   if (a.use_max_logit != 0 && a.use_max_logit != 1)
-    return splash::fail(SPLASH_EINVAL, "splash_attn_fwd: use_max_logit must be 0 or 1");
+    return splash::fail(SPLASH_EINVAL, "%s: use_max_logit must be 0 or 1", fn);
   if (a.use_max_logit && !std::isfinite(a.max_logit))
-    return splash::fail(SPLASH_EINVAL, "splash_attn_fwd: max_logit must be finite");
-  if (!a.seg_q && a.seg_kv)
-    return splash::fail(SPLASH_EINVAL, "splash_attn_fwd: seg_kv given without seg_q");
+    return splash::fail(SPLASH_EINVAL, "%s: max_logit must be finite", fn);
+  if (!a.seg_q && a.seg_kv) return splash::fail(SPLASH_EINVAL, "%s: seg_kv given without seg_q", fn);
 
   int32_t bq = 0, bkv = 0;
   splash_fwd_tile(a.dtype, a.d_qk, a.d_v, &bq, &bkv);
   if (a.block_q != bq || a.block_kv != bkv)
-    return splash::fail(SPLASH_ESHAPE,
-                        "splash_attn_fwd: tables built for blocks %dx%d, kernel uses %dx%d",
+    return splash::fail(SPLASH_ESHAPE, "%s: tables built for blocks %dx%d, kernel uses %dx%d", fn,
                         a.block_q, a.block_kv, bq, bkv);
   const int64_t nq = (static_cast<int64_t>(a.L) + bq - 1) / bq;
   if (a.n_q_blocks != nq)
-    return splash::fail(SPLASH_ESHAPE, "splash_attn_fwd: n_q_blocks=%d but L=%d needs %lld",
-                        a.n_q_blocks, a.L, static_cast<long long>(nq));
+    return splash::fail(SPLASH_ESHAPE, "%s: n_q_blocks=%d but L=%d needs %lld", fn, a.n_q_blocks,
+                        a.L, static_cast<long long>(nq));
   if (a.n_active < 0 || a.n_patterns < 0)
-    return splash::fail(SPLASH_EINVAL, "splash_attn_fwd: negative table size");
+    return splash::fail(SPLASH_EINVAL, "%s: negative table size", fn);
 
   const int64_t n_heads = static_cast<int64_t>(a.B) * a.Hq;
-  if (n_heads == 0 || a.L == 0) return SPLASH_OK;  // nothing to compute
+  if (n_heads == 0 || a.L == 0) return -1;  // nothing to compute
   const int64_t n_wg = n_heads * nq;
   const int64_t max_d = a.d_qk > a.d_v ? a.d_qk : a.d_v;
   if (n_wg > INT32_MAX || n_heads * a.L > (int64_t{1} << 46) / max_d)
-    return splash::fail(SPLASH_ESHAPE, "splash_attn_fwd: problem too large");
+    return splash::fail(SPLASH_ESHAPE, "%s: problem too large", fn);
 
-  if (!a.q || !a.k || !a.v || !a.o)
-    return splash::fail(SPLASH_EINVAL, "splash_attn_fwd: NULL q/k/v/o");
+  if (!a.q || !a.k || !a.v || !a.o) return splash::fail(SPLASH_EINVAL, "%s: NULL q/k/v/o", fn);
   if (!aligned16(a.q) || !aligned16(a.k) || !aligned16(a.v) || !aligned16(a.o))
-    return splash::fail(SPLASH_EINVAL, "splash_attn_fwd: q/k/v/o must be 16-byte aligned");
+    return splash::fail(SPLASH_EINVAL, "%s: q/k/v/o must be 16-byte aligned", fn);
   if (!a.row_ptr || !a.row_order)
-    return splash::fail(SPLASH_EINVAL, "splash_attn_fwd: NULL row_ptr or row_order");
+    return splash::fail(SPLASH_EINVAL, "%s: NULL row_ptr or row_order", fn);
   if (a.n_active > 0 && (!a.active_cols || !a.block_code || !a.mask_next))
-    return splash::fail(SPLASH_EINVAL, "splash_attn_fwd: NULL active_cols, block_code or mask_next");
+    return splash::fail(SPLASH_EINVAL, "%s: NULL active_cols, block_code or mask_next", fn);
   if (a.mask_mode == SPLASH_MASK_STORED && a.n_active > 0 && a.n_patterns > 0 &&
       !a.partial_mask_blocks)
-    return splash::fail(SPLASH_EINVAL, "splash_attn_fwd: stored mask mode needs partial_mask_blocks");
+    return splash::fail(SPLASH_EINVAL, "%s: stored mask mode needs partial_mask_blocks", fn);
 
   splash::FwdParams p{};
   p.q = a.q;
@@ -155,12 +154,74 @@ extern "C" int splash_attn_fwd(const splash_fwd_args* args, void* stream) {
   p.soft_cap = a.soft_cap > 0.0f ? a.soft_cap : 0.0f;
   p.mle = a.use_max_logit;
   p.mle_log2 = a.use_max_logit ? a.max_logit * 1.4426950408889634f : 0.0f;
+  p.n_split = 1;
+  p.ws_o = nullptr;
+  p.ws_lse = nullptr;
   choose_xcd_units(a, &p);
+  *out = p;
+  return SPLASH_OK;
+}
 
+int64_t split_workspace_bytes(int64_t n_split, int64_t B, int64_t Hq, int64_t L, int64_t d_v) {
+  return n_split * B * Hq * L * (d_v + 1) * static_cast<int64_t>(sizeof(float));
+}
+
+}  // namespace
+
+extern "C" int splash_attn_fwd(const splash_fwd_args* args, void* stream) {
+  splash::clear_error();
+  splash::FwdParams p{};
+  const int rc = prepare(args, "splash_attn_fwd", &p);
+  if (rc == -1) return SPLASH_OK;
+  if (rc != SPLASH_OK) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const hipError_t e = a.dtype == SPLASH_F32 ? splash::launch_fwd_f32(p, a.d_qk, a.d_v, s)
-                                             : splash::launch_fwd_bf16(p, a.d_qk, a.d_v, s);
+  const hipError_t e = args->dtype == SPLASH_F32 ? splash::launch_fwd_f32(p, args->d_qk, args->d_v, s)
+                                                 : splash::launch_fwd_bf16(p, args->d_qk, args->d_v, s);
   if (e != hipSuccess)
     return splash::fail(SPLASH_EHIP, "splash_attn_fwd: launch failed: %s", hipGetErrorString(e));
+  return SPLASH_OK;
+}
+
+extern "C" int splash_split_workspace_bytes(int32_t n_split, int32_t B, int32_t Hq, int32_t L,
+                                            int32_t d_v, int64_t* bytes) {
+  splash::clear_error();
+  if (!bytes) return splash::fail(SPLASH_EINVAL, "splash_split_workspace_bytes: NULL output");
+  if (n_split < 1 || n_split > SPLASH_MAX_SPLIT || B < 0 || Hq < 0 || L < 0 || d_v <= 0)
+    return splash::fail(SPLASH_EINVAL,
+                        "splash_split_workspace_bytes: bad sizes n_split=%d B=%d Hq=%d L=%d d_v=%d",
+                        n_split, B, Hq, L, d_v);
+  *bytes = split_workspace_bytes(n_split, B, Hq, L, d_v);
+  return SPLASH_OK;
+}
+
+extern "C" int splash_attn_fwd_split(const splash_fwd_args* args, int32_t n_split, void* workspace,
+                                     int64_t workspace_bytes, void* stream) {
+  splash::clear_error();
+  splash::FwdParams p{};
+  const int rc = prepare(args, "splash_attn_fwd_split", &p);
+  if (rc != SPLASH_OK && rc != -1) return rc;
+  if (args->dtype != SPLASH_BF16)
+    return splash::fail(SPLASH_EUNSUPPORTED, "splash_attn_fwd_split: bf16 only");
+  if (n_split < 1 || n_split > SPLASH_MAX_SPLIT)
+    return splash::fail(SPLASH_EINVAL, "splash_attn_fwd_split: n_split=%d not in [1, %d]", n_split,
+                        SPLASH_MAX_SPLIT);
+  if (rc == -1) return SPLASH_OK;
+  const int64_t need = split_workspace_bytes(n_split, args->B, args->Hq, args->L, args->d_v);
+  if (!workspace || workspace_bytes < need)
+    return splash::fail(SPLASH_EINVAL, "splash_attn_fwd_split: workspace of %lld bytes needed, %lld given",
+                        static_cast<long long>(need), static_cast<long long>(workspace_bytes));
+  if (!aligned16(workspace))
+    return splash::fail(SPLASH_EINVAL, "splash_attn_fwd_split: workspace must be 16-byte aligned");
+  if (static_cast<int64_t>(p.B) * p.Hq * p.n_q_blocks * n_split > INT32_MAX)
+    return splash::fail(SPLASH_ESHAPE, "splash_attn_fwd_split: problem too large");
+  const int64_t rows = static_cast<int64_t>(p.B) * p.Hq * p.L;
+  p.n_split = n_split;
+  p.ws_o = static_cast<float*>(workspace);
+  p.ws_lse = p.ws_o + n_split * rows * args->d_v;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = splash::launch_fwd_bf16(p, args->d_qk, args->d_v, s);
+  if (e == hipSuccess) e = splash::launch_split_merge_bf16(p, args->d_v, s);
+  if (e != hipSuccess)
+    return splash::fail(SPLASH_EHIP, "splash_attn_fwd_split: launch failed: %s", hipGetErrorString(e));
   return SPLASH_OK;
 }

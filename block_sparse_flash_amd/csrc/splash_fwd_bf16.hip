@@ -60,6 +60,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
@@ -232,9 +233,10 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // One item: the 256 query rows of q-block row r of query head `head`
-// (flattened b * Hq + h), over the row's active kv blocks.
-template <int DQK, int DV, bool CAP>
-__device__ __forceinline__ void item_fwd(const FwdParams& p, int head, int r) {
+// (flattened b * Hq + h), over chunk `split` of the row's active kv blocks
+// (the whole row when there is no split).
+template <int DQK, int DV, bool CAP, bool SPLIT>
+__device__ __forceinline__ void item_fwd(const FwdParams& p, int head, int r, int split) {
   using C = Cfg<DQK, DV>;
   constexpr int KS = C::KS;
   constexpr int DT = C::DT;
@@ -309,8 +311,14 @@ __device__ __forceinline__ void item_fwd(const FwdParams& p, int head, int r) {
   const int qa = qw;
   const int qb = min(qw + 31, L - 1);
 
-  const int g0 = ld_table(p.row_ptr, r);
-  const int n = ld_table(p.row_ptr, r + 1) - g0;
+  // Blocks [row_ptr[r] + lo, row_ptr[r] + hi) of the active list: chunk
+  // `split` of n_split near-equal contiguous chunks.
+  const int row0 = ld_table(p.row_ptr, r);
+  const int n_row = ld_table(p.row_ptr, r + 1) - row0;
+  const int lo = SPLIT ? (int)(((int64_t)n_row * split) / p.n_split) : 0;
+  const int hi_blk = SPLIT ? (int)(((int64_t)n_row * (split + 1)) / p.n_split) : n_row;
+  const int g0 = row0 + lo;
+  const int n = hi_blk - lo;
   const int32_t* cols = p.active_cols + g0;
   auto colc = [&](int x) { return ld_table(cols, min(x, n - 1)); };
 
@@ -769,6 +777,24 @@ __device__ __forceinline__ void item_fwd(const FwdParams& p, int head, int r) {
 
   // Epilogue: o = O / l, lse = (m zc + log2 l) ln 2.
   const float lt = lsum + __shfl_xor(lsum, 32);
+  if constexpr (SPLIT) {
+    // Split-KV partial: o and lse of this chunk alone, in float32 (an empty
+    // chunk gives o = 0, lse = -inf, which the merge weighs by 0).
+    if (qi < L) {
+      const float inv = (lt > 0.0f) ? 1.0f / lt : 0.0f;
+      const int64_t row = ((int64_t)split * p.B * p.Hq + head) * L + qi;
+      float* og = p.ws_o + row * DV;
+      sfor<0, DT * 4>([&](auto i_) {
+        constexpr int dt = SIDX(i_) / 4;
+        constexpr int q4 = SIDX(i_) % 4;
+        const f32x4 w = {oacc[dt][4 * q4] * inv, oacc[dt][4 * q4 + 1] * inv, oacc[dt][4 * q4 + 2] * inv,
+                         oacc[dt][4 * q4 + 3] * inv};
+        *reinterpret_cast<f32x4*>(og + 32 * dt + 8 * q4 + 4 * hi) = w;
+      });
+      if (hi == 0) p.ws_lse[row] = (lt > 0.0f) ? (mref * zc + __log2f(lt)) * kLn2 : -INFINITY;
+    }
+    return;
+  }
   if (qi < L) {
     const float inv = (lt > 0.0f) ? 1.0f / lt : 0.0f;
     uint16_t* og = static_cast<uint16_t*>(p.o) + ((int64_t)head * L + qi) * DV;
@@ -799,19 +825,23 @@ __device__ __forceinline__ int item_of_round(int k, int w, int G, bool snake) {
   return k * G + w;
 }
 
-template <int DQK, int DV, bool CAP>
+template <int DQK, int DV, bool CAP, bool SPLIT>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void splash_fwd_bf16_kernel(FwdParams p) {
   const int w = blockIdx.x;
   const int G = gridDim.x;
-  const int T = p.B * p.Hq * p.n_q_blocks;
+  // Items: (head, q-block row) x split, split-major, so that the items of
+  // one split keep the XCD placement of the unsplit order.
+  const int T0 = p.B * p.Hq * p.n_q_blocks;
+  const int T = SPLIT ? T0 * p.n_split : T0;
   const bool snake = (G % kNumXcd) == 0;
   for (int k = 0; k * G < T; ++k) {
     const int t = item_of_round(k, w, G, snake);
     if (t >= T) continue;
+    const int split = SPLIT ? t / T0 : 0;
     int head, rank;
-    map_workgroup(p, t, &head, &rank);
-    item_fwd<DQK, DV, CAP>(p, head, ld_table(p.row_order, rank));
+    map_workgroup(p, t - split * T0, &head, &rank);
+    item_fwd<DQK, DV, CAP, SPLIT>(p, head, ld_table(p.row_order, rank), split);
   }
 }
 
@@ -820,13 +850,13 @@ void splash_fwd_bf16_kernel(FwdParams p) {
 // balanced; with segment ids, rows mix partial and full blocks unevenly and
 // the hardware's dynamic dispatch of one work-group per item balances better
 // (a grid of one work-group per item is the same kernel with one round).
-template <int DQK, int DV, bool CAP>
+template <int DQK, int DV, bool CAP, bool SPLIT>
 hipError_t launch(const FwdParams& p, int n_cu, hipStream_t s) {
-  const int64_t n_items = (int64_t)p.B * p.Hq * p.n_q_blocks;
+  const int64_t n_items = (int64_t)p.B * p.Hq * p.n_q_blocks * (SPLIT ? p.n_split : 1);
   const bool persistent = p.seg_q == nullptr;
   const int64_t grid = (persistent && n_items > n_cu) ? n_cu : n_items;
   const int bytes = Cfg<DQK, DV>::LDS_BYTES;
-  auto fn = splash_fwd_bf16_kernel<DQK, DV, CAP>;
+  auto fn = splash_fwd_bf16_kernel<DQK, DV, CAP, SPLIT>;
   if (bytes > 65536) {
     // Opt in to more than 64 KiB of dynamic LDS (gfx950 has 160 KiB per CU).
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
@@ -839,7 +869,9 @@ hipError_t launch(const FwdParams& p, int n_cu, hipStream_t s) {
 
 template <int DQK, int DV>
 hipError_t launch_cap(const FwdParams& p, int n_cu, hipStream_t s) {
-  return p.soft_cap > 0.0f ? launch<DQK, DV, true>(p, n_cu, s) : launch<DQK, DV, false>(p, n_cu, s);
+  if (p.ws_o)
+    return p.soft_cap > 0.0f ? launch<DQK, DV, true, true>(p, n_cu, s) : launch<DQK, DV, false, true>(p, n_cu, s);
+  return p.soft_cap > 0.0f ? launch<DQK, DV, true, false>(p, n_cu, s) : launch<DQK, DV, false, false>(p, n_cu, s);
 }
 
 // Compute units of the current device (cached per device).

@@ -27,6 +27,16 @@
  *                      by the joto.ai page on core LLM operators, section
  *                      "LSE and online softmax" (lse = m + log l).
  *
+ *   splash_attn_fwd_split  the same forward with each query row's active
+ *                      kv blocks cut into n_split contiguous chunks computed
+ *                      as separate work items, then merged exactly through
+ *                      their log-sum-exp residuals (split-KV).  Defined by
+ *                      Lecture 13 section 5.1 (partial (m, l, o) results of
+ *                      separate key ranges merge in any order, as in split-KV
+ *                      inference) and the joto.ai page, section "LSE and
+ *                      online softmax" (split-K: lse = log sum_s e^{lse_s},
+ *                      o = sum_s e^{lse_s - lse} o_s).
+ *
  * Conventions for every call:
  *   - Return value: SPLASH_OK (0) or one of the SPLASH_E* codes below.  On an
  *     error nothing is written to any output and no kernel is launched;
@@ -46,7 +56,10 @@
 extern "C" {
 #endif
 
-#define SPLASH_VERSION 101
+#define SPLASH_VERSION 102
+
+/* Largest n_split of splash_attn_fwd_split. */
+#define SPLASH_MAX_SPLIT 64
 
 enum splash_status {
   SPLASH_OK = 0,
@@ -226,6 +239,33 @@ typedef struct splash_fwd_args {
  * failed).  B, Hq or L equal to 0 is a no-op.  Device-side faults surface at
  * the caller's next synchronisation. */
 int splash_attn_fwd(const splash_fwd_args* args, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Split-KV forward.
+ * ---------------------------------------------------------------------- */
+
+/* Bytes of device workspace splash_attn_fwd_split needs for these sizes:
+ * n_split * B * Hq * L * (d_v + 1) * 4 (float32 partial outputs and
+ * log-sum-exp values).  Errors: SPLASH_EINVAL (NULL bytes, n_split not in
+ * [1, SPLASH_MAX_SPLIT], negative size, d_v <= 0). */
+int splash_split_workspace_bytes(int32_t n_split, int32_t B, int32_t Hq, int32_t L,
+                                 int32_t d_v, int64_t* bytes);
+
+/* The forward of splash_attn_fwd (same arguments, same results up to
+ * float32 rounding order) with every query row's active kv blocks cut into
+ * n_split near-equal contiguous chunks, each processed as a separate work
+ * item: more items for shapes with few heads or q blocks.  Each chunk's
+ * normalised output and lse go to `workspace` (device, 16-B aligned,
+ * caller-owned, at least splash_split_workspace_bytes; its contents on entry
+ * are ignored and on return are scratch); a second kernel on the same
+ * stream merges them into args->o and args->lse (a chunk with no allowed
+ * key has weight 0).  bf16 only.  Errors: those of splash_attn_fwd, plus
+ * SPLASH_EUNSUPPORTED (f32), SPLASH_EINVAL (n_split not in
+ * [1, SPLASH_MAX_SPLIT], NULL, misaligned or too small workspace),
+ * SPLASH_ESHAPE (items beyond int32).  Calls that share a workspace must be
+ * ordered on one stream. */
+int splash_attn_fwd_split(const splash_fwd_args* args, int32_t n_split, void* workspace,
+                          int64_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }  /* extern "C" */

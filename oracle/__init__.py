@@ -15,7 +15,8 @@ Sources (pages cited by title and section):
   MaskInfo, bounds, segment ids and AND-combined masks), 6.6 (one byte per
   pattern element), exercises 7, 11, 12 and their answers.
 * "拆解大模型几项核心操作背后的数学与 Infra 优化逻辑" (joto.ai blog), sections
-  "Causal Mask", "Online Softmax" and "LSE 与 Online Softmax" (lse = m + log l).
+  "Causal Mask", "Online Softmax" and "LSE 与 Online Softmax" (lse = m + log l,
+  and the split-K merge of per-range outputs through their lse).
 
 Parity pins: every function here is pinned by tests under ``tests/`` against
 worked examples printed on the pages (``tests/golden/``), closed forms,
@@ -30,6 +31,7 @@ from .attention import (
     attention_brute,
     online_softmax_steps,
     merge_partials,
+    merge_lse,
     mle_safe_range,
 )
 from .mask_tables import mask_tables_ref
@@ -40,6 +42,7 @@ __all__ = [
     "attention_brute",
     "online_softmax_steps",
     "merge_partials",
+    "merge_lse",
     "mle_safe_range",
     "mask_tables_ref",
 ]

@@ -267,3 +267,29 @@ def merge_partials(part1, part2):
     l = l1 * a1 + l2 * a2
     o = (np.asarray(u1, np.float64) * a1 + np.asarray(u2, np.float64) * a2) / l
     return m, l, o
+
+
+def merge_lse(o_parts, lse_parts):
+    """Merge the outputs of attention over disjoint key ranges (split-K).
+
+    ``o_parts[s]`` is the normalised output over key range s and
+    ``lse_parts[s]`` its natural-log log-sum-exp (-inf for a range with no
+    allowed key).  Per the joto.ai page, section "LSE 与 Online Softmax"
+    (split-K reduction; also Lecture 13 section 5.1: partial results of
+    separate key ranges combine in any order):
+        lse = log sum_s e^{lse_s},    o = sum_s e^{lse_s - lse} o_s.
+    A row whose ranges are all empty gets o = 0, lse = -inf.
+    Shapes: o_parts [S, ..., d], lse_parts [S, ...]; float64 throughout.
+    """
+    o_parts = np.asarray(o_parts, dtype=np.float64)
+    lse_parts = np.asarray(lse_parts, dtype=np.float64)
+    mx = lse_parts.max(axis=0)
+    empty = np.isneginf(mx)
+    shift = np.where(empty, 0.0, mx)
+    w = np.exp(lse_parts - shift[None])             # e^{-inf} = 0
+    den = w.sum(axis=0)
+    with np.errstate(divide="ignore"):
+        lse = np.where(empty, -np.inf, shift + np.log(np.where(empty, 1.0, den)))
+    o = (w[..., None] * o_parts).sum(axis=0) / np.where(empty, 1.0, den)[..., None]
+    o = np.where(empty[..., None], 0.0, o)
+    return o, lse

@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
     assert set(declared) == set(_lib.EXPORTED), declared
     for name in declared:
         assert hasattr(lib, name), name
-    assert lib.splash_version() == 101
+    assert lib.splash_version() == 102
 
 
 def _assert_tables_equal(t, ref):
@@ -204,4 +204,39 @@ def test_forward_null_args_and_noops():
     assert lib.splash_attn_fwd(ctypes.byref(_good_args(B=0)), None) == 0
     assert lib.splash_attn_fwd(ctypes.byref(_good_args(Hq=0)), None) == 0
     assert lib.splash_attn_fwd(ctypes.byref(_good_args(L=0, n_q_blocks=0)), None) == 0
+    assert lib.splash_last_error() == b""
+
+
+def test_split_workspace_bytes():
+    lib = _lib.load()
+    nb = ctypes.c_int64()
+    assert lib.splash_split_workspace_bytes(3, 2, 4, 1000, 128, ctypes.byref(nb)) == 0
+    assert nb.value == 3 * 2 * 4 * 1000 * (128 + 1) * 4
+    for bad in [(0, 1, 1, 1, 64), (_lib.SPLASH_MAX_SPLIT + 1, 1, 1, 1, 64), (2, -1, 1, 1, 64),
+                (2, 1, 1, 1, 0)]:
+        assert lib.splash_split_workspace_bytes(*bad, ctypes.byref(nb)) == 1
+    assert lib.splash_split_workspace_bytes(2, 1, 1, 1, 64, None) == 1
+
+
+@pytest.mark.parametrize("over,n_split,ws,ws_bytes,code", [
+    (dict(dtype=0, block_q=64, n_q_blocks=4), 2, 0x20000, 1 << 30, 4),  # f32: bf16 only
+    (dict(), 0, 0x20000, 1 << 30, 1),                 # n_split < 1
+    (dict(), 65, 0x20000, 1 << 30, 1),                # n_split > SPLASH_MAX_SPLIT
+    (dict(), 2, None, 1 << 30, 1),                    # no workspace
+    (dict(), 2, 0x20000, 1024, 1),                    # workspace too small
+    (dict(), 2, 0x20008, 1 << 30, 1),                 # misaligned workspace
+    (dict(Hq=3, Hkv=2), 2, 0x20000, 1 << 30, 2),      # errors of splash_attn_fwd apply
+    (dict(scale=0.0), 2, 0x20000, 1 << 30, 1),
+])
+def test_split_forward_validation_errors(over, n_split, ws, ws_bytes, code):
+    lib = _lib.load()
+    args = _good_args(**over)
+    assert lib.splash_attn_fwd_split(ctypes.byref(args), n_split, ws, ws_bytes, None) == code
+    assert len(lib.splash_last_error()) > 0
+
+
+def test_split_forward_noops():
+    lib = _lib.load()
+    assert lib.splash_attn_fwd_split(None, 2, None, 0, None) == 1
+    assert lib.splash_attn_fwd_split(ctypes.byref(_good_args(B=0)), 2, None, 0, None) == 0
     assert lib.splash_last_error() == b""

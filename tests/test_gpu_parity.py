@@ -191,6 +191,62 @@ def test_more_items_than_work_groups():
     _announce(f"  max-abs o {eo:.3g} lse {el:.3g}")
 
 
+SPLIT_CASES = [
+    # (B, Hq, Hkv, L, d_qk, d_v, mask kwargs, soft_cap, n_split)
+    (1, 2, 2, 1000, 128, 128, dict(causal=True), 0.0, 2),
+    (1, 4, 2, 777, 128, 128, dict(causal=True, window_left=200), 0.0, 5),
+    (1, 4, 1, 900, 128, 64, dict(causal=True, segs=(40, 300)), 50.0, 3),
+    (2, 2, 2, 520, 192, 128, dict(causal=True), 0.0, 4),
+    (1, 2, 1, 300, 64, 64, dict(window_left=70, window_right=33), 3.0, 7),
+    (1, 2, 2, 640, 64, 128, dict(), 0.0, 64),   # more chunks than blocks: empty chunks
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=lambda c: f"B{c[0]}H{c[1]}/{c[2]}-L{c[3]}-d{c[4]}x{c[5]}-s{c[8]}"
+                         + ("-cap" if c[7] else "") + "-" + "-".join(sorted(c[6])))
+def test_split_kv_every_element(case):
+    """splash_attn_fwd_split: chunks of each row's active blocks merged
+    through their lse (split-K) give the oracle's attention."""
+    B, Hq, Hkv, L, dqk, dv, mk, cap, S = case
+    _announce(f"split-KV {case}")
+    seed = 7000 + L + S
+    q, k, v = (stored(a, "bf16") for a in draw_qkv(B, Hq, Hkv, L, dqk, dv, seed, qk_std=1.5 if cap else 1.0))
+    mk = dict(mk)
+    seg = None
+    if "segs" in mk:
+        lo, hi = mk.pop("segs")
+        seg = segment_ids(L, seed, lo, hi)
+    scale = 1.0 / math.sqrt(dqk)
+    o, lse = _run(q, k, v, scale=scale, soft_cap=cap, seg_q=seg, n_split=S, **mk)
+    o_ref, lse_ref = attention_ref(as_f64(q), as_f64(k), as_f64(v), scale=scale,
+                                   soft_cap=cap, seg_q=seg, **mk)
+    eo, el = _compare(o, lse, o_ref, lse_ref, "bf16")
+    _announce(f"  max-abs o {eo:.3g} lse {el:.3g}")
+
+
+def test_split_kv_rows_without_keys_and_reuse():
+    """Rows with no allowed key stay o = 0, lse = -inf through the merge;
+    one workspace serves two calls in a row, the second smaller."""
+    _announce("split-KV empty rows + workspace reuse")
+    from block_sparse_flash_amd import split_workspace_bytes
+    B, H, L, d = 1, 2, 600, 128
+    q, k, v = (stored(a, "bf16") for a in draw_qkv(B, H, H, L, d, d, 78))
+    seg_q = np.repeat(np.arange(6), 100).astype(np.int32)
+    seg_kv = seg_q.copy()
+    seg_kv[seg_kv == 2] = 9
+    ws = torch.empty(split_workspace_bytes(4, B, H, L, d), dtype=torch.uint8, device="cuda")
+    o, lse = _run(q, k, v, causal=True, seg_q=seg_q, seg_kv=seg_kv, n_split=4, workspace=ws)
+    o_ref, lse_ref = attention_ref(as_f64(q), as_f64(k), as_f64(v), scale=d ** -0.5,
+                                   causal=True, seg_q=seg_q, seg_kv=seg_kv)
+    _compare(o, lse, o_ref, lse_ref, "bf16")
+    assert np.all(o[:, :, 200:300] == 0) and np.all(np.isneginf(lse[:, :, 200:300]))
+    L2 = 300
+    q2, k2, v2 = (stored(a, "bf16") for a in draw_qkv(B, H, H, L2, d, d, 79))
+    o2, l2 = _run(q2, k2, v2, causal=True, n_split=3, workspace=ws)
+    o2_ref, l2_ref = attention_ref(as_f64(q2), as_f64(k2), as_f64(v2), scale=d ** -0.5, causal=True)
+    _compare(o2, l2, o2_ref, l2_ref, "bf16")
+
+
 def test_empty_problem_is_noop():
     _announce("empty problem")
     q = torch.zeros((1, 2, 0, 128), dtype=torch.bfloat16, device="cuda")

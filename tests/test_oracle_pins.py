@@ -8,7 +8,7 @@ import pytest
 import scipy.special
 from hypothesis import given, settings, strategies as st
 
-from oracle import (allowed, attention_brute, attention_ref, merge_partials,
+from oracle import (allowed, attention_brute, attention_ref, merge_lse, merge_partials,
                     mle_safe_range, online_softmax_steps)
 from tests.conftest import read_golden
 
@@ -59,6 +59,40 @@ def test_merge_matches_whole_row():
     # Order independence.
     m2, l2, o2 = merge_partials(part(x[cut:], v[cut:]), part(x[:cut], v[:cut]))
     assert m2 == m and abs(l2 - l) < 1e-14 and np.max(np.abs(o2 - o)) < 1e-15
+
+
+@pytest.mark.parametrize("S", [1, 2, 3, 7])
+def test_merge_lse_matches_whole_rows(S):
+    """Split-K merge (joto.ai "LSE 与 Online Softmax"): outputs and lse of
+    disjoint key ranges, each taken with scipy on its own range, merge into
+    scipy's softmax and logsumexp of the whole masked row; ranges with no
+    allowed key weigh nothing, and a row with none at all stays empty."""
+    rng = np.random.default_rng(100 + S)
+    R, N, d = 6, 23, 4
+    x = rng.normal(size=(R, N)) * 4
+    allowed_ = rng.random((R, N)) < 0.6
+    allowed_[1, 5:] = False            # keys only in the first range(s)
+    allowed_[4, :] = False             # a row with no allowed key
+    v = rng.normal(size=(N, d))
+    cuts = np.linspace(0, N, S + 1).astype(int)
+    o_parts, lse_parts = [], []
+    for s in range(S):
+        a, b = cuts[s], cuts[s + 1]
+        xs = np.where(allowed_[:, a:b], x[:, a:b], -np.inf)
+        lse_s = scipy.special.logsumexp(xs, axis=1)
+        w = np.zeros_like(xs)
+        ok = np.isfinite(lse_s)
+        w[ok] = scipy.special.softmax(xs[ok], axis=1)
+        o_parts.append(w @ v[a:b])
+        lse_parts.append(lse_s)
+    o, lse = merge_lse(o_parts, lse_parts)
+    xf = np.where(allowed_, x, -np.inf)
+    full = np.isfinite(scipy.special.logsumexp(xf, axis=1))
+    assert np.array_equal(full, np.isfinite(lse))
+    ref_w = scipy.special.softmax(xf[full], axis=1)
+    assert np.max(np.abs(o[full] - ref_w @ v)) < 1e-13
+    assert np.max(np.abs(lse[full] - scipy.special.logsumexp(xf[full], axis=1))) < 1e-13
+    assert np.all(o[~full] == 0) and np.all(np.isneginf(lse[~full]))
 
 
 def _rand_case(seed, B, Hq, Hkv, L, dqk, dv, std=1.0):
