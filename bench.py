@@ -114,6 +114,8 @@ def main():
     ap.add_argument("--max-logit", type=float, default=None,
                     help="Max Logit Estimate constant (logit units) in place of the running "
                          "row max; the default is the running max")
+    ap.add_argument("--n-split", type=int, default=1,
+                    help="split-KV: chunks per row merged through their lse (bf16; 1 = plain forward)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run one device-to-device copy of this many MiB "
                          "(a plain copy of known size, for scaling HBM counters)")
@@ -128,9 +130,9 @@ def main():
 
     import torch
     from block_sparse_flash_amd import compile_mask, fwd_tile, splash_fwd
-    from block_sparse_flash_amd.inputs import WORKLOADS, make_inputs
+    from block_sparse_flash_amd.inputs import ALL_WORKLOADS, make_inputs
 
-    w = WORKLOADS[args.workload]
+    w = ALL_WORKLOADS[args.workload]
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     q, k, v, seg = make_inputs(w)
@@ -144,6 +146,11 @@ def main():
     lse = torch.empty((w.B, w.Hq, w.L), dtype=torch.float32, device=dev)
     kw = dict(scale=w.softmax_scale, soft_cap=w.soft_cap, seg_q=seg, tables=tabs,
               mask_mode=args.mask_mode, out=out, lse=lse, max_logit=args.max_logit, **mask_kw)
+    if args.n_split != 1:
+        from block_sparse_flash_amd import split_workspace_bytes
+        ws = torch.empty(split_workspace_bytes(args.n_split, w.B, w.Hq, w.L, w.d_v),
+                         dtype=torch.uint8, device=dev)
+        kw.update(n_split=args.n_split, workspace=ws)
 
     for _ in range(args.warmup):
         splash_fwd(qd, kd, vd, **kw)
@@ -194,6 +201,7 @@ def main():
                    "d_qk": w.d_qk, "d_v": w.d_v, "mask": mask, "soft_cap": w.soft_cap,
                    "scale": w.softmax_scale, "block_q": bq, "block_kv": bkv,
                    "mask_mode": args.mask_mode, "max_logit": args.max_logit,
+                   "n_split": args.n_split,
                    "parallelism": "single GPU"},
         "pct_of_peak": round(100.0 * tflops / peak, 2),
         "unmasked_tflop_per_step": flop_per_step / 1e12,

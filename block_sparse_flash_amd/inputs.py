@@ -75,6 +75,16 @@ WORKLOADS = {
 
 WORKLOAD_ORDER = list(WORKLOADS)
 
+# A shape for the split-KV forward: two heads of causal attention at
+# L=32768, 256 (head, q-block row) items of 4 to 512 active blocks, so that
+# without splitting the longest rows set the time on 256 CUs.
+EXTRA_WORKLOADS = {
+    "causal_bf16_L32768_H2": Workload(
+        "causal_bf16_L32768_H2", "bf16", 1, 2, 2, 32768, 128, 128,
+        causal=True, seed=6),
+}
+ALL_WORKLOADS = {**WORKLOADS, **EXTRA_WORKLOADS}
+
 
 def segment_ids(L: int, seed: int, lo: int = 512, hi: int = 8192) -> np.ndarray:
     """Contiguous document ids 0, 1, 2, ... with lengths drawn uniformly from

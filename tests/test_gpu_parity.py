@@ -15,8 +15,8 @@ import pytest
 torch = pytest.importorskip("torch")
 
 from block_sparse_flash_amd import compile_mask, fwd_tile, splash_fwd
-from block_sparse_flash_amd.inputs import (WORKLOADS, as_f64, draw_qkv, make_inputs,
-                                           segment_ids, stored)
+from block_sparse_flash_amd.inputs import (EXTRA_WORKLOADS, WORKLOADS, as_f64, draw_qkv,
+                                           make_inputs, segment_ids, stored)
 from oracle import allowed, attention_ref, mle_safe_range
 
 pytestmark = pytest.mark.gpu
@@ -279,10 +279,13 @@ def _sample_rows(L, bq, rng, n_random=24):
     return np.array(sorted(rows))
 
 
-@pytest.mark.parametrize("name", list(WORKLOADS))
-def test_full_size_workloads_sampled(name):
-    w = WORKLOADS[name]
-    _announce(f"full-size {name}")
+FULL_SIZE = [(name, 1) for name in WORKLOADS] + [(name, 4) for name in EXTRA_WORKLOADS]
+
+
+@pytest.mark.parametrize("name,n_split", FULL_SIZE, ids=lambda x: str(x))
+def test_full_size_workloads_sampled(name, n_split):
+    w = {**WORKLOADS, **EXTRA_WORKLOADS}[name]
+    _announce(f"full-size {name} n_split={n_split}")
     q, k, v, seg = make_inputs(w)
     bq, bkv = fwd_tile(w.dtype, w.d_qk, w.d_v)
     tabs = compile_mask(w.L, bq, bkv, causal=w.causal, window_left=w.window_left,
@@ -290,7 +293,7 @@ def test_full_size_workloads_sampled(name):
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
     o, lse = splash_fwd(qd, kd, vd, scale=w.softmax_scale, soft_cap=w.soft_cap,
                         causal=w.causal, window_left=w.window_left,
-                        window_right=w.window_right, seg_q=seg, tables=tabs)
+                        window_right=w.window_right, seg_q=seg, tables=tabs, n_split=n_split)
     torch.cuda.synchronize()
     rng = np.random.default_rng(w.seed + 7)
     n_heads = w.B * w.Hq
