@@ -48,6 +48,8 @@
 
 #include <hip/hip_runtime.h>
 #include <math.h>
+
+#include <atomic>
 #include <stdint.h>
 #include <stdlib.h>
 
@@ -874,17 +876,18 @@ hipError_t launch_cap(const FwdParams& p, int n_cu, hipStream_t s) {
   return p.soft_cap > 0.0f ? launch<DQK, DV, true, false>(p, n_cu, s) : launch<DQK, DV, false, false>(p, n_cu, s);
 }
 
-// Compute units of the current device (cached per device).
+// Compute units of the current device (cached per device; concurrent first
+// calls store the same value).
 int device_cus() {
-  static int cache[64] = {0};
+  static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cache[dev] == 0) {
-    int n = 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cache[dev] = n;
+    cache[dev].store(n, std::memory_order_relaxed);
   }
-  return cache[dev];
+  return n;
 }
 
 }  // namespace

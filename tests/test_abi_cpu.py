@@ -189,6 +189,7 @@ def _good_args(**over):
     (dict(use_max_logit=2), 1),
     (dict(use_max_logit=1, max_logit=math.nan), 1),
     (dict(use_max_logit=1, max_logit=math.inf), 1),
+    (dict(Hq=1 << 20, L=1 << 20, n_q_blocks=4096), 2),   # items beyond int32
 ])
 def test_forward_validation_errors(over, code):
     lib = _lib.load()

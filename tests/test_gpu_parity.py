@@ -224,6 +224,29 @@ def test_split_kv_every_element(case):
     _announce(f"  max-abs o {eo:.3g} lse {el:.3g}")
 
 
+def test_ragged_full_length_persistent():
+    """L = 32768 - 37 (a ragged last q block and kv block) with GQA 16/4 and
+    a causal 4096-key window: 2048 items over the persistent rounds; sampled
+    rows (both ends of every edge block class) against the oracle."""
+    B, Hq, Hkv, L, d = 1, 16, 4, 32768 - 37, 128
+    _announce(f"ragged full length B={B} Hq={Hq} Hkv={Hkv} L={L}")
+    q, k, v = (stored(a, "bf16") for a in draw_qkv(B, Hq, Hkv, L, d, d, 41))
+    mk = dict(causal=True, window_left=4095)
+    o, lse = splash_fwd(q.cuda(), k.cuda(), v.cuda(), **mk)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(41)
+    rows = _sample_rows(L, 256, rng)
+    heads = [(0, 0), (0, 5), (0, Hq - 1)]
+    o_ref, lse_ref = attention_ref(as_f64(q), as_f64(k), as_f64(v), scale=d ** -0.5, rows=rows,
+                                   heads=heads, **mk)
+    o_np = o.float().cpu().numpy()
+    lse_np = lse.cpu().numpy()
+    for (b, h) in heads:
+        _compare(o_np[b, h, rows].astype(np.float64), lse_np[b, h, rows].astype(np.float64),
+                 o_ref[b, h], lse_ref[b, h], "bf16")
+    assert bool(torch.isfinite(lse).all())
+
+
 def test_split_kv_rows_without_keys_and_reuse():
     """Rows with no allowed key stay o = 0, lse = -inf through the merge;
     one workspace serves two calls in a row, the second smaller."""
