@@ -37,24 +37,28 @@ import numpy as np
 def allowed(i, j, *, L_q: int, L_kv: int, causal: bool = False,
             window_left: int = -1, window_right: int = -1,
             seg_q: Optional[np.ndarray] = None,
-            seg_kv: Optional[np.ndarray] = None) -> np.ndarray:
-    """Element mask: True where query position ``i`` may attend key ``j``.
+            seg_kv: Optional[np.ndarray] = None, q_offset: int = 0) -> np.ndarray:
+    """Element mask: True where query row ``i`` may attend key ``j``.
 
     ``i`` and ``j`` are integer arrays that broadcast against each other
     (typically a column and a row of positions).  The mask is the logical
     AND of the causal, local-window and segment-id (document) masks
     (Lecture 13 section 6.4; causal mask: joto.ai "Causal Mask" section),
-    and of ``i < L_q`` and ``j < L_kv`` (padding is masked).
+    and of ``i < L_q`` and ``j < L_kv`` (padding is masked).  Query row i
+    sits at key position ``q_offset + i`` for the causal and window tests
+    (0: queries and keys aligned; decoding the last L_q of L_kv positions
+    uses L_kv - L_q); segment ids are looked up by row and key index.
     """
     i = np.asarray(i, dtype=np.int64)
     j = np.asarray(j, dtype=np.int64)
     ok = (i < L_q) & (j < L_kv) & (i >= 0) & (j >= 0)
+    pos = i + int(q_offset)
     if causal:
-        ok = ok & (j <= i)
+        ok = ok & (j <= pos)
     if window_left >= 0:
-        ok = ok & (i - j <= window_left)
+        ok = ok & (pos - j <= window_left)
     if window_right >= 0:
-        ok = ok & (j - i <= window_right)
+        ok = ok & (j - pos <= window_right)
     if seg_q is not None:
         sq = np.asarray(seg_q, dtype=np.int64)
         skv = sq if seg_kv is None else np.asarray(seg_kv, dtype=np.int64)
@@ -76,7 +80,8 @@ def attention_ref(q, k, v, *, scale: float, soft_cap: float = 0.0,
                   window_right: int = -1, seg_q=None, seg_kv=None,
                   rows: Optional[Sequence[int]] = None,
                   heads: Optional[Iterable[tuple]] = None,
-                  panel: int = 512, max_logit: Optional[float] = None):
+                  panel: int = 512, max_logit: Optional[float] = None,
+                  q_offset: int = 0):
     """Exact masked attention forward in float64.
 
     Shapes: ``q`` [B, Hq, L_q, d_qk], ``k`` [B, Hkv, L_kv, d_qk],
@@ -84,7 +89,8 @@ def attention_ref(q, k, v, *, scale: float, soft_cap: float = 0.0,
     and widened to float64).  ``seg_q``/``seg_kv`` are [L] or [B, L]
     integer ids (``seg_kv`` defaults to ``seg_q``).  ``rows`` restricts the
     computation to those query positions (sampled outputs); ``heads`` to
-    those (b, h) pairs.
+    those (b, h) pairs.  ``q_offset``: key position of query row 0 (see
+    ``allowed``).
 
     Returns ``(o, lse)``: o [B, Hq, n_rows, d_v] and lse [B, Hq, n_rows] in
     float64.  Heads not in ``heads`` are left as NaN.
@@ -133,7 +139,8 @@ def attention_ref(q, k, v, *, scale: float, soft_cap: float = 0.0,
                 s = soft_cap * np.tanh(s / soft_cap)
             a = allowed(sel[:, None], kv_pos, L_q=L_q, L_kv=L_kv,
                         causal=causal, window_left=window_left,
-                        window_right=window_right, seg_q=sq, seg_kv=skv)
+                        window_right=window_right, seg_q=sq, seg_kv=skv,
+                        q_offset=q_offset)
             s_a = np.where(a, s, -np.inf)
             has = a.any(axis=1)
             if max_logit is None:
@@ -168,7 +175,7 @@ def mle_safe_range(max_logit: float, min_row_max: float):
 
 def attention_brute(q, k, v, *, scale: float, soft_cap: float = 0.0,
                     causal: bool = False, window_left: int = -1,
-                    window_right: int = -1, seg_q=None, seg_kv=None):
+                    window_right: int = -1, seg_q=None, seg_kv=None, q_offset: int = 0):
     """Scalar-loop attention for tiny inputs (a pin for ``attention_ref``).
 
     Uses the plain definition without the max shift: w_ij = e^{s_ij} /
@@ -194,13 +201,14 @@ def attention_brute(q, k, v, *, scale: float, soft_cap: float = 0.0,
             oh, lh = [], []
             for i in range(L_q):
                 exps, idx = [], []
+                pos = i + q_offset
                 for j in range(L_kv):
                     ok = True
-                    if causal and j > i:
+                    if causal and j > pos:
                         ok = False
-                    if window_left >= 0 and i - j > window_left:
+                    if window_left >= 0 and pos - j > window_left:
                         ok = False
-                    if window_right >= 0 and j - i > window_right:
+                    if window_right >= 0 and j - pos > window_right:
                         ok = False
                     if sq is not None and int(sq[i]) != int(skv[j]):
                         ok = False

@@ -44,9 +44,10 @@ def mask_tables_ref(L_q: int, L_kv: int, block_q: int, block_kv: int, *,
                     causal: bool = False, window_left: int = -1,
                     window_right: int = -1,
                     seg_q: Optional[np.ndarray] = None,
-                    seg_kv: Optional[np.ndarray] = None) -> dict:
+                    seg_kv: Optional[np.ndarray] = None, q_offset: int = 0) -> dict:
     """Build every MaskInfo array by scanning the element mask block row by
-    block row.  Returns a dict of numpy arrays plus the size counters."""
+    block row (query row i at key position q_offset + i).  Returns a dict of
+    numpy arrays plus the size counters."""
     nq = -(-L_q // block_q)
     nkv = -(-L_kv // block_kv)
     full_count = block_q * block_kv
@@ -60,7 +61,7 @@ def mask_tables_ref(L_q: int, L_kv: int, block_q: int, block_kv: int, *,
         q_pos = np.arange(r * block_q, (r + 1) * block_q)[:, None]
         m = allowed(q_pos, kv_pos, L_q=L_q, L_kv=L_kv, causal=causal,
                     window_left=window_left, window_right=window_right,
-                    seg_q=seg_q, seg_kv=seg_kv)
+                    seg_q=seg_q, seg_kv=seg_kv, q_offset=q_offset)
         blocks = m.reshape(block_q, nkv, block_kv)
         counts = blocks.sum(axis=(0, 2))
         row_active = []

@@ -70,7 +70,7 @@ def test_pattern_counts_section_6_6():
     assert t["partial_mask_blocks"].nbytes == int(g["window_pattern_bytes"])
 
 
-def _brute_tables(L_q, L_kv, bq, bkv, causal, wl, wr, seg_q, seg_kv):
+def _brute_tables(L_q, L_kv, bq, bkv, causal, wl, wr, seg_q, seg_kv, q_offset=0):
     """Independent scan with scalar loops (no numpy mask algebra)."""
     nq = (L_q + bq - 1) // bq
     nkv = (L_kv + bkv - 1) // bkv
@@ -78,11 +78,12 @@ def _brute_tables(L_q, L_kv, bq, bkv, causal, wl, wr, seg_q, seg_kv):
     def ok(i, j):
         if i >= L_q or j >= L_kv:
             return False
-        if causal and j > i:
+        pos = i + q_offset
+        if causal and j > pos:
             return False
-        if wl >= 0 and i - j > wl:
+        if wl >= 0 and pos - j > wl:
             return False
-        if wr >= 0 and j - i > wr:
+        if wr >= 0 and j - pos > wr:
             return False
         if seg_q is not None and seg_q[i] != seg_kv[j]:
             return False
@@ -141,3 +142,25 @@ def test_tables_match_brute_scan(L, bq, bkv, causal, wl, wr, use_seg, seed):
     assert sorted(order) == list(range(len(lens)))
     for a, b in zip(order, order[1:]):
         assert lens[a] > lens[b] or (lens[a] == lens[b] and a < b)
+
+
+@settings(max_examples=60, deadline=None)
+@given(Lq=st.integers(1, 20), Lkv=st.integers(1, 40), off=st.integers(0, 30),
+       bq=st.sampled_from([1, 2, 4]), bkv=st.sampled_from([1, 3, 8]), causal=st.booleans(),
+       wl=st.integers(-1, 9), wr=st.integers(-1, 9), use_seg=st.booleans(),
+       seed=st.integers(0, 1000))
+def test_tables_match_brute_scan_with_offsets(Lq, Lkv, off, bq, bkv, causal, wl, wr, use_seg,
+                                              seed):
+    """Queries at key positions q_offset + i (decode shapes, L_q != L_kv)."""
+    sq = skv = None
+    if use_seg:
+        rng = np.random.default_rng(seed)
+        sq = rng.integers(0, 3, size=Lq).astype(np.int32)
+        skv = rng.integers(0, 3, size=Lkv).astype(np.int32)
+    t = mask_tables_ref(Lq, Lkv, bq, bkv, causal=causal, window_left=wl, window_right=wr,
+                        seg_q=sq, seg_kv=skv, q_offset=off)
+    classes, pats, nxt = _brute_tables(Lq, Lkv, bq, bkv, causal, wl, wr, sq, skv, off)
+    assert t["block_mask"].tolist() == classes
+    assert t["mask_next"].tolist() == nxt
+    for p, bits in zip(t["partial_mask_blocks"], pats):
+        assert p.tolist() == [list(r) for r in bits]

@@ -267,3 +267,42 @@ def test_mle_constant_cancels(c, mask):
     ob, lb = attention_brute(q, k, v, **kw)
     assert np.max(np.abs(o1 - np.asarray(ob))) < 1e-12
     assert np.max(np.abs(l1 - np.asarray(lb))) < 1e-10
+
+
+@pytest.mark.parametrize("mk", [dict(causal=True), dict(causal=True, window_left=9),
+                                dict(window_left=5, window_right=3), dict(causal=True, segs=True)])
+def test_decode_rows_are_rows_of_aligned_attention(mk):
+    """Queries at key positions q_offset + i (decoding the last L_q of L_kv
+    positions, q_offset = L_kv - L_q) see exactly what those rows see in
+    the aligned attention over all L_kv positions."""
+    B, H, L, Lq, d = 2, 3, 37, 5, 4
+    q, k, v = _rand_case(5, B, H, H, L, d, d)
+    mk = dict(mk)
+    seg = None
+    if mk.pop("segs", False):
+        seg = np.repeat(np.arange(5), 8)[:L].astype(np.int64)
+    o_full, l_full = attention_ref(q, k, v, scale=0.7, seg_q=seg, **mk)
+    o_dec, l_dec = attention_ref(q[:, :, L - Lq:], k, v, scale=0.7, q_offset=L - Lq,
+                                 seg_q=None if seg is None else seg[L - Lq:], seg_kv=seg, **mk)
+    assert np.max(np.abs(o_dec - o_full[:, :, L - Lq:])) < 1e-12
+    assert np.max(np.abs(l_dec - l_full[:, :, L - Lq:])) < 1e-12
+
+
+@settings(max_examples=40, deadline=None)
+@given(seed=st.integers(0, 10_000), Lq=st.integers(1, 6), Lkv=st.integers(1, 11),
+       off=st.integers(0, 12), causal=st.booleans(), wl=st.integers(-1, 5),
+       wr=st.integers(-1, 5), cap=st.sampled_from([0.0, 2.0]))
+def test_ref_matches_brute_force_with_offsets(seed, Lq, Lkv, off, causal, wl, wr, cap):
+    rng = np.random.default_rng(seed)
+    q = rng.normal(size=(1, 2, Lq, 3))
+    k = rng.normal(size=(1, 1, Lkv, 3))
+    v = rng.normal(size=(1, 1, Lkv, 2))
+    kw = dict(scale=0.9, soft_cap=cap, causal=causal, window_left=wl, window_right=wr,
+              q_offset=off)
+    o, lse = attention_ref(q, k, v, panel=2, **kw)
+    ob, lb = attention_brute(q, k, v, **kw)
+    assert np.max(np.abs(o - np.asarray(ob))) < 1e-12
+    lb = np.asarray(lb)
+    assert np.array_equal(np.isneginf(lse), np.isneginf(lb))
+    fin = np.isfinite(lb)
+    assert np.max(np.abs(lse[fin] - lb[fin]), initial=0.0) < 1e-12
