@@ -38,7 +38,8 @@ c_ptr = ctypes.c_void_p
 class MaskDesc(ctypes.Structure):
     _fields_ = [("L_q", c_i32), ("L_kv", c_i32), ("block_q", c_i32),
                 ("block_kv", c_i32), ("causal", c_i32), ("window_left", c_i32),
-                ("window_right", c_i32), ("seg_q", c_ptr), ("seg_kv", c_ptr)]
+                ("window_right", c_i32), ("seg_q", c_ptr), ("seg_kv", c_ptr),
+                ("q_offset", c_i32)]
 
 
 class MaskSizes(ctypes.Structure):

@@ -79,14 +79,15 @@ class MaskTables:
 
 def compile_mask(L_q: int, block_q: int, block_kv: int, *, L_kv: Optional[int] = None,
                  causal: bool = False, window_left: int = -1, window_right: int = -1,
-                 seg_q=None, seg_kv=None) -> MaskTables:
-    """Run ``attn_mask_compile`` (both phases) and return the host tables."""
+                 seg_q=None, seg_kv=None, q_offset: int = 0) -> MaskTables:
+    """Run ``attn_mask_compile`` (both phases) and return the host tables.
+    Query row i sits at key position ``q_offset + i``."""
     lib = _lib.load()
     L_kv = L_q if L_kv is None else L_kv
     sq = _seg_array(seg_q, L_q)
     skv = _seg_array(seg_kv, L_kv) if seg_kv is not None else None
     desc = _lib.MaskDesc(L_q, L_kv, block_q, block_kv, int(bool(causal)), window_left,
-                         window_right, _ptr(sq), _ptr(skv))
+                         window_right, _ptr(sq), _ptr(skv), int(q_offset))
     sizes = _lib.MaskSizes()
     _lib.check(lib.attn_mask_compile(ctypes.byref(desc), ctypes.byref(sizes), None))
     nq, nkv, na, npat = sizes.n_q_blocks, sizes.n_kv_blocks, sizes.n_active, sizes.n_patterns

@@ -41,6 +41,7 @@ struct Run {
 
 struct MaskSpec {
   int64_t Lq, Lkv, bq, bkv;
+  int64_t qoff;                 // key position of query row 0
   bool causal;
   int64_t wl, wr;
   const int32_t* sq;
@@ -49,11 +50,13 @@ struct MaskSpec {
   std::vector<int32_t> run_of;  // key -> index of its run
 
   // Allowed keys of row i before the segment test: [lo, hi] (empty if lo>hi).
+  // Row i sits at key position qoff + i.
   void interval(int64_t i, int64_t* lo, int64_t* hi) const {
+    const int64_t pos = qoff + i;
     int64_t a = 0, b = Lkv - 1;
-    if (causal) b = std::min(b, i);
-    if (wl >= 0) a = std::max(a, i - wl);
-    if (wr >= 0) b = std::min(b, i + wr);
+    if (causal) b = std::min(b, pos);
+    if (wl >= 0) a = std::max(a, pos - wl);
+    if (wr >= 0) b = std::min(b, pos + wr);
     *lo = a;
     *hi = b;
   }
@@ -110,6 +113,7 @@ int compile(const splash_mask_desc& d, Compiled* out) {
   MaskSpec m;
   m.Lq = d.L_q;
   m.Lkv = d.L_kv;
+  m.qoff = d.q_offset;
   m.bq = d.block_q;
   m.bkv = d.block_kv;
   m.causal = d.causal != 0;
@@ -235,6 +239,8 @@ extern "C" int attn_mask_compile(const splash_mask_desc* desc, splash_mask_sizes
                         d.block_q, d.block_kv);
   if (d.causal != 0 && d.causal != 1)
     return splash::fail(SPLASH_EINVAL, "attn_mask_compile: causal must be 0 or 1");
+  if (d.q_offset < 0)
+    return splash::fail(SPLASH_EINVAL, "attn_mask_compile: q_offset must be >= 0 (%d)", d.q_offset);
   if (d.window_left < -1 || d.window_right < -1)
     return splash::fail(SPLASH_EINVAL, "attn_mask_compile: window must be -1 or >= 0 (%d, %d)",
                         d.window_left, d.window_right);

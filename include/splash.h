@@ -98,12 +98,13 @@ const char* splash_last_error(void);
  * Mask preprocessing (MaskInfo).
  * ---------------------------------------------------------------------- */
 
-/* The mask: element (i, j) (query position i, key position j) is allowed iff
+/* The mask: element (i, j) (query row i, key position j) is allowed iff
  *   i < L_q and j < L_kv                      (padding of ragged blocks)
- *   and (!causal or j <= i)
- *   and (window_left  < 0 or i - j <= window_left)
- *   and (window_right < 0 or j - i <= window_right)
- *   and (seg_q == NULL or seg_q[i] == seg_kv[j]).
+ *   and (!causal or j <= p)
+ *   and (window_left  < 0 or p - j <= window_left)
+ *   and (window_right < 0 or j - p <= window_right)
+ *   and (seg_q == NULL or seg_q[i] == seg_kv[j]),
+ * where p = q_offset + i is the key position of query row i.
  * The blocks are block_q x block_kv; the last block row / column may hang
  * over the sequence end (ragged L), its padded elements count as masked. */
 typedef struct splash_mask_desc {
@@ -117,6 +118,10 @@ typedef struct splash_mask_desc {
   const int32_t* seg_q;   /* host [L_q] segment ids, or NULL: no segment mask */
   const int32_t* seg_kv;  /* host [L_kv], or NULL: same array as seg_q
                              (then L_kv must equal L_q) */
+  int32_t q_offset;       /* >= 0: query row i sits at key position
+                             q_offset + i in the causal and window tests
+                             (0: aligned; decoding the last L_q of L_kv
+                             positions: L_kv - L_q) */
 } splash_mask_desc;
 
 typedef struct splash_mask_sizes {

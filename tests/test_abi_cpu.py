@@ -86,6 +86,23 @@ def test_tables_bit_exact_random(Lq, dL, bq, bkv, causal, wl, wr, seg_mode, seed
     _assert_tables_equal(t, mask_tables_ref(Lq, Lkv, bq, bkv, **kw))
 
 
+@settings(max_examples=100, deadline=None)
+@given(Lq=st.integers(1, 80), Lkv=st.integers(1, 200), off=st.integers(0, 150),
+       bq=st.sampled_from([1, 4, 16, 64]), bkv=st.sampled_from([1, 5, 16, 64]),
+       causal=st.booleans(), wl=st.integers(-1, 40), wr=st.integers(-1, 40),
+       use_seg=st.booleans(), seed=st.integers(0, 10_000))
+def test_tables_bit_exact_with_offsets(Lq, Lkv, off, bq, bkv, causal, wl, wr, use_seg, seed):
+    """Decode shapes: query row i at key position q_offset + i."""
+    rng = np.random.default_rng(seed)
+    sq = skv = None
+    if use_seg:
+        sq = rng.integers(0, 3, size=Lq).astype(np.int32)
+        skv = np.sort(rng.integers(0, 3, size=Lkv)).astype(np.int32)
+    kw = dict(causal=causal, window_left=wl, window_right=wr, seg_q=sq, seg_kv=skv)
+    t = compile_mask(Lq, bq, bkv, L_kv=Lkv, q_offset=off, **kw)
+    _assert_tables_equal(t, mask_tables_ref(Lq, Lkv, bq, bkv, q_offset=off, **kw))
+
+
 def test_empty_and_no_allowed_mask():
     t = compile_mask(0, 64, 64, causal=True)
     assert t.n_q_blocks == 0 and t.n_active == 0 and t.row_ptr.tolist() == [0]
@@ -116,6 +133,7 @@ def test_mask_compile_errors():
         _lib.MaskDesc(10, 10, 4, 4, 2, -1, -1, None, None),
         _lib.MaskDesc(10, 10, 4, 4, 0, -2, -1, None, None),
         _lib.MaskDesc(10, 10, 4, 4, 0, -1, -7, None, None),
+        _lib.MaskDesc(10, 10, 4, 4, 1, -1, -1, None, None, -1),
     ]
     for d in bad:
         assert _compile_raw(d) == 1
