@@ -68,7 +68,8 @@ class FwdArgs(ctypes.Structure):
                 ("partial_mask_blocks", c_ptr),
                 ("mask_mode", c_i32), ("scale", ctypes.c_float),
                 ("soft_cap", ctypes.c_float),
-                ("use_max_logit", c_i32), ("max_logit", ctypes.c_float)]
+                ("use_max_logit", c_i32), ("max_logit", ctypes.c_float),
+                ("L_kv", c_i32), ("q_offset", c_i32)]
 
 
 class SplashError(RuntimeError):

@@ -54,6 +54,7 @@ class MaskTables:
     row_ptr: np.ndarray
     row_order: np.ndarray
     partial_mask_blocks: np.ndarray
+    q_offset: int = 0
     _device: dict = field(default_factory=dict, repr=False)
 
     def device(self, device):
@@ -106,7 +107,8 @@ def compile_mask(L_q: int, block_q: int, block_kv: int, *, L_kv: Optional[int] =
     _lib.check(lib.attn_mask_compile(ctypes.byref(desc), ctypes.byref(sizes), ctypes.byref(tabs)))
     arrays["block_mask"] = arrays["block_mask"].reshape(nq, nkv)
     arrays["partial_mask_blocks"] = arrays["partial_mask_blocks"].reshape(npat, block_q, block_kv)
-    return MaskTables(L_q, L_kv, block_q, block_kv, nq, nkv, na, sizes.n_partial, npat, **arrays)
+    return MaskTables(L_q, L_kv, block_q, block_kv, nq, nkv, na, sizes.n_partial, npat, **arrays,
+                      q_offset=int(q_offset))
 
 
 def fwd_tile(dtype: str, d_qk: int, d_v: int):
@@ -130,12 +132,16 @@ def splash_fwd(q, k, v, *, scale: Optional[float] = None, soft_cap: float = 0.0,
                causal: bool = False, window_left: int = -1, window_right: int = -1,
                seg_q=None, seg_kv=None, tables: Optional[MaskTables] = None,
                mask_mode: str = "computed", out=None, lse=None, return_lse: bool = True,
-               max_logit: Optional[float] = None, n_split: int = 1, workspace=None, stream=None):
+               max_logit: Optional[float] = None, n_split: int = 1, workspace=None,
+               q_offset: int = 0, stream=None):
     """Block-sparse attention forward on the GPU.
 
-    q [B, Hq, L, d_qk], k [B, Hkv, L, d_qk], v [B, Hkv, L, d_v]: contiguous
-    torch tensors on one GPU, all float32 or all bfloat16.  ``seg_q`` /
-    ``seg_kv``: segment ids [L] (shared by the batch) or [B, L].  ``tables``:
+    q [B, Hq, L, d_qk], k [B, Hkv, L_kv, d_qk], v [B, Hkv, L_kv, d_v]:
+    contiguous torch tensors on one GPU, all float32 or all bfloat16.  Query
+    row i sits at key position ``q_offset + i`` (decoding the last L of L_kv
+    positions: ``q_offset = L_kv - L``); L_kv != L or q_offset != 0 is bf16
+    only.  ``seg_q``: segment ids [L] (shared by the batch) or [B, L];
+    ``seg_kv``: [L_kv] or [B, L_kv] (required when L_kv != L).  ``tables``:
     a MaskTables compiled for this mask at the kernel's block sizes
     (``fwd_tile``); compiled here when omitted.  ``max_logit``: the Max Logit
     Estimate constant (logit units) used instead of the running row max, or
@@ -156,9 +162,9 @@ def splash_fwd(q, k, v, *, scale: Optional[float] = None, soft_cap: float = 0.0,
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be [B, H, L, d]")
     B, Hq, L, d_qk = q.shape
-    Hkv = k.shape[1]
+    Hkv, L_kv = k.shape[1], k.shape[2]
     d_v = v.shape[3]
-    if tuple(k.shape) != (B, Hkv, L, d_qk) or tuple(v.shape[:3]) != (B, Hkv, L):
+    if tuple(k.shape) != (B, Hkv, L_kv, d_qk) or tuple(v.shape[:3]) != (B, Hkv, L_kv):
         raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
     q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
     if scale is None:
@@ -174,11 +180,13 @@ def splash_fwd(q, k, v, *, scale: Optional[float] = None, soft_cap: float = 0.0,
         skv = None
         if seg_kv is not None:
             skv = torch.as_tensor(np.asarray(seg_kv.cpu() if hasattr(seg_kv, "cpu") else seg_kv),
-                                  dtype=torch.int32).reshape(-1, L)
+                                  dtype=torch.int32).reshape(-1, L_kv)
+        elif L_kv != L:
+            raise ValueError("seg_kv is required when L_kv != L")
         rows_q = sq.expand(B, L) if sq.shape[0] == 1 else sq
-        rows_kv = None if skv is None else (skv.expand(B, L) if skv.shape[0] == 1 else skv)
+        rows_kv = None if skv is None else (skv.expand(B, L_kv) if skv.shape[0] == 1 else skv)
         if rows_q.shape[0] != B or (rows_kv is not None and rows_kv.shape[0] != B):
-            raise ValueError("segment ids must be [L] or [B, L]")
+            raise ValueError("segment ids must be [L] or [B, L] ([L_kv] or [B, L_kv] for seg_kv)")
         per_batch = B > 1 and (not bool((rows_q == rows_q[:1]).all()) or
                                (rows_kv is not None and not bool((rows_kv == rows_kv[:1]).all())))
         seg_q_dev = rows_q.contiguous().to(q.device)
@@ -206,13 +214,15 @@ def splash_fwd(q, k, v, *, scale: Optional[float] = None, soft_cap: float = 0.0,
         if tables is None or per_batch:
             ids_q = None if seg_q_dev is None else seg_q_dev[bsel or 0].cpu().numpy()
             ids_kv = None if seg_kv_dev is None else seg_kv_dev[bsel or 0].cpu().numpy()
-            tabs = compile_mask(L, bq, bkv, causal=causal, window_left=window_left,
-                                window_right=window_right, seg_q=ids_q, seg_kv=ids_kv)
+            tabs = compile_mask(L, bq, bkv, L_kv=L_kv, causal=causal, window_left=window_left,
+                                window_right=window_right, seg_q=ids_q, seg_kv=ids_kv,
+                                q_offset=q_offset)
         else:
             tabs = tables
-        if (tabs.block_q, tabs.block_kv, tabs.L_q) != (bq, bkv, L):
-            raise ValueError(f"tables were compiled for L={tabs.L_q} blocks "
-                             f"{tabs.block_q}x{tabs.block_kv}; need L={L} blocks {bq}x{bkv}")
+        got = (tabs.block_q, tabs.block_kv, tabs.L_q, tabs.L_kv, tabs.q_offset)
+        if got != (bq, bkv, L, L_kv, q_offset):
+            raise ValueError(f"tables were compiled for (block_q, block_kv, L_q, L_kv, q_offset)="
+                             f"{got}; need {(bq, bkv, L, L_kv, q_offset)}")
         dev = tabs.device(q.device)
         if bsel is None:
             qb, kb, vb, ob = q, k, v, out
@@ -237,7 +247,8 @@ def splash_fwd(q, k, v, *, scale: Optional[float] = None, soft_cap: float = 0.0,
             dev["active_cols"].data_ptr(), dev["block_code"].data_ptr(),
             dev["mask_next"].data_ptr(), dev["partial_mask_blocks"].data_ptr(),
             _MASK_MODES[mask_mode], float(scale), float(soft_cap),
-            0 if max_logit is None else 1, 0.0 if max_logit is None else float(max_logit))
+            0 if max_logit is None else 1, 0.0 if max_logit is None else float(max_logit),
+            L_kv, int(q_offset))
         if n_split == 1:
             _lib.check(lib.splash_attn_fwd(ctypes.byref(args), ctypes.c_void_p(stream)))
         else:

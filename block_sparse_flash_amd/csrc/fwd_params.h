@@ -12,11 +12,13 @@ struct FwdParams {
   const void* v;
   void* o;
   float* lse;          // may be null
-  int32_t B, Hq, Hkv, L, group;  // group = Hq / Hkv
+  int32_t B, Hq, Hkv, L, group;  // L: query rows; group = Hq / Hkv
+  int32_t Lkv;            // key/value positions
+  int32_t q_off;          // query row i sits at key position q_off + i
   // mask
   int32_t causal, window_left, window_right;
   const int32_t* seg_q;   // [B, L] or null
-  const int32_t* seg_kv;  // [B, L] or null (then seg_q is used)
+  const int32_t* seg_kv;  // [B, Lkv] or null (then seg_q is used, Lkv = L)
   int32_t mask_stored;    // 1: partial blocks read patterns
   // tables
   int32_t n_q_blocks;

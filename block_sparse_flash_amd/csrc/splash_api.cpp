@@ -94,6 +94,14 @@ int prepare(const splash_fwd_args* args, const char* fn, splash::FwdParams* out)
   if (a.use_max_logit && !std::isfinite(a.max_logit))
     return splash::fail(SPLASH_EINVAL, "%s: max_logit must be finite", fn);
   if (!a.seg_q && a.seg_kv) return splash::fail(SPLASH_EINVAL, "%s: seg_kv given without seg_q", fn);
+  if (a.L_kv < 0 || a.q_offset < 0)
+    return splash::fail(SPLASH_EINVAL, "%s: negative L_kv=%d or q_offset=%d", fn, a.L_kv, a.q_offset);
+  const int32_t Lkv = a.L_kv == 0 ? a.L : a.L_kv;
+  const bool decode = Lkv != a.L || a.q_offset != 0;
+  if (decode && a.dtype != SPLASH_BF16)
+    return splash::fail(SPLASH_EUNSUPPORTED, "%s: L_kv != L or q_offset != 0 needs bf16", fn);
+  if (a.seg_q && !a.seg_kv && Lkv != a.L)
+    return splash::fail(SPLASH_EINVAL, "%s: seg_kv is NULL but L_kv (%d) != L (%d)", fn, Lkv, a.L);
 
   int32_t bq = 0, bkv = 0;
   splash_fwd_tile(a.dtype, a.d_qk, a.d_v, &bq, &bkv);
@@ -111,7 +119,12 @@ int prepare(const splash_fwd_args* args, const char* fn, splash::FwdParams* out)
   if (n_heads == 0 || a.L == 0) return -1;  // nothing to compute
   const int64_t n_wg = n_heads * nq;
   const int64_t max_d = a.d_qk > a.d_v ? a.d_qk : a.d_v;
-  if (n_wg > INT32_MAX || n_heads * a.L > (int64_t{1} << 46) / max_d)
+  // Byte offsets inside one head's q, k or v (buffer ranges) and key
+  // positions q_offset + row (+ window) stay within int32.
+  const int64_t max_len = a.L > Lkv ? a.L : Lkv;
+  if (n_wg > INT32_MAX || n_heads * max_len > (int64_t{1} << 46) / max_d ||
+      (max_len + 2 * bq) * max_d * 2 > INT32_MAX ||
+      static_cast<int64_t>(a.q_offset) + a.L + Lkv + 2 * bq > INT32_MAX)
     return splash::fail(SPLASH_ESHAPE, "%s: problem too large", fn);
 
   if (!a.q || !a.k || !a.v || !a.o) return splash::fail(SPLASH_EINVAL, "%s: NULL q/k/v/o", fn);
@@ -135,10 +148,14 @@ int prepare(const splash_fwd_args* args, const char* fn, splash::FwdParams* out)
   p.Hq = a.Hq;
   p.Hkv = a.Hkv;
   p.L = a.L;
+  p.Lkv = Lkv;
+  p.q_off = a.q_offset;
   p.group = a.Hq / a.Hkv;
   p.causal = a.causal;
-  p.window_left = a.window_left;
-  p.window_right = a.window_right;
+  // Windows wider than the key range restrict nothing; clamping them keeps
+  // position + window within int32 in the kernels.
+  p.window_left = a.window_left > Lkv ? Lkv : a.window_left;
+  p.window_right = a.window_right > Lkv ? Lkv : a.window_right;
   p.seg_q = a.seg_q;
   p.seg_kv = a.seg_kv;
   p.mask_stored = a.mask_mode == SPLASH_MASK_STORED ? 1 : 0;

@@ -257,21 +257,23 @@ __device__ __forceinline__ void item_fwd(const FwdParams& p, int head, int r, in
   const int b = head / p.Hq;
   const int hq = head - b * p.Hq;
   const int kvh = b * p.Hkv + hq / p.group;
-  const int L = p.L;
+  const int L = p.L;      // query rows
+  const int Lk = p.Lkv;   // key positions
   const int qw = r * BM + wave * 32;  // first query row of this wave
   const int qi = qw + l32;            // this lane's query row
+  const int qp = p.q_off + qi;        // its key position (causal, window)
 
   const uint16_t* qg = static_cast<const uint16_t*>(p.q) + (int64_t)head * L * DQK;
-  const uint16_t* kg = static_cast<const uint16_t*>(p.k) + (int64_t)kvh * L * DQK;
-  const uint16_t* vg = static_cast<const uint16_t*>(p.v) + (int64_t)kvh * L * DV;
+  const uint16_t* kg = static_cast<const uint16_t*>(p.k) + (int64_t)kvh * Lk * DQK;
+  const uint16_t* vg = static_cast<const uint16_t*>(p.v) + (int64_t)kvh * Lk * DV;
   // Buffer resources: reads past the sequence end return zero.
   const uint64_t qaddr = reinterpret_cast<uint64_t>(qg);
   const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(qaddr >> 32)) << 32) |
               (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)qaddr)),
       (short)0, __builtin_amdgcn_readfirstlane(L * DQK * 2), kRsrcWord3);
-  const u32x4 krs = uniform(make_rsrc(kg, (uint32_t)(L * DQK * 2)));
-  const u32x4 vrs = uniform(make_rsrc(vg, (uint32_t)(L * DV * 2)));
+  const u32x4 krs = uniform(make_rsrc(kg, (uint32_t)(Lk * DQK * 2)));
+  const u32x4 vrs = uniform(make_rsrc(vg, (uint32_t)(Lk * DV * 2)));
 
   // No LDS initialisation: every tile copy covers its whole tile (rows past
   // the sequence end read as zero through the buffer range check) and the
@@ -303,15 +305,16 @@ __device__ __forceinline__ void item_fwd(const FwdParams& p, int head, int r, in
 
   const bool has_seg = p.seg_q != nullptr;
   const int32_t* segq = has_seg ? p.seg_q + (int64_t)b * L : nullptr;
-  const int32_t* segk = has_seg ? (p.seg_kv ? p.seg_kv + (int64_t)b * L : segq) : nullptr;
+  const int32_t* segk = has_seg ? (p.seg_kv ? p.seg_kv + (int64_t)b * Lk : segq) : nullptr;
   const int my_seg = (has_seg && qi < L) ? segq[qi] : 0;
   // Allowed key interval of this lane's row before the segment test.
-  int klo = 0, khi = L - 1;
-  if (p.causal) khi = min(khi, qi);
-  if (p.window_left >= 0) klo = max(klo, qi - p.window_left);
-  if (p.window_right >= 0) khi = min(khi, qi + p.window_right);
-  const int qa = qw;
-  const int qb = min(qw + 31, L - 1);
+  int klo = 0, khi = Lk - 1;
+  if (p.causal) khi = min(khi, qp);
+  if (p.window_left >= 0) klo = max(klo, qp - p.window_left);
+  if (p.window_right >= 0) khi = min(khi, qp + p.window_right);
+  // Key positions of this wave's first and last valid query rows.
+  const int qa = p.q_off + qw;
+  const int qb = p.q_off + min(qw + 31, L - 1);
 
   // Blocks [row_ptr[r] + lo, row_ptr[r] + hi) of the active list: chunk
   // `split` of n_split near-equal contiguous chunks.
@@ -353,7 +356,7 @@ __device__ __forceinline__ void item_fwd(const FwdParams& p, int head, int r, in
       return;
     }
     // Corner tests on this wave's rows: no element mask when all are allowed.
-    const bool all = !has_seg && kz < L && (!p.causal || kz <= qa) &&
+    const bool all = !has_seg && kz < Lk && (!p.causal || kz <= qa) &&
                      (p.window_left < 0 || qb - ka <= p.window_left) &&
                      (p.window_right < 0 || kz - qa <= p.window_right);
     if (all) return;
@@ -362,7 +365,7 @@ __device__ __forceinline__ void item_fwd(const FwdParams& p, int head, int r, in
         constexpr int t = SIDX(i_) / 16;
         constexpr int i = SIDX(i_) % 16;
         const int key = ka + 32 * t + 8 * (i / 4) + 4 * hi + (i % 4);
-        const bool ok = (key >= klo) & (key <= khi) & (segk[min(key, L - 1)] == my_seg);
+        const bool ok = (key >= klo) & (key <= khi) & (segk[min(key, Lk - 1)] == my_seg);
         sv[t][i] = ok ? sv[t][i] : kMasked;
       });
     } else {
@@ -408,7 +411,7 @@ __device__ __forceinline__ void item_fwd(const FwdParams& p, int head, int r, in
     // group 1 together with the block's K tile; the mask then reads them
     // with four-key LDS loads instead of one global load per key.
     const bool seg_lds = has_seg && !p.mask_stored;
-    const u32x4 srs = uniform(make_rsrc(segk, (uint32_t)(has_seg ? L * 4 : 0)));
+    const u32x4 srs = uniform(make_rsrc(segk, (uint32_t)(has_seg ? Lk * 4 : 0)));
     auto segbuf = [&](int slot) { return lds + C::SEG_OFF + slot * (BN * 4); };
     auto seg_copy = [&](int c, int slot) __attribute__((always_inline)) {
       if (seg_lds && gw == 0) dma4(srs, (uint32_t)(uintptr_t)segbuf(slot), (c * BN + lane) * 4);

@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define SPLASH_VERSION 102
+#define SPLASH_VERSION 103
 
 /* Largest n_split of splash_attn_fwd_split. */
 #define SPLASH_MAX_SPLIT 64
@@ -183,12 +183,13 @@ typedef struct splash_fwd_args {
   int32_t Hq;            /* query heads, >= 0 */
   int32_t Hkv;           /* key/value heads, >= 1, divides Hq; query head h
                             reads kv head h / (Hq / Hkv) */
-  int32_t L;             /* sequence length (queries = keys), >= 0 */
+  int32_t L;             /* query rows (also key positions unless L_kv is
+                            set, see below), >= 0 */
   int32_t d_qk;          /* q/k head dim: f32 {64, 128}; bf16 {64, 128, 192} */
   int32_t d_v;           /* v head dim:   f32 {64, 128}; bf16 {64, 128} */
   const void* q;         /* device [B, Hq,  L, d_qk] contiguous, 16-B aligned */
-  const void* k;         /* device [B, Hkv, L, d_qk] contiguous, 16-B aligned */
-  const void* v;         /* device [B, Hkv, L, d_v]  contiguous, 16-B aligned */
+  const void* k;         /* device [B, Hkv, L_kv, d_qk] contiguous, 16-B aligned */
+  const void* v;         /* device [B, Hkv, L_kv, d_v]  contiguous, 16-B aligned */
   void* o;               /* device [B, Hq,  L, d_v]  output, same dtype as q,
                             16-B aligned; rows with no allowed key get 0 */
   float* lse;            /* device [B, Hq, L] float32 natural-log lse of the
@@ -201,9 +202,9 @@ typedef struct splash_fwd_args {
   int32_t window_left;
   int32_t window_right;
   const int32_t* seg_q;  /* device [B, L] or NULL */
-  const int32_t* seg_kv; /* device [B, L] or NULL (NULL: same as seg_q) */
+  const int32_t* seg_kv; /* device [B, L_kv] or NULL (NULL: same as seg_q) */
   /* Execution table (device copies of attn_mask_compile output for
-   * L_q = L_kv = L and this call's block sizes). */
+   * L_q = L, this call's L_kv and q_offset and its block sizes). */
   int32_t block_q;       /* must equal splash_fwd_tile's block_q */
   int32_t block_kv;      /* must equal splash_fwd_tile's block_kv */
   int32_t n_q_blocks;    /* ceil(L / block_q) */
@@ -232,15 +233,29 @@ typedef struct splash_fwd_args {
    * soft cap, max_logit = soft_cap can never overflow.  0 = running max. */
   int32_t use_max_logit;
   float max_logit;       /* finite when use_max_logit = 1 */
+  /* Decoding shapes.  L counts the query rows; the keys and values have
+   * L_kv positions, and query row i sits at key position q_offset + i in the
+   * causal and window tests (as in splash_mask_desc; decoding the last L of
+   * L_kv positions: q_offset = L_kv - L).  Then k and v are
+   * [B, Hkv, L_kv, d], seg_kv is [B, L_kv] (required with seg_q when
+   * L_kv != L), q, o, lse and seg_q keep L, and the tables come from
+   * attn_mask_compile with L_q = L, this L_kv and this q_offset.  A
+   * zero-initialised pair (L_kv = 0, q_offset = 0) means L_kv = L, so a
+   * query set with no keys at all is given by tables without active blocks.
+   * L_kv != L or q_offset != 0 is bf16 only. */
+  int32_t L_kv;          /* >= 0; 0: equal to L */
+  int32_t q_offset;      /* >= 0 */
 } splash_fwd_args;
 
 /* Enqueue the forward on `stream` (a hipStream_t; NULL = the default
  * stream) and return without waiting.  Validation errors are returned
  * synchronously: SPLASH_EINVAL (NULL args or buffers, misaligned pointer,
  * bad flag, scale <= 0 or not finite, soft_cap not finite, max_logit not
- * finite with use_max_logit = 1), SPLASH_ESHAPE
+ * finite with use_max_logit = 1, negative L_kv or q_offset, seg_q without
+ * seg_kv when L_kv != L), SPLASH_ESHAPE
  * (Hq % Hkv != 0, block sizes or n_q_blocks not matching, size overflow),
- * SPLASH_EDTYPE, SPLASH_EUNSUPPORTED (head dims), SPLASH_EHIP (the launch
+ * SPLASH_EDTYPE, SPLASH_EUNSUPPORTED (head dims; L_kv != L or q_offset != 0
+ * with f32), SPLASH_EHIP (the launch
  * failed).  B, Hq or L equal to 0 is a no-op.  Device-side faults surface at
  * the caller's next synchronisation. */
 int splash_attn_fwd(const splash_fwd_args* args, void* stream);

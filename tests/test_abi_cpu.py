@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
     assert set(declared) == set(_lib.EXPORTED), declared
     for name in declared:
         assert hasattr(lib, name), name
-    assert lib.splash_version() == 102
+    assert lib.splash_version() == 103
 
 
 def _assert_tables_equal(t, ref):
@@ -208,6 +208,13 @@ def _good_args(**over):
     (dict(use_max_logit=1, max_logit=math.nan), 1),
     (dict(use_max_logit=1, max_logit=math.inf), 1),
     (dict(Hq=1 << 20, L=1 << 20, n_q_blocks=4096), 2),   # items beyond int32
+    (dict(L_kv=-1), 1),
+    (dict(q_offset=-1), 1),
+    (dict(dtype=0, block_q=64, n_q_blocks=4, L_kv=300), 4),    # decode shapes: bf16 only
+    (dict(dtype=0, block_q=64, n_q_blocks=4, q_offset=8), 4),
+    (dict(L_kv=512, seg_q=0x10000), 1),                        # seg_kv needed
+    (dict(L_kv=1 << 24), 2),                                   # key bytes beyond int32
+    (dict(q_offset=(1 << 31) - 300), 2),                       # positions beyond int32
 ])
 def test_forward_validation_errors(over, code):
     lib = _lib.load()

@@ -224,6 +224,82 @@ def test_split_kv_every_element(case):
     _announce(f"  max-abs o {eo:.3g} lse {el:.3g}")
 
 
+DECODE_CASES = [
+    # (B, Hq, Hkv, L_q, L_kv, q_offset, d_qk, d_v, mask kwargs, soft_cap, mask_mode, n_split)
+    (2, 8, 2, 1, 3000, 2999, 128, 128, dict(causal=True), 0.0, "computed", 1),     # one new token
+    (2, 8, 2, 1, 3000, 2999, 128, 128, dict(causal=True), 0.0, "computed", 8),
+    (1, 4, 1, 16, 1000, 984, 128, 128, dict(causal=True, window_left=300, segs=(50, 400)), 0.0,
+     "computed", 1),
+    (1, 4, 1, 16, 1000, 984, 128, 128, dict(causal=True, window_left=300, segs=(50, 400)), 0.0,
+     "stored", 3),
+    (1, 2, 2, 300, 777, 477, 192, 128, dict(causal=True), 0.0, "computed", 1),    # chunked prefill
+    (1, 4, 4, 5, 4100, 4095, 64, 64, dict(causal=True, window_left=1000), 30.0, "computed", 4),
+    (1, 2, 1, 40, 500, 0, 128, 64, dict(window_right=100), 0.0, "computed", 1),
+    (1, 2, 2, 300, 100, 0, 64, 128, dict(), 0.0, "computed", 2),                  # L_kv < L_q
+    # rows past the last key; those beyond position 949 see no key at all
+    (1, 2, 2, 64, 700, 900, 128, 128, dict(causal=True, window_left=250), 0.0, "computed", 1),
+    (1, 2, 2, 64, 700, 900, 128, 128, dict(causal=True, window_left=250), 0.0, "computed", 5),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CASES,
+                         ids=lambda c: f"B{c[0]}H{c[1]}/{c[2]}-Lq{c[3]}-Lkv{c[4]}-off{c[5]}-d{c[6]}x{c[7]}"
+                         f"-{c[10]}-s{c[11]}" + ("-cap" if c[9] else "") + "-" + "-".join(sorted(c[8])))
+def test_decode_shapes_every_element(case):
+    """L_q != L_kv with query row i at key position q_offset + i (decoding
+    and chunked prefill), with and without split-KV, against the oracle."""
+    B, Hq, Hkv, Lq, Lkv, off, dqk, dv, mk, cap, mode, S = case
+    _announce(f"decode {case}")
+    seed = 9000 + Lq + Lkv + S
+    q, k, v = (stored(a, "bf16")
+               for a in draw_qkv(B, Hq, Hkv, Lq, dqk, dv, seed, qk_std=1.5 if cap else 1.0, L_kv=Lkv))
+    mk = dict(mk)
+    seg_q = seg_kv = None
+    if "segs" in mk:
+        lo, hi = mk.pop("segs")
+        seg_kv = segment_ids(Lkv, seed, lo, hi)
+        seg_q = seg_kv[off:off + Lq].copy()     # the new rows continue the cached documents
+    scale = 1.0 / math.sqrt(dqk)
+    o, lse = _run(q, k, v, scale=scale, soft_cap=cap, seg_q=seg_q, seg_kv=seg_kv, q_offset=off,
+                  mask_mode=mode, n_split=S, **mk)
+    o_ref, lse_ref = attention_ref(as_f64(q), as_f64(k), as_f64(v), scale=scale, soft_cap=cap,
+                                   seg_q=seg_q, seg_kv=seg_kv, q_offset=off, **mk)
+    eo, el = _compare(o, lse, o_ref, lse_ref, "bf16")
+    _announce(f"  max-abs o {eo:.3g} lse {el:.3g}")
+
+
+def test_decode_full_length_gqa_split():
+    """Decoding 16 new rows against a 32768-key cache: B=4, GQA 32/8, causal,
+    q_offset = L_kv - L_q, split into 16 chunks; every row against the
+    oracle, and the unsplit forward agrees."""
+    B, Hq, Hkv, Lq, Lkv, d = 4, 32, 8, 16, 32768, 128
+    _announce(f"decode full length B={B} Hq={Hq} Hkv={Hkv} L_q={Lq} L_kv={Lkv}")
+    q, k, v = (stored(a, "bf16") for a in draw_qkv(B, Hq, Hkv, Lq, d, d, 77, L_kv=Lkv))
+    off = Lkv - Lq
+    o, lse = _run(q, k, v, causal=True, q_offset=off, n_split=16)
+    heads = [(b, h) for b in range(B) for h in (0, 9, Hq - 1)]
+    o_ref, lse_ref = attention_ref(as_f64(q), as_f64(k), as_f64(v), scale=1.0 / math.sqrt(d),
+                                   causal=True, q_offset=off, heads=heads)
+    sel = (np.array([b for b, _ in heads]), np.array([h for _, h in heads]))
+    eo, el = _compare(o[sel], lse[sel], o_ref[sel], lse_ref[sel], "bf16")
+    o1, lse1 = _run(q, k, v, causal=True, q_offset=off)
+    assert float(np.max(np.abs(o1 - o))) <= 2e-2 and float(np.max(np.abs(lse1 - lse))) <= 1e-3
+    _announce(f"  max-abs o {eo:.3g} lse {el:.3g}")
+
+
+def test_decode_mismatched_tables_rejected():
+    """Tables compiled for another L_kv or q_offset are refused by the
+    binding before any launch."""
+    q, k, v = (stored(a, "bf16") for a in draw_qkv(1, 2, 2, 8, 128, 128, 5, L_kv=600))
+    bq, bkv = fwd_tile("bf16", 128, 128)
+    t = compile_mask(8, bq, bkv, L_kv=600, causal=True, q_offset=500)
+    with pytest.raises(ValueError):
+        splash_fwd(q.cuda(), k.cuda(), v.cuda(), causal=True, q_offset=592, tables=t)
+    o, _ = splash_fwd(q.cuda(), k.cuda(), v.cuda(), causal=True, q_offset=500, tables=t)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all()
+
+
 def test_ragged_full_length_persistent():
     """L = 32768 - 37 (a ragged last q block and kv block) with GQA 16/4 and
     a causal 4096-key window: 2048 items over the persistent rounds; sampled
