@@ -24,6 +24,7 @@ sys.path.insert(0, ROOT)
 
 DEFAULT_WORKLOAD = "causal_mha_bf16_L4096_d128"
 PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}   # dense MFMA bf16; fp32 vector
+PEAK_HBM_GBS = 8000.0                           # HBM3E
 KERNEL_SOURCES = {"bf16": "splash_fwd_bf16.hip", "f32": "splash_fwd_f32.hip"}
 
 
@@ -34,9 +35,9 @@ def unmasked_pairs(tabs, w, seg):
     segments being contiguous here)."""
     import numpy as np
     L = w.L
-    i = np.arange(L, dtype=np.int64)
+    i = w.q_offset + np.arange(L, dtype=np.int64)   # key positions of the query rows
     lo = np.zeros(L, np.int64)
-    hi = np.full(L, L - 1, np.int64)
+    hi = np.full(L, w.keys - 1, np.int64)
     if w.causal:
         hi = np.minimum(hi, i)
     if w.window_left >= 0:
@@ -94,14 +95,15 @@ def cpu_baseline(w, q, k, v, seg, budget_s):
         b, h = divmod(done, w.Hq)
         attention_ref(qf, kf, vf, scale=w.softmax_scale, soft_cap=w.soft_cap,
                       causal=w.causal, window_left=w.window_left,
-                      window_right=w.window_right, seg_q=seg, heads=[(b, h)])
+                      window_right=w.window_right, seg_q=seg, heads=[(b, h)],
+                      q_offset=w.q_offset)
         done += 1
     dt = time.perf_counter() - t0
     flop = 2.0 * (w.d_qk + w.d_v) * pairs * done
     return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"{done} of {w.B * w.Hq} (batch, head) pairs in order, all {w.L} "
-                      f"rows each, float64 numpy, {dt:.1f} s"}
+                      f"rows each (against {w.keys} keys), float64 numpy, {dt:.1f} s"}
 
 
 def main():
@@ -114,8 +116,9 @@ def main():
     ap.add_argument("--max-logit", type=float, default=None,
                     help="Max Logit Estimate constant (logit units) in place of the running "
                          "row max; the default is the running max")
-    ap.add_argument("--n-split", type=int, default=1,
-                    help="split-KV: chunks per row merged through their lse (bf16; 1 = plain forward)")
+    ap.add_argument("--n-split", type=int, default=None,
+                    help="split-KV: chunks per row merged through their lse (bf16; 1 = plain "
+                         "forward); default: the workload's own (1 except for decoding)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run one device-to-device copy of this many MiB "
                          "(a plain copy of known size, for scaling HBM counters)")
@@ -133,6 +136,8 @@ def main():
     from block_sparse_flash_amd.inputs import ALL_WORKLOADS, make_inputs
 
     w = ALL_WORKLOADS[args.workload]
+    if args.n_split is None:
+        args.n_split = w.n_split
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     q, k, v, seg = make_inputs(w)
@@ -140,12 +145,13 @@ def main():
     bq, bkv = fwd_tile(w.dtype, w.d_qk, w.d_v)
     mask_kw = dict(causal=w.causal, window_left=w.window_left, window_right=w.window_right)
     t0 = time.perf_counter()
-    tabs = compile_mask(w.L, bq, bkv, seg_q=seg, **mask_kw)
+    tabs = compile_mask(w.L, bq, bkv, L_kv=w.keys, seg_q=seg, q_offset=w.q_offset, **mask_kw)
     mask_ms = (time.perf_counter() - t0) * 1e3
     out = torch.empty((w.B, w.Hq, w.L, w.d_v), dtype=qd.dtype, device=dev)
     lse = torch.empty((w.B, w.Hq, w.L), dtype=torch.float32, device=dev)
     kw = dict(scale=w.softmax_scale, soft_cap=w.soft_cap, seg_q=seg, tables=tabs,
-              mask_mode=args.mask_mode, out=out, lse=lse, max_logit=args.max_logit, **mask_kw)
+              mask_mode=args.mask_mode, out=out, lse=lse, max_logit=args.max_logit,
+              q_offset=w.q_offset, **mask_kw)
     if args.n_split != 1:
         from block_sparse_flash_amd import split_workspace_bytes
         ws = torch.empty(split_workspace_bytes(args.n_split, w.B, w.Hq, w.L, w.d_v),
@@ -174,6 +180,22 @@ def main():
     tflops = flop_per_step / (ms_per_step * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
     traffic = committed_traffic(w.name, w.dtype)
+    decode = w.keys != w.L or w.q_offset != 0
+    if decode:
+        # Decoding: a few query rows against a long K/V cache; the forward
+        # streams K and V once per K/V head and is bound by HBM.  Algorithmic
+        # bytes: K and V of every K/V head, q and o of every query head, lse.
+        elt = 2 if w.dtype == "bf16" else 4
+        algo_bytes = (elt * (w.B * w.Hkv * w.keys * (w.d_qk + w.d_v) + w.B * w.Hq * w.L * (w.d_qk + w.d_v))
+                      + 4 * w.B * w.Hq * w.L)
+        gbs = algo_bytes / (ms_per_step * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
+                    "algorithmic_bytes": algo_bytes}
+    else:
+        roofline = {"bound": "mfma" if w.dtype == "bf16" else "alu",
+                    "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                    "frac": round(tflops / peak, 4), "traffic": traffic}
 
     cpu = None
     if args.cpu_budget > 0:
@@ -198,6 +220,7 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic (seeded N(0,1) inputs)",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "L": w.L,
+                   "L_kv": w.keys, "q_offset": w.q_offset,
                    "d_qk": w.d_qk, "d_v": w.d_v, "mask": mask, "soft_cap": w.soft_cap,
                    "scale": w.softmax_scale, "block_q": bq, "block_kv": bkv,
                    "mask_mode": args.mask_mode, "max_logit": args.max_logit,
@@ -208,9 +231,7 @@ def main():
         "active_blocks": tabs.n_active, "partial_blocks": tabs.n_partial,
         "mask_compile_ms": round(mask_ms, 3),
         "wall_s_timed_region": round(wall, 4),
-        "roofline": {"bound": "mfma" if w.dtype == "bf16" else "alu",
-                     "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(tflops / peak, 4), "traffic": traffic},
+        "roofline": roofline,
         "cpu_baseline": cpu,
     }
     if args.copy_calibration_mib > 0:

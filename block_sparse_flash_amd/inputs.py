@@ -39,10 +39,17 @@ class Workload:
     qk_std: float = 1.0     # q and k ~ N(0, qk_std^2); v ~ N(0, 1)
     seed: int = 0
     scale: Optional[float] = None   # None: 1/sqrt(d_qk)
+    L_kv: Optional[int] = None      # key positions; None: L
+    q_offset: int = 0               # query row i sits at key position q_offset + i
+    n_split: int = 1                # split-KV chunks the bench uses by default
 
     @property
     def softmax_scale(self) -> float:
         return self.scale if self.scale is not None else 1.0 / math.sqrt(self.d_qk)
+
+    @property
+    def keys(self) -> int:
+        return self.L if self.L_kv is None else self.L_kv
 
     def asdict(self):
         d = asdict(self)
@@ -82,6 +89,12 @@ EXTRA_WORKLOADS = {
     "causal_bf16_L32768_H2": Workload(
         "causal_bf16_L32768_H2", "bf16", 1, 2, 2, 32768, 128, 128,
         causal=True, seed=6),
+    # Decoding 16 new rows per sequence (speculative or multi-token decode)
+    # against a 32768-position K/V cache: GQA 32/8, causal, the new rows at
+    # the last 16 positions; split-KV into 16 chunks per row.
+    "decode_gqa_bf16_Lq16_Lkv32768": Workload(
+        "decode_gqa_bf16_Lq16_Lkv32768", "bf16", 8, 32, 8, 16, 128, 128,
+        causal=True, seed=7, L_kv=32768, q_offset=32768 - 16, n_split=16),
 }
 ALL_WORKLOADS = {**WORKLOADS, **EXTRA_WORKLOADS}
 
@@ -134,6 +147,8 @@ def as_f64(t) -> np.ndarray:
 def make_inputs(w: Workload):
     """(q, k, v, seg) for a workload: q/k/v stored torch CPU tensors, seg an
     int32 numpy array [L] or None."""
-    q, k, v = draw_qkv(w.B, w.Hq, w.Hkv, w.L, w.d_qk, w.d_v, w.seed, w.qk_std)
+    q, k, v = draw_qkv(w.B, w.Hq, w.Hkv, w.L, w.d_qk, w.d_v, w.seed, w.qk_std, L_kv=w.keys)
+    if w.segments and (w.keys != w.L or w.q_offset):
+        raise ValueError("segment ids are drawn for L_q = L_kv workloads only")
     seg = segment_ids(w.L, w.seed, w.seg_min, w.seg_max) if w.segments else None
     return stored(q, w.dtype), stored(k, w.dtype), stored(v, w.dtype), seg

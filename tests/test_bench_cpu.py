@@ -1,0 +1,54 @@
+"""CPU checks of bench.py's bookkeeping: the unmasked pair count behind the
+TFLOP/s figure equals the number of pairs the oracle's mask definition
+allows, for the named workloads (decoding included)."""
+
+import importlib.util
+import os
+
+import numpy as np
+import pytest
+
+from block_sparse_flash_amd.inputs import ALL_WORKLOADS, segment_ids
+from oracle import allowed
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _bench():
+    spec = importlib.util.spec_from_file_location("bench", os.path.join(ROOT, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def _allowed_count(w, seg):
+    j = np.arange(w.keys)[None, :]
+    total = 0
+    for r0 in range(0, w.L, 2048):
+        i = np.arange(r0, min(r0 + 2048, w.L))[:, None]
+        a = allowed(i, j, L_q=w.L, L_kv=w.keys, causal=w.causal, window_left=w.window_left,
+                    window_right=w.window_right, seg_q=seg, q_offset=w.q_offset)
+        total += int(np.count_nonzero(a))
+    return total
+
+
+@pytest.mark.parametrize("name", [n for n, w in ALL_WORKLOADS.items() if w.L * w.keys <= 1 << 26])
+def test_pair_count_matches_mask_definition(name):
+    w = ALL_WORKLOADS[name]
+    seg = segment_ids(w.L, w.seed, w.seg_min, w.seg_max) if w.segments else None
+    assert _bench().unmasked_pairs(None, w, seg) == _allowed_count(w, seg)
+
+
+def test_pair_count_decode_closed_form():
+    """16 causal rows at the last 16 of 32768 positions: row i sees
+    32768 - 16 + i + 1 keys."""
+    w = ALL_WORKLOADS["decode_gqa_bf16_Lq16_Lkv32768"]
+    assert _bench().unmasked_pairs(None, w, None) == sum(32768 - 16 + i + 1 for i in range(16))
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr

@@ -378,7 +378,8 @@ def _sample_rows(L, bq, rng, n_random=24):
     return np.array(sorted(rows))
 
 
-FULL_SIZE = [(name, 1) for name in WORKLOADS] + [(name, 4) for name in EXTRA_WORKLOADS]
+FULL_SIZE = [(name, 1) for name in WORKLOADS] + \
+    [(name, w.n_split if w.n_split > 1 else 4) for name, w in EXTRA_WORKLOADS.items()]
 
 
 @pytest.mark.parametrize("name,n_split", FULL_SIZE, ids=lambda x: str(x))
@@ -387,12 +388,13 @@ def test_full_size_workloads_sampled(name, n_split):
     _announce(f"full-size {name} n_split={n_split}")
     q, k, v, seg = make_inputs(w)
     bq, bkv = fwd_tile(w.dtype, w.d_qk, w.d_v)
-    tabs = compile_mask(w.L, bq, bkv, causal=w.causal, window_left=w.window_left,
-                        window_right=w.window_right, seg_q=seg)
+    tabs = compile_mask(w.L, bq, bkv, L_kv=w.keys, causal=w.causal, window_left=w.window_left,
+                        window_right=w.window_right, seg_q=seg, q_offset=w.q_offset)
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
     o, lse = splash_fwd(qd, kd, vd, scale=w.softmax_scale, soft_cap=w.soft_cap,
                         causal=w.causal, window_left=w.window_left,
-                        window_right=w.window_right, seg_q=seg, tables=tabs, n_split=n_split)
+                        window_right=w.window_right, seg_q=seg, tables=tabs, n_split=n_split,
+                        q_offset=w.q_offset)
     torch.cuda.synchronize()
     rng = np.random.default_rng(w.seed + 7)
     n_heads = w.B * w.Hq
@@ -403,7 +405,7 @@ def test_full_size_workloads_sampled(name, n_split):
     o_ref, lse_ref = attention_ref(qf, kf, vf, scale=w.softmax_scale, soft_cap=w.soft_cap,
                                    causal=w.causal, window_left=w.window_left,
                                    window_right=w.window_right, seg_q=seg, rows=rows,
-                                   heads=heads)
+                                   heads=heads, q_offset=w.q_offset)
     o_np = o.float().cpu().numpy()
     lse_np = lse.cpu().numpy()
     worst = (0.0, 0.0)
