@@ -16,7 +16,8 @@ Sources (pages cited by title and section):
   pattern element), exercises 7, 11, 12 and their answers.
 * "拆解大模型几项核心操作背后的数学与 Infra 优化逻辑" (joto.ai blog), sections
   "Causal Mask", "Online Softmax" and "LSE 与 Online Softmax" (lse = m + log l,
-  and the split-K merge of per-range outputs through their lse).
+  the split-K merge of per-range outputs through their lse, and the backward
+  rebuilding p = exp(s - lse) from the stored lse).
 
 Parity pins: every function here is pinned by tests under ``tests/`` against
 worked examples printed on the pages (``tests/golden/``), closed forms,
@@ -34,7 +35,8 @@ from .attention import (
     merge_lse,
     mle_safe_range,
 )
-from .mask_tables import mask_tables_ref
+from .backward import attention_bwd_ref
+from .mask_tables import column_tables_ref, mask_tables_ref
 
 __all__ = [
     "allowed",
@@ -45,4 +47,6 @@ __all__ = [
     "merge_lse",
     "mle_safe_range",
     "mask_tables_ref",
+    "column_tables_ref",
+    "attention_bwd_ref",
 ]

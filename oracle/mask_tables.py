@@ -113,3 +113,34 @@ def mask_tables_ref(L_q: int, L_kv: int, block_q: int, block_kv: int, *,
         "row_order": row_order,
         "partial_mask_blocks": pmb,
     }
+
+
+def column_tables_ref(block_mask: np.ndarray):
+    """Column-major view of the active blocks, for work items that own one
+    kv-block column (the gradients of K and V sum over the q-block rows that
+    read a kv block).  From the block classes by definition:
+
+    * ``col_ptr`` int32 [nkv + 1]: CSR offsets per kv-block column;
+    * ``col_rows`` int32 [n_active]: for each column c in ascending order, the
+      rows r with ``block_mask[r, c] != 0``, ascending;
+    * ``col_entry`` int32 [n_active]: the index of block (r, c) in the
+      row-major active order of ``mask_tables_ref`` (so its ``block_code``
+      and ``mask_next`` can be looked up).
+    """
+    bm = np.asarray(block_mask)
+    nq, nkv = bm.shape
+    index = {}
+    for r in range(nq):
+        for c in range(nkv):
+            if bm[r, c] != 0:
+                index[(r, c)] = len(index)
+    col_ptr, col_rows, col_entry = [0], [], []
+    for c in range(nkv):
+        for r in range(nq):
+            if bm[r, c] != 0:
+                col_rows.append(r)
+                col_entry.append(index[(r, c)])
+        col_ptr.append(len(col_rows))
+    return {"col_ptr": np.asarray(col_ptr, dtype=np.int32),
+            "col_rows": np.asarray(col_rows, dtype=np.int32),
+            "col_entry": np.asarray(col_entry, dtype=np.int32)}
