@@ -28,7 +28,7 @@ SPLASH_MASK_STORED = 1
 # Every symbol include/splash.h declares.
 EXPORTED = ("splash_version", "splash_last_error", "attn_mask_compile",
             "splash_fwd_tile", "splash_attn_fwd", "splash_split_workspace_bytes",
-            "splash_attn_fwd_split")
+            "splash_attn_fwd_split", "attn_mask_columns", "splash_attn_bwd")
 SPLASH_MAX_SPLIT = 64
 
 c_i32 = ctypes.c_int32
@@ -70,6 +70,22 @@ class FwdArgs(ctypes.Structure):
                 ("soft_cap", ctypes.c_float),
                 ("use_max_logit", c_i32), ("max_logit", ctypes.c_float),
                 ("L_kv", c_i32), ("q_offset", c_i32)]
+
+
+class BwdArgs(ctypes.Structure):
+    _fields_ = [("dtype", c_i32), ("B", c_i32), ("Hq", c_i32), ("Hkv", c_i32),
+                ("L", c_i32), ("L_kv", c_i32), ("q_offset", c_i32),
+                ("d_qk", c_i32), ("d_v", c_i32),
+                ("q", c_ptr), ("k", c_ptr), ("v", c_ptr), ("o", c_ptr), ("lse", c_ptr),
+                ("dout", c_ptr), ("dq", c_ptr), ("dk", c_ptr), ("dv", c_ptr),
+                ("delta", c_ptr),
+                ("causal", c_i32), ("window_left", c_i32), ("window_right", c_i32),
+                ("seg_q", c_ptr), ("seg_kv", c_ptr),
+                ("block_q", c_i32), ("block_kv", c_i32), ("n_q_blocks", c_i32),
+                ("n_kv_blocks", c_i32), ("n_active", c_i32),
+                ("row_ptr", c_ptr), ("active_cols", c_ptr), ("col_ptr", c_ptr),
+                ("col_rows", c_ptr),
+                ("scale", ctypes.c_float), ("soft_cap", ctypes.c_float)]
 
 
 class SplashError(RuntimeError):
@@ -114,6 +130,10 @@ def load():
         lib.splash_attn_fwd_split.restype = ctypes.c_int
         lib.splash_attn_fwd_split.argtypes = [ctypes.POINTER(FwdArgs), c_i32, c_ptr,
                                               ctypes.c_int64, c_ptr]
+        lib.attn_mask_columns.restype = ctypes.c_int
+        lib.attn_mask_columns.argtypes = [c_i32, c_i32, c_i32, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr]
+        lib.splash_attn_bwd.restype = ctypes.c_int
+        lib.splash_attn_bwd.argtypes = [ctypes.POINTER(BwdArgs), c_ptr]
         _lib = lib
         return lib
 

@@ -56,6 +56,37 @@ class MaskTables:
     partial_mask_blocks: np.ndarray
     q_offset: int = 0
     _device: dict = field(default_factory=dict, repr=False)
+    _columns: Optional[dict] = field(default=None, repr=False)
+
+    def columns(self):
+        """Column-major view of the active list (``attn_mask_columns``):
+        host arrays ``col_ptr`` [n_kv_blocks + 1], ``col_rows`` and
+        ``col_entry`` [n_active]."""
+        if self._columns is None:
+            lib = _lib.load()
+            cols = {"col_ptr": np.zeros(self.n_kv_blocks + 1, np.int32),
+                    "col_rows": np.zeros(self.n_active, np.int32),
+                    "col_entry": np.zeros(self.n_active, np.int32)}
+            row_ptr = np.ascontiguousarray(self.row_ptr, dtype=np.int32)
+            active_cols = np.ascontiguousarray(self.active_cols, dtype=np.int32)
+            _lib.check(lib.attn_mask_columns(self.n_q_blocks, self.n_kv_blocks, self.n_active,
+                                             _ptr(row_ptr), _ptr(active_cols),
+                                             _ptr(cols["col_ptr"]), _ptr(cols["col_rows"]),
+                                             _ptr(cols["col_entry"])))
+            self._columns = cols
+        return self._columns
+
+    def device_columns(self, device):
+        """Device copies (torch tensors) of ``col_ptr`` and ``col_rows``."""
+        import torch
+        key = "cols:" + str(torch.device(device))
+        if key not in self._device:
+            cols = self.columns()
+            def up(a):
+                t = torch.from_numpy(np.ascontiguousarray(a)).to(torch.int32)
+                return (t if t.numel() else torch.zeros(1, dtype=torch.int32)).to(device)
+            self._device[key] = {"col_ptr": up(cols["col_ptr"]), "col_rows": up(cols["col_rows"])}
+        return self._device[key]
 
     def device(self, device):
         """Device copies (torch tensors) of the arrays the forward reads."""
@@ -265,3 +296,91 @@ def split_workspace_bytes(n_split: int, B: int, Hq: int, L: int, d_v: int) -> in
     _lib.check(lib.splash_split_workspace_bytes(int(n_split), int(B), int(Hq), int(L), int(d_v),
                                                 ctypes.byref(nb)))
     return nb.value
+
+
+def _segment_rows(seg, B, n, device, name):
+    """Segment ids [n] or [B, n] as a device int32 tensor [B, n] (None stays None)."""
+    import torch
+    if seg is None:
+        return None
+    t = torch.as_tensor(np.asarray(seg.cpu() if hasattr(seg, "cpu") else seg), dtype=torch.int32)
+    t = t.reshape(-1, n)
+    if t.shape[0] == 1:
+        t = t.expand(B, n)
+    if t.shape[0] != B:
+        raise ValueError(f"{name} must be [{n}] or [B, {n}]")
+    return t.contiguous().to(device)
+
+
+def splash_bwd(q, k, v, o, lse, dout, *, scale: Optional[float] = None, soft_cap: float = 0.0,
+               causal: bool = False, window_left: int = -1, window_right: int = -1,
+               seg_q=None, seg_kv=None, q_offset: int = 0, tables: Optional[MaskTables] = None,
+               stream=None):
+    """Block-sparse attention backward on the GPU (``splash_attn_bwd``).
+
+    q, k, v, ``o`` (the forward's output) and ``dout`` (the upstream
+    gradient, shaped like o) are contiguous bfloat16 GPU tensors with the
+    forward's shapes; ``lse`` is the forward's float32 lse [B, Hq, L]; the
+    mask arguments are those of the forward.  Returns (dq, dk, dv) as float32
+    tensors shaped like q, k and v.  Head dims (64, 64) or (128, 128).
+    """
+    import torch
+    lib = _lib.load()
+    for t in (q, k, v, o, dout):
+        if not t.is_cuda or t.dtype != torch.bfloat16:
+            raise TypeError("q, k, v, o and dout must be bfloat16 GPU tensors")
+    if not lse.is_cuda or lse.dtype != torch.float32:
+        raise TypeError("lse must be a float32 GPU tensor")
+    B, Hq, L, d_qk = q.shape
+    Hkv, L_kv = k.shape[1], k.shape[2]
+    d_v = v.shape[3]
+    if (tuple(k.shape) != (B, Hkv, L_kv, d_qk) or tuple(v.shape[:3]) != (B, Hkv, L_kv)
+            or tuple(o.shape) != (B, Hq, L, d_v) or tuple(dout.shape) != (B, Hq, L, d_v)
+            or tuple(lse.shape) != (B, Hq, L)):
+        raise ValueError("shape mismatch among q, k, v, o, lse, dout")
+    q, k, v, o, dout, lse = (t.contiguous() for t in (q, k, v, o, dout, lse))
+    if scale is None:
+        scale = 1.0 / float(d_qk) ** 0.5
+    bq, bkv = fwd_tile("bf16", d_qk, d_v)
+    if seg_q is None and seg_kv is not None:
+        raise ValueError("seg_kv given without seg_q")
+    if seg_q is not None and seg_kv is None and L_kv != L:
+        raise ValueError("seg_kv is required when L_kv != L")
+    sq = _segment_rows(seg_q, B, L, q.device, "seg_q")
+    skv = _segment_rows(seg_kv, B, L_kv, q.device, "seg_kv")
+    per_batch = B > 1 and sq is not None and (
+        not bool((sq == sq[:1]).all()) or (skv is not None and not bool((skv == skv[:1]).all())))
+    dq = torch.empty((B, Hq, L, d_qk), dtype=torch.float32, device=q.device)
+    dk = torch.empty((B, Hkv, L_kv, d_qk), dtype=torch.float32, device=q.device)
+    dv = torch.empty((B, Hkv, L_kv, d_v), dtype=torch.float32, device=q.device)
+    delta = torch.empty((B, Hq, max(L, 1)), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    for bsel in (range(B) if per_batch else [None]):
+        if tables is None or per_batch:
+            b0 = bsel or 0
+            tabs = compile_mask(L, bq, bkv, L_kv=L_kv, causal=causal, window_left=window_left,
+                                window_right=window_right, q_offset=q_offset,
+                                seg_q=None if sq is None else sq[b0].cpu().numpy(),
+                                seg_kv=None if skv is None else skv[b0].cpu().numpy())
+        else:
+            tabs = tables
+        got = (tabs.block_q, tabs.block_kv, tabs.L_q, tabs.L_kv, tabs.q_offset)
+        if got != (bq, bkv, L, L_kv, q_offset):
+            raise ValueError(f"tables were compiled for (block_q, block_kv, L_q, L_kv, q_offset)="
+                             f"{got}; need {(bq, bkv, L, L_kv, q_offset)}")
+        dev = tabs.device(q.device)
+        cdev = tabs.device_columns(q.device)
+        sl = slice(None) if bsel is None else slice(bsel, bsel + 1)
+        nb = B if bsel is None else 1
+        ptr = lambda t: None if t is None else t[sl].data_ptr()
+        args = _lib.BwdArgs(
+            _DTYPES["bf16"], nb, Hq, Hkv, L, L_kv, int(q_offset), d_qk, d_v,
+            ptr(q), ptr(k), ptr(v), ptr(o), ptr(lse), ptr(dout), ptr(dq), ptr(dk), ptr(dv),
+            ptr(delta), int(bool(causal)), window_left, window_right, ptr(sq), ptr(skv),
+            bq, bkv, tabs.n_q_blocks, tabs.n_kv_blocks, tabs.n_active,
+            dev["row_ptr"].data_ptr(), dev["active_cols"].data_ptr(),
+            cdev["col_ptr"].data_ptr(), cdev["col_rows"].data_ptr(),
+            float(scale), float(soft_cap))
+        _lib.check(lib.splash_attn_bwd(ctypes.byref(args), ctypes.c_void_p(stream)))
+    return dq, dk, dv

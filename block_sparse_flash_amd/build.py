@@ -27,6 +27,8 @@ SOURCES = [
     "splash_fwd_f32.hip",
     "splash_fwd_bf16.hip",
     "splash_split_merge.hip",
+    "splash_bwd_api.cpp",
+    "splash_bwd_bf16.hip",
 ]
 
 ARCH = "gfx950"

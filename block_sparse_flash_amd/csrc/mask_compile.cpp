@@ -287,3 +287,40 @@ extern "C" int attn_mask_compile(const splash_mask_desc* desc, splash_mask_sizes
     return splash::fail(SPLASH_EINTERNAL, "attn_mask_compile: unexpected exception");
   }
 }
+
+// Column-major view of an execution table: a counting sort of the row-major
+// active list by kv-block column (rows stay ascending inside a column).
+extern "C" int attn_mask_columns(int32_t n_q_blocks, int32_t n_kv_blocks, int32_t n_active,
+                                 const int32_t* row_ptr, const int32_t* active_cols,
+                                 int32_t* col_ptr, int32_t* col_rows, int32_t* col_entry) {
+  splash::clear_error();
+  if (n_q_blocks < 0 || n_kv_blocks < 0 || n_active < 0)
+    return splash::fail(SPLASH_EINVAL, "attn_mask_columns: negative size");
+  if (!row_ptr || !col_ptr || (n_active > 0 && (!active_cols || !col_rows || !col_entry)))
+    return splash::fail(SPLASH_EINVAL, "attn_mask_columns: NULL array");
+  if (row_ptr[0] != 0 || row_ptr[n_q_blocks] != n_active)
+    return splash::fail(SPLASH_EINVAL, "attn_mask_columns: row_ptr must run from 0 to n_active");
+  for (int32_t r = 0; r < n_q_blocks; ++r) {
+    if (row_ptr[r + 1] < row_ptr[r])
+      return splash::fail(SPLASH_EINVAL, "attn_mask_columns: row_ptr decreases at row %d", r);
+    for (int32_t e = row_ptr[r]; e < row_ptr[r + 1]; ++e) {
+      const int32_t c = active_cols[e];
+      if (c < 0 || c >= n_kv_blocks || (e > row_ptr[r] && c <= active_cols[e - 1]))
+        return splash::fail(SPLASH_EINVAL,
+                            "attn_mask_columns: columns of row %d must ascend within [0, %d)", r,
+                            n_kv_blocks);
+    }
+  }
+  for (int32_t c = 0; c <= n_kv_blocks; ++c) col_ptr[c] = 0;
+  for (int32_t e = 0; e < n_active; ++e) ++col_ptr[active_cols[e] + 1];
+  for (int32_t c = 0; c < n_kv_blocks; ++c) col_ptr[c + 1] += col_ptr[c];
+  std::vector<int32_t> fill(col_ptr, col_ptr + n_kv_blocks);
+  for (int32_t r = 0; r < n_q_blocks; ++r) {
+    for (int32_t e = row_ptr[r]; e < row_ptr[r + 1]; ++e) {
+      const int32_t x = fill[active_cols[e]]++;
+      col_rows[x] = r;
+      col_entry[x] = e;
+    }
+  }
+  return SPLASH_OK;
+}

@@ -1,0 +1,498 @@
+// bf16 block-sparse attention backward for gfx950 on MFMA.
+//
+// Method: the forward keeps only o and the per-row logsumexp residual
+// ("Lecture 13 - Pallas Kernels and Splash Attention", section 6.3); the
+// backward rebuilds the probabilities on chip as p = e^(logit - lse) (joto.ai
+// page on core LLM operators, "LSE and online softmax": read q and k,
+// recompute the dot product, subtract the stored lse scalar, exponentiate).
+// With y = scale q.k, logit z = cap tanh(y / cap) (z = y without a cap),
+// D_i = do_i . o_i and dp_ij = do_i . v_j, the chain rule through the softmax
+// gives dy_ij = p_ij (dp_ij - D_i) dz/dy, and
+//   dv_j = sum_i p_ij do_i,  dk_j = scale sum_i dy_ij q_i,  dq_i = scale sum_j dy_ij k_j.
+// Only the active blocks of the execution table are visited; the element
+// mask (causal, window, segment ids, padding) is evaluated from positions on
+// every visited block.
+//
+// gfx950 design:
+//   * delta kernel: one wave per query row computes D_i from o and do.
+//   * dk/dv kernel: one work-group (4 waves) per (K/V head, 64-key block)
+//     walks the block's column of the table (the q blocks that read it) for
+//     every query head of the GQA group, in 64-row sub-tiles, so dk and dv
+//     are summed in registers with no atomics.  Wave w owns keys
+//     32 (w % 2) .. + 31 and rows 32 (w / 2) .. + 31 of each sub-tile.
+//     S = Q K^T and dP = dO V^T come out of v_mfma_f32_32x32x16_bf16 with one
+//     key per lane and 16 rows per lane; those accumulator items, rounded to
+//     bf16, are directly the A operand of dV += P^T dO and dK += dS^T Q (the
+//     MFMA's reduction index runs over the rows in the order the accumulator
+//     holds them), and the B operands come from transposed copies of Q and
+//     dO in LDS.  The two row halves are summed through LDS at the end.
+//   * dq kernel: one work-group (8 waves, 32 rows each) per (query head,
+//     256-row q block) walks the row's active kv blocks; S^T = K Q^T and
+//     dP^T = V dO^T hold one row per lane, and dS^T feeds dQ += dS K the same
+//     way, with K transposed in LDS.
+//   * LDS tiles are padded (row-major rows by 16 bytes, transposed rows to
+//     68 elements) so that the 32 lanes of an operand read fall in distinct
+//     banks.
+//   * Gradients are accumulated and written in float32.
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "bwd_params.h"
+#include "fwd_params.h"
+
+namespace splash {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) float lds_f32;
+typedef __attribute__((address_space(3))) int32_t lds_i32;
+
+constexpr int BQ = kBf16BlockQ;   // rows per q block of the tables
+constexpr int BK = kBf16BlockKV;  // keys per kv block of the tables
+constexpr int SUB = 64;           // rows per sub-tile in the dk/dv kernel
+constexpr int TP = 68;            // row stride (elements) of transposed tiles
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Row stride (elements) of a row-major tile with D columns.
+template <int D>
+constexpr int rs() { return D + 8; }
+
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
+
+__device__ __forceinline__ bf16x8 ld_op(const lds_u16* ptr) { return *reinterpret_cast<const lds_bf16x8*>(ptr); }
+
+// Two 4-element runs (8 bytes each) of a transposed tile as one operand.
+__device__ __forceinline__ bf16x8 ld_op2(const lds_u16* lo, const lds_u16* hi) {
+  const u32x2 a = *reinterpret_cast<const lds_u32x2*>(lo);
+  const u32x2 b = *reinterpret_cast<const lds_u32x2*>(hi);
+  const u32x4 v = {a[0], a[1], b[0], b[1]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Whether query row qi may attend key `key` by position (segments apart).
+__device__ __forceinline__ bool pair_ok(const BwdParams& p, int qi, int key) {
+  const int pos = p.q_off + qi;
+  bool ok = (qi < p.L) & (key < p.Lkv);
+  if (p.causal) ok = ok & (key <= pos);
+  if (p.window_left >= 0) ok = ok & (pos - key <= p.window_left);
+  if (p.window_right >= 0) ok = ok & (key - pos <= p.window_right);
+  return ok;
+}
+
+// Copies rows row0 .. row0 + 63 of a row-major [n_valid, D] bf16 matrix
+// into LDS (zeros past n_valid): row-major with stride rs<D>() into `rm`
+// and/or transposed ([D][TP]) into `tr`.
+template <int D, int NTHR, bool RM, bool TR>
+__device__ __forceinline__ void load_tile(const uint16_t* g, int row0, int n_valid, lds_u16* rm,
+                                          lds_u16* tr, int tid) {
+  constexpr int CH = D / 8;
+  constexpr int TOTAL = 64 * CH;
+  static_assert(TOTAL % NTHR == 0, "whole chunks per thread");
+#pragma unroll
+  for (int it = 0; it < TOTAL / NTHR; ++it) {
+    const int x = it * NTHR + tid;
+    const int r = x / CH;
+    const int c = x - r * CH;
+    u32x4 val = {0u, 0u, 0u, 0u};
+    if (row0 + r < n_valid) val = *reinterpret_cast<const u32x4*>(g + (int64_t)(row0 + r) * D + c * 8);
+    if constexpr (RM) *reinterpret_cast<lds_u32x4*>(rm + r * rs<D>() + c * 8) = val;
+    if constexpr (TR) {
+      const u16x8 e = __builtin_bit_cast(u16x8, val);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) tr[(c * 8 + i) * TP + r] = e[i];
+    }
+  }
+}
+
+// Probability and score gradient of one (row, key) pair from its raw dot
+// product s, the row's lse (log2 units), its D and dP.
+template <bool CAP>
+__device__ __forceinline__ void p_and_ds(const BwdParams& p, bool ok, float s, float lse2, float dpv,
+                                         float dlt, float* pe, float* ds) {
+  float z2, fac = 1.0f;
+  if constexpr (CAP) {
+    // t = tanh(y / cap) = 1 - 2 / (e^{2y/cap} + 1), y = scale s.
+    const float u = 1.0f / (__builtin_amdgcn_exp2f(2.0f * kLog2e * p.scale / p.soft_cap * s) + 1.0f);
+    const float t = 1.0f - 2.0f * u;
+    z2 = p.soft_cap * kLog2e * t;
+    fac = 1.0f - t * t;
+  } else {
+    z2 = p.scale_log2 * s;
+  }
+  const float e = ok ? __builtin_amdgcn_exp2f(z2 - lse2) : 0.0f;
+  *pe = e;
+  *ds = e * (dpv - dlt) * fac;
+}
+
+template <int DV>
+__global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
+  const int lane = threadIdx.x & 63;
+  const int64_t n_rows = (int64_t)p.B * p.Hq * p.L;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= n_rows) return;
+  const uint16_t* o = static_cast<const uint16_t*>(p.o) + row * DV;
+  const uint16_t* d = static_cast<const uint16_t*>(p.dout) + row * DV;
+  float acc = 0.0f;
+#pragma unroll
+  for (int e = lane; e < DV; e += 64) acc += bf16_to_f32(o[e]) * bf16_to_f32(d[e]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  if (lane == 0) p.delta[row] = acc;
+}
+
+template <int DQK, int DV>
+struct DkdvLds {
+  static constexpr int RK = rs<DQK>();
+  static constexpr int RV = rs<DV>();
+  static constexpr int K_OFF = 0;                          // K [64][RK]
+  static constexpr int V_OFF = K_OFF + 64 * RK * 2;        // V [64][RV]
+  static constexpr int Q_OFF = V_OFF + 64 * RV * 2;        // Q [64][RK]
+  static constexpr int QT_OFF = Q_OFF + 64 * RK * 2;       // Q^T [DQK][TP]
+  static constexpr int O_OFF = QT_OFF + DQK * TP * 2;      // dO [64][RV]
+  static constexpr int OT_OFF = O_OFF + 64 * RV * 2;       // dO^T [DV][TP]
+  static constexpr int LSE_OFF = OT_OFF + DV * TP * 2;     // lse * log2(e) [64]
+  static constexpr int D_OFF = LSE_OFF + 64 * 4;           // D [64]
+  static constexpr int SEG_OFF = D_OFF + 64 * 4;           // row segment ids [64]
+  static constexpr int BYTES = SEG_OFF + 64 * 4;
+  // The final row-half reduction reuses [Q_OFF, LSE_OFF).
+  static constexpr int RED_BYTES = 2 * (DQK / 32 + DV / 32) * 16 * 64 * 4;
+  static_assert(RED_BYTES <= LSE_OFF - Q_OFF, "reduction fits the Q/dO area");
+  static_assert(BYTES <= 163840, "fits the LDS of a CU");
+};
+
+template <int DQK, int DV, bool CAP>
+__global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
+  using M = DkdvLds<DQK, DV>;
+  constexpr int RK = M::RK, RV = M::RV;
+  constexpr int NQ = DQK / 32, NV = DV / 32;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  typedef __attribute__((address_space(3))) uint8_t lds_u8;
+  lds_u8* lds = (lds_u8*)smem;
+  lds_u16* Ks = (lds_u16*)(lds + M::K_OFF);
+  lds_u16* Vs = (lds_u16*)(lds + M::V_OFF);
+  lds_u16* Qs = (lds_u16*)(lds + M::Q_OFF);
+  lds_u16* QT = (lds_u16*)(lds + M::QT_OFF);
+  lds_u16* Os = (lds_u16*)(lds + M::O_OFF);
+  lds_u16* OT = (lds_u16*)(lds + M::OT_OFF);
+  lds_f32* lse2s = (lds_f32*)(lds + M::LSE_OFF);
+  lds_f32* Ds = (lds_f32*)(lds + M::D_OFF);
+  lds_i32* segqs = (lds_i32*)(lds + M::SEG_OFF);
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+  const int kh = wave & 1;   // key half of the block
+  const int rh = wave >> 1;  // row half of each sub-tile
+
+  const int c = blockIdx.x % p.n_kv_blocks;
+  const int bk = blockIdx.x / p.n_kv_blocks;  // b * Hkv + kv head
+  const int b = bk / p.Hkv;
+  const int kvh = bk - b * p.Hkv;
+  const int key0 = c * BK;
+  const uint16_t* kg = static_cast<const uint16_t*>(p.k) + (int64_t)bk * p.Lkv * DQK;
+  const uint16_t* vg = static_cast<const uint16_t*>(p.v) + (int64_t)bk * p.Lkv * DV;
+  load_tile<DQK, 256, true, false>(kg, key0, p.Lkv, Ks, nullptr, tid);
+  load_tile<DV, 256, true, false>(vg, key0, p.Lkv, Vs, nullptr, tid);
+
+  const bool has_seg = p.seg_q != nullptr;
+  const int my_key = key0 + 32 * kh + l32;
+  const int32_t* segk = has_seg ? (p.seg_kv ? p.seg_kv + (int64_t)b * p.Lkv : p.seg_q + (int64_t)b * p.L) : nullptr;
+  const int kseg = (has_seg && my_key < p.Lkv) ? segk[my_key] : 0;
+
+  f32x16 dkacc[NQ], dvacc[NV];
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) dkacc[i] = f32x16{};
+#pragma unroll
+  for (int i = 0; i < NV; ++i) dvacc[i] = f32x16{};
+
+  const int x0 = p.col_ptr[c];
+  const int x1 = p.col_ptr[c + 1];
+  for (int g = 0; g < p.group; ++g) {
+    const int head = b * p.Hq + kvh * p.group + g;
+    const uint16_t* qg = static_cast<const uint16_t*>(p.q) + (int64_t)head * p.L * DQK;
+    const uint16_t* og = static_cast<const uint16_t*>(p.dout) + (int64_t)head * p.L * DV;
+    const float* lse = p.lse + (int64_t)head * p.L;
+    const float* dl = p.delta + (int64_t)head * p.L;
+    const int32_t* sq = has_seg ? p.seg_q + (int64_t)b * p.L : nullptr;
+    for (int x = x0; x < x1; ++x) {
+      const int r = p.col_rows[x];
+      for (int sub = 0; sub < BQ / SUB; ++sub) {
+        const int row0 = r * BQ + sub * SUB;
+        if (row0 >= p.L) break;
+        // Sub-tiles whose positions allow no pair with this block are skipped.
+        const int pa = p.q_off + row0;
+        const int pz = pa + SUB - 1;
+        if (p.causal && pz < key0) continue;
+        if (p.window_left >= 0 && pa - (key0 + BK - 1) > p.window_left) continue;
+        if (p.window_right >= 0 && key0 - pz > p.window_right) continue;
+        __syncthreads();  // the previous sub-tile is consumed
+        load_tile<DQK, 256, true, true>(qg, row0, p.L, Qs, QT, tid);
+        load_tile<DV, 256, true, true>(og, row0, p.L, Os, OT, tid);
+        if (tid < SUB) {
+          const int qi = row0 + tid;
+          const bool in = qi < p.L;
+          lse2s[tid] = in ? lse[qi] * kLog2e : INFINITY;
+          Ds[tid] = in ? dl[qi] : 0.0f;
+          segqs[tid] = (has_seg && in) ? sq[qi] : 0;
+        }
+        __syncthreads();
+
+        // S = Q K^T and dP = dO V^T: rows 32 rh + items, key 32 kh + l32.
+        f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+        for (int st = 0; st < DQK / 16; ++st)
+          s = mfma(ld_op(Qs + (32 * rh + l32) * RK + 16 * st + 8 * hi),
+                   ld_op(Ks + (32 * kh + l32) * RK + 16 * st + 8 * hi), s);
+#pragma unroll
+        for (int st = 0; st < DV / 16; ++st)
+          dp = mfma(ld_op(Os + (32 * rh + l32) * RV + 16 * st + 8 * hi),
+                    ld_op(Vs + (32 * kh + l32) * RV + 16 * st + 8 * hi), dp);
+
+        float pv[16], dsv[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int rl = 32 * rh + 8 * (e / 4) + 4 * hi + (e % 4);
+          const bool ok = pair_ok(p, row0 + rl, my_key) & (!has_seg || segqs[rl] == kseg);
+          p_and_ds<CAP>(p, ok, s[e], lse2s[rl], dp[e], Ds[rl], &pv[e], &dsv[e]);
+        }
+        // dV += P^T dO, dK += dS^T Q over this wave's 32 rows (two k-steps).
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          bf16x8 pa8, da8;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            pa8[j] = (__bf16)pv[8 * ks + j];
+            da8[j] = (__bf16)dsv[8 * ks + j];
+          }
+          const int rr = 32 * rh + 16 * ks + 4 * hi;
+#pragma unroll
+          for (int et = 0; et < NV; ++et) {
+            const lds_u16* t = OT + (32 * et + l32) * TP + rr;
+            dvacc[et] = mfma(pa8, ld_op2(t, t + 8), dvacc[et]);
+          }
+#pragma unroll
+          for (int dt = 0; dt < NQ; ++dt) {
+            const lds_u16* t = QT + (32 * dt + l32) * TP + rr;
+            dkacc[dt] = mfma(da8, ld_op2(t, t + 8), dkacc[dt]);
+          }
+        }
+      }
+    }
+  }
+
+  // Sum the two row halves: waves with rh = 1 park their sums in LDS.
+  __syncthreads();
+  lds_f32* red = (lds_f32*)(lds + M::Q_OFF) + kh * (NQ + NV) * 16 * 64;
+  if (rh == 1) {
+#pragma unroll
+    for (int t = 0; t < NQ; ++t)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) red[(t * 16 + e) * 64 + lane] = dkacc[t][e];
+#pragma unroll
+    for (int t = 0; t < NV; ++t)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) red[((NQ + t) * 16 + e) * 64 + lane] = dvacc[t][e];
+  }
+  __syncthreads();
+  if (rh == 0) {
+    float* dkg = p.dk + (int64_t)bk * p.Lkv * DQK;
+    float* dvg = p.dv + (int64_t)bk * p.Lkv * DV;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int key = key0 + 32 * kh + 8 * (e / 4) + 4 * hi + (e % 4);
+      if (key < p.Lkv) {
+#pragma unroll
+        for (int t = 0; t < NQ; ++t)
+          dkg[(int64_t)key * DQK + 32 * t + l32] = p.scale * (dkacc[t][e] + red[(t * 16 + e) * 64 + lane]);
+#pragma unroll
+        for (int t = 0; t < NV; ++t)
+          dvg[(int64_t)key * DV + 32 * t + l32] = dvacc[t][e] + red[((NQ + t) * 16 + e) * 64 + lane];
+      }
+    }
+  }
+}
+
+template <int DQK, int DV>
+struct DqLds {
+  static constexpr int RK = rs<DQK>();
+  static constexpr int RV = rs<DV>();
+  static constexpr int K_OFF = 0;                      // K [64][RK]
+  static constexpr int V_OFF = K_OFF + 64 * RK * 2;    // V [64][RV]
+  static constexpr int KT_OFF = V_OFF + 64 * RV * 2;   // K^T [DQK][TP]
+  static constexpr int SEG_OFF = KT_OFF + DQK * TP * 2;  // key segment ids [64]
+  static constexpr int BYTES = SEG_OFF + 64 * 4;
+  static_assert(BYTES <= 65536, "default LDS allocation");
+};
+
+template <int DQK, int DV, bool CAP>
+__global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
+  using M = DqLds<DQK, DV>;
+  constexpr int RK = M::RK, RV = M::RV;
+  constexpr int NQ = DQK / 32;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  typedef __attribute__((address_space(3))) uint8_t lds_u8;
+  lds_u8* lds = (lds_u8*)smem;
+  lds_u16* Ks = (lds_u16*)(lds + M::K_OFF);
+  lds_u16* Vs = (lds_u16*)(lds + M::V_OFF);
+  lds_u16* KT = (lds_u16*)(lds + M::KT_OFF);
+  lds_i32* segks = (lds_i32*)(lds + M::SEG_OFF);
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+
+  const int r = blockIdx.x % p.n_q_blocks;
+  const int head = blockIdx.x / p.n_q_blocks;  // b * Hq + h
+  const int b = head / p.Hq;
+  const int h = head - b * p.Hq;
+  const int bk = b * p.Hkv + h / p.group;
+  const int qi = r * BQ + 32 * wave + l32;  // this lane's row
+  const bool in = qi < p.L;
+
+  const uint16_t* qg = static_cast<const uint16_t*>(p.q) + (int64_t)head * p.L * DQK;
+  const uint16_t* og = static_cast<const uint16_t*>(p.dout) + (int64_t)head * p.L * DV;
+  const uint16_t* kg = static_cast<const uint16_t*>(p.k) + (int64_t)bk * p.Lkv * DQK;
+  const uint16_t* vg = static_cast<const uint16_t*>(p.v) + (int64_t)bk * p.Lkv * DV;
+
+  // Q and dO of this lane's row as B operands: k-step s -> elements 16s + 8hi .. + 7.
+  bf16x8 qf[DQK / 16], df[DV / 16];
+#pragma unroll
+  for (int st = 0; st < DQK / 16; ++st) {
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (in) v = *reinterpret_cast<const u32x4*>(qg + (int64_t)qi * DQK + 16 * st + 8 * hi);
+    qf[st] = __builtin_bit_cast(bf16x8, v);
+  }
+#pragma unroll
+  for (int st = 0; st < DV / 16; ++st) {
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (in) v = *reinterpret_cast<const u32x4*>(og + (int64_t)qi * DV + 16 * st + 8 * hi);
+    df[st] = __builtin_bit_cast(bf16x8, v);
+  }
+  const float lse2 = in ? p.lse[(int64_t)head * p.L + qi] * kLog2e : INFINITY;
+  const float dlt = in ? p.delta[(int64_t)head * p.L + qi] : 0.0f;
+  const bool has_seg = p.seg_q != nullptr;
+  const int qseg = (has_seg && in) ? p.seg_q[(int64_t)b * p.L + qi] : 0;
+  const int32_t* segk = has_seg ? (p.seg_kv ? p.seg_kv + (int64_t)b * p.Lkv : p.seg_q + (int64_t)b * p.L) : nullptr;
+
+  f32x16 dqacc[NQ];
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) dqacc[i] = f32x16{};
+
+  const int x0 = p.row_ptr[r];
+  const int x1 = p.row_ptr[r + 1];
+  for (int x = x0; x < x1; ++x) {
+    const int key0 = p.active_cols[x] * BK;
+    __syncthreads();  // the previous block is consumed
+    load_tile<DQK, 512, true, true>(kg, key0, p.Lkv, Ks, KT, tid);
+    load_tile<DV, 512, true, false>(vg, key0, p.Lkv, Vs, nullptr, tid);
+    if (tid < BK) segks[tid] = (has_seg && key0 + tid < p.Lkv) ? segk[key0 + tid] : 0;
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      // S^T = K Q^T and dP^T = V dO^T: keys 32t + items, row l32.
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int st = 0; st < DQK / 16; ++st)
+        s = mfma(ld_op(Ks + (32 * t + l32) * RK + 16 * st + 8 * hi), qf[st], s);
+#pragma unroll
+      for (int st = 0; st < DV / 16; ++st)
+        dp = mfma(ld_op(Vs + (32 * t + l32) * RV + 16 * st + 8 * hi), df[st], dp);
+      float pv[16], dsv[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int kl = 32 * t + 8 * (e / 4) + 4 * hi + (e % 4);
+        const bool ok = pair_ok(p, qi, key0 + kl) & (!has_seg || segks[kl] == qseg);
+        p_and_ds<CAP>(p, ok, s[e], lse2, dp[e], dlt, &pv[e], &dsv[e]);
+      }
+      // dQ += dS K over this tile's 32 keys (two k-steps).
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        bf16x8 da8;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) da8[j] = (__bf16)dsv[8 * ks + j];
+        const int kk = 32 * t + 16 * ks + 4 * hi;
+#pragma unroll
+        for (int dt = 0; dt < NQ; ++dt) {
+          const lds_u16* tp = KT + (32 * dt + l32) * TP + kk;
+          dqacc[dt] = mfma(da8, ld_op2(tp, tp + 8), dqacc[dt]);
+        }
+      }
+    }
+  }
+
+  // dq rows 32 wave + items, columns 32 dt + l32.
+  float* dqg = p.dq + (int64_t)head * p.L * DQK;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int row = r * BQ + 32 * wave + 8 * (e / 4) + 4 * hi + (e % 4);
+    if (row < p.L) {
+#pragma unroll
+      for (int t = 0; t < NQ; ++t) dqg[(int64_t)row * DQK + 32 * t + l32] = p.scale * dqacc[t][e];
+    }
+  }
+}
+
+template <int DQK, int DV, bool CAP>
+hipError_t launch_all(const BwdParams& p, hipStream_t s) {
+  const int64_t rows = (int64_t)p.B * p.Hq * p.L;
+  if (rows > 0) {
+    hipLaunchKernelGGL(bwd_delta_kernel<DV>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int64_t n_kv_items = (int64_t)p.B * p.Hkv * p.n_kv_blocks;
+  if (n_kv_items > 0) {
+    const int bytes = DkdvLds<DQK, DV>::BYTES;
+    auto fn = bwd_dkdv_kernel<DQK, DV, CAP>;
+    if (bytes > 65536) {
+      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+      (void)hipGetLastError();
+    }
+    hipLaunchKernelGGL(fn, dim3((unsigned)n_kv_items), dim3(256), bytes, s, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int64_t n_q_items = (int64_t)p.B * p.Hq * p.n_q_blocks;
+  if (n_q_items > 0) {
+    constexpr int bytes = DqLds<DQK, DV>::BYTES;
+    auto fn = bwd_dq_kernel<DQK, DV, CAP>;
+    hipLaunchKernelGGL(fn, dim3((unsigned)n_q_items), dim3(512), bytes, s, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <int DQK, int DV>
+hipError_t launch_cap(const BwdParams& p, hipStream_t s) {
+  return p.soft_cap > 0.0f ? launch_all<DQK, DV, true>(p, s) : launch_all<DQK, DV, false>(p, s);
+}
+
+}  // namespace
+
+hipError_t launch_bwd_bf16(const BwdParams& p, int d_qk, int d_v, hipStream_t s) {
+  if (d_qk == 128 && d_v == 128) return launch_cap<128, 128>(p, s);
+  if (d_qk == 64 && d_v == 64) return launch_cap<64, 64>(p, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace splash

@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define SPLASH_VERSION 103
+#define SPLASH_VERSION 104
 
 /* Largest n_split of splash_attn_fwd_split. */
 #define SPLASH_MAX_SPLIT 64
@@ -165,6 +165,20 @@ typedef struct splash_mask_tables {
  * match), SPLASH_ENOMEM. */
 int attn_mask_compile(const splash_mask_desc* desc, splash_mask_sizes* sizes,
                       splash_mask_tables* tables);
+
+/* Column-major view of the active list (host arrays), for work that owns
+ * one kv-block column: the backward sums the gradients of a K/V block over
+ * the q-block rows that read it.  From row_ptr [n_q_blocks + 1] and
+ * active_cols [n_active] of attn_mask_compile, fills col_ptr
+ * [n_kv_blocks + 1] (CSR offsets per column), col_rows [n_active] (the rows
+ * of each column, ascending) and col_entry [n_active] (the row-major index
+ * of each block, for block_code / mask_next).  Caller-owned arrays.
+ * Errors: SPLASH_EINVAL (negative size, NULL array, row_ptr not running
+ * from 0 to n_active or decreasing, a row's columns not ascending within
+ * [0, n_kv_blocks)). */
+int attn_mask_columns(int32_t n_q_blocks, int32_t n_kv_blocks, int32_t n_active,
+                      const int32_t* row_ptr, const int32_t* active_cols,
+                      int32_t* col_ptr, int32_t* col_rows, int32_t* col_entry);
 
 /* ------------------------------------------------------------------------
  * Forward.
@@ -286,6 +300,77 @@ int splash_split_workspace_bytes(int32_t n_split, int32_t B, int32_t Hq, int32_t
  * ordered on one stream. */
 int splash_attn_fwd_split(const splash_fwd_args* args, int32_t n_split, void* workspace,
                           int64_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Backward.
+ *
+ * Gradients of the forward's o with respect to q, k and v, given the
+ * upstream gradient do = dLoss/do and the forward's residual lse.  The
+ * probabilities are rebuilt on chip from the stored lse, p = e^(logit - lse)
+ * (Lecture 13 section 6.3: the forward writes the per-row logsumexp for the
+ * backward; joto.ai "LSE and online softmax": the backward recomputes p from
+ * q, k and the lse scalar of each row), so no attention matrix is stored.
+ * With y = scale q.k, logit z = cap tanh(y / cap) (z = y without a cap):
+ *   dv_j = sum_i p_ij do_i,   dp_ij = do_i . v_j,   D_i = do_i . o_i,
+ *   dy_ij = p_ij (dp_ij - D_i) (1 - tanh^2(y_ij / cap) with a cap),
+ *   dq_i = scale sum_j dy_ij k_j,   dk_j = scale sum_i dy_ij q_i,
+ * summed over the query heads of a K/V group for dk and dv.
+ * ---------------------------------------------------------------------- */
+
+typedef struct splash_bwd_args {
+  int32_t dtype;         /* SPLASH_BF16 (q, k, v, o, dout) */
+  int32_t B, Hq, Hkv;    /* as in splash_fwd_args */
+  int32_t L;             /* query rows */
+  int32_t L_kv;          /* key positions; 0: equal to L */
+  int32_t q_offset;      /* query row i sits at key position q_offset + i */
+  int32_t d_qk, d_v;     /* (64, 64) or (128, 128) */
+  const void* q;         /* device [B, Hq, L, d_qk] */
+  const void* k;         /* device [B, Hkv, L_kv, d_qk] */
+  const void* v;         /* device [B, Hkv, L_kv, d_v] */
+  const void* o;         /* device [B, Hq, L, d_v]: the forward's output */
+  const float* lse;      /* device [B, Hq, L]: the forward's lse */
+  const void* dout;      /* device [B, Hq, L, d_v]: upstream gradient */
+  float* dq;             /* device [B, Hq, L, d_qk] float32 output */
+  float* dk;             /* device [B, Hkv, L_kv, d_qk] float32 output */
+  float* dv;             /* device [B, Hkv, L_kv, d_v] float32 output */
+  float* delta;          /* device [B, Hq, L] float32 scratch, caller-owned:
+                            receives D_i = do_i . o_i */
+  /* Mask (as in splash_fwd_args; the element mask is computed from
+   * positions and segment ids on every active block). */
+  int32_t causal;
+  int32_t window_left;
+  int32_t window_right;
+  const int32_t* seg_q;  /* device [B, L] or NULL */
+  const int32_t* seg_kv; /* device [B, L_kv] or NULL (NULL: same as seg_q) */
+  /* Tables for L_q = L, L_kv, q_offset at the forward's block sizes: the
+   * row-major list of attn_mask_compile and its column view from
+   * attn_mask_columns, as device copies. */
+  int32_t block_q;       /* splash_fwd_tile's block_q for (bf16, d_qk, d_v) */
+  int32_t block_kv;      /* splash_fwd_tile's block_kv */
+  int32_t n_q_blocks;    /* ceil(L / block_q) */
+  int32_t n_kv_blocks;   /* ceil(L_kv / block_kv) */
+  int32_t n_active;
+  const int32_t* row_ptr;      /* device [n_q_blocks + 1] */
+  const int32_t* active_cols;  /* device [n_active] */
+  const int32_t* col_ptr;      /* device [n_kv_blocks + 1] */
+  const int32_t* col_rows;     /* device [n_active] */
+  float scale;           /* as in the forward */
+  float soft_cap;        /* as in the forward; <= 0 disables it */
+} splash_bwd_args;
+
+/* Enqueue the backward on `stream` (a hipStream_t; NULL = the default
+ * stream): a kernel for delta, one for dk and dv (one work-group per K/V
+ * head and kv block, looping over the column's q blocks and the group's
+ * query heads: no atomics) and one for dq (one work-group per query head
+ * and q block, looping over the row's kv blocks).  Every element of dq, dk
+ * and dv is written (0 where no allowed pair reaches it).  Validation
+ * errors are returned synchronously: SPLASH_EINVAL (NULL or misaligned
+ * buffers, bad flag or window, scale, soft_cap, negative sizes),
+ * SPLASH_ESHAPE (Hq % Hkv, block sizes or block counts not matching,
+ * size overflow), SPLASH_EDTYPE, SPLASH_EUNSUPPORTED (f32, head dims),
+ * SPLASH_EHIP (a launch failed).  B, Hq or L equal to 0 writes dk and dv
+ * only if it has keys (zeros); all sizes 0 is a no-op. */
+int splash_attn_bwd(const splash_bwd_args* args, void* stream);
 
 #ifdef __cplusplus
 }  /* extern "C" */

@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
     assert set(declared) == set(_lib.EXPORTED), declared
     for name in declared:
         assert hasattr(lib, name), name
-    assert lib.splash_version() == 103
+    assert lib.splash_version() == 104
 
 
 def _assert_tables_equal(t, ref):
@@ -265,4 +265,89 @@ def test_split_forward_noops():
     lib = _lib.load()
     assert lib.splash_attn_fwd_split(None, 2, None, 0, None) == 1
     assert lib.splash_attn_fwd_split(ctypes.byref(_good_args(B=0)), 2, None, 0, None) == 0
+    assert lib.splash_last_error() == b""
+
+
+@settings(max_examples=60, deadline=None)
+@given(Lq=st.integers(1, 300), Lkv=st.integers(1, 300), off=st.integers(0, 100),
+       bq=st.sampled_from([4, 16, 64]), bkv=st.sampled_from([5, 16, 64]),
+       causal=st.booleans(), wl=st.integers(-1, 60), wr=st.integers(-1, 60))
+def test_columns_bit_exact(Lq, Lkv, off, bq, bkv, causal, wl, wr):
+    """attn_mask_columns against the oracle's column view of the block mask."""
+    from oracle import column_tables_ref
+    t = compile_mask(Lq, bq, bkv, L_kv=Lkv, q_offset=off, causal=causal, window_left=wl,
+                     window_right=wr)
+    got = t.columns()
+    ref = column_tables_ref(t.block_mask)
+    for name in ("col_ptr", "col_rows", "col_entry"):
+        assert np.array_equal(got[name], ref[name]), name
+
+
+def test_columns_errors():
+    lib = _lib.load()
+    P = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    row_ptr = np.array([0, 2, 3], np.int32)
+    cols = np.array([0, 1, 1], np.int32)
+    cp, cr, ce = np.zeros(3, np.int32), np.zeros(3, np.int32), np.zeros(3, np.int32)
+    assert lib.attn_mask_columns(2, 2, 3, P(row_ptr), P(cols), P(cp), P(cr), P(ce)) == 0
+    assert cp.tolist() == [0, 1, 3] and cr.tolist() == [0, 0, 1] and ce.tolist() == [0, 1, 2]
+    assert lib.attn_mask_columns(-1, 2, 3, P(row_ptr), P(cols), P(cp), P(cr), P(ce)) == 1
+    assert lib.attn_mask_columns(2, 2, 3, None, P(cols), P(cp), P(cr), P(ce)) == 1
+    assert lib.attn_mask_columns(2, 2, 4, P(row_ptr), P(cols), P(cp), P(cr), P(ce)) == 1
+    bad = np.array([1, 0, 1], np.int32)          # columns not ascending in row 0
+    assert lib.attn_mask_columns(2, 2, 3, P(row_ptr), P(bad), P(cp), P(cr), P(ce)) == 1
+    out = np.array([0, 2, 1], np.int32)          # column out of range
+    assert lib.attn_mask_columns(2, 2, 3, P(row_ptr), P(out), P(cp), P(cr), P(ce)) == 1
+    assert len(lib.splash_last_error()) > 0
+
+
+def _good_bwd(**over):
+    fake = 0x10000
+    a = dict(dtype=1, B=1, Hq=2, Hkv=1, L=256, L_kv=0, q_offset=0, d_qk=128, d_v=128,
+             q=fake, k=fake, v=fake, o=fake, lse=fake, dout=fake, dq=fake, dk=fake, dv=fake,
+             delta=fake, causal=1, window_left=-1, window_right=-1, seg_q=None, seg_kv=None,
+             block_q=256, block_kv=64, n_q_blocks=1, n_kv_blocks=4, n_active=4,
+             row_ptr=fake, active_cols=fake, col_ptr=fake, col_rows=fake,
+             scale=0.088, soft_cap=0.0)
+    a.update(over)
+    return _lib.BwdArgs(**a)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(dtype=5), 3),
+    (dict(dtype=0), 4),                         # bf16 only
+    (dict(d_qk=192), 4),
+    (dict(d_qk=64, d_v=128), 4),
+    (dict(B=-1), 1),
+    (dict(Hkv=0), 1),
+    (dict(Hq=3, Hkv=2), 2),
+    (dict(L_kv=-1), 1),
+    (dict(q_offset=-1), 1),
+    (dict(causal=2), 1),
+    (dict(window_right=-3), 1),
+    (dict(scale=0.0), 1),
+    (dict(soft_cap=math.inf), 1),
+    (dict(seg_kv=0x10000), 1),
+    (dict(L_kv=300, n_kv_blocks=5, seg_q=0x10000), 1),
+    (dict(block_q=128), 2),
+    (dict(n_q_blocks=2), 2),
+    (dict(n_kv_blocks=3), 2),
+    (dict(n_active=-1), 1),
+    (dict(dq=None), 1),
+    (dict(delta=None), 1),
+    (dict(col_ptr=None), 1),
+    (dict(col_rows=None), 1),
+    (dict(dk=0x10004), 1),
+    (dict(L_kv=1 << 24, n_kv_blocks=(1 << 24) // 64), 2),
+])
+def test_backward_validation_errors(over, code):
+    lib = _lib.load()
+    assert lib.splash_attn_bwd(ctypes.byref(_good_bwd(**over)), None) == code
+    assert len(lib.splash_last_error()) > 0
+
+
+def test_backward_null_args_and_noop():
+    lib = _lib.load()
+    assert lib.splash_attn_bwd(None, None) == 1
+    assert lib.splash_attn_bwd(ctypes.byref(_good_bwd(B=0)), None) == 0
     assert lib.splash_last_error() == b""

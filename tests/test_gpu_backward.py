@@ -1,0 +1,111 @@
+"""GPU parity of the backward (``splash_attn_bwd`` through the C ABI) against
+the float64 oracle gradients ``attention_bwd_ref``.
+
+Inputs are the stored bf16 q, k, v and upstream gradient; o and lse come from
+this library's forward, as a training step would use them.  Tolerance: the
+max-abs error of each gradient tensor at most TOL times that tensor's
+max-abs reference value.  The kernels round p and dS to bf16 (8 significant
+bits, relative error up to 2^-9) as MFMA operands and take D = do . o from
+the bf16 forward output, so each product term carries a relative error of a
+few 2^-9; TOL = 2^-5 leaves a factor of about 5 over that for the sums.
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from block_sparse_flash_amd import compile_mask, fwd_tile, splash_bwd, splash_fwd
+from block_sparse_flash_amd.inputs import as_f64, draw_qkv, segment_ids, stored
+from oracle import attention_bwd_ref
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2.0 ** -5
+
+
+def _announce(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def _check(name, got, ref):
+    got = got.detach().float().cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(got)), f"{name}: non-finite gradient"
+    scale = float(np.max(np.abs(ref))) if ref.size else 0.0
+    err = float(np.max(np.abs(got - ref))) if ref.size else 0.0
+    assert err <= TOL * scale + 1e-6, f"{name}: max-abs error {err:.3g} > {TOL} x {scale:.3g}"
+    return err / scale if scale > 0 else 0.0
+
+
+def _run_case(B, Hq, Hkv, Lq, Lkv, d, mk, cap, seed, q_offset=0, seg_q=None, seg_kv=None):
+    q, k, v = (stored(a, "bf16") for a in draw_qkv(B, Hq, Hkv, Lq, d, d, seed,
+                                                   qk_std=1.5 if cap else 1.0, L_kv=Lkv))
+    rng = np.random.default_rng(seed + 99)
+    do = stored(rng.standard_normal((B, Hq, Lq, d), dtype=np.float32), "bf16")
+    scale = 1.0 / math.sqrt(d)
+    qd, kd, vd, dod = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    o, lse = splash_fwd(qd, kd, vd, scale=scale, soft_cap=cap, seg_q=seg_q, seg_kv=seg_kv,
+                        q_offset=q_offset, **mk)
+    dq, dk, dv = splash_bwd(qd, kd, vd, o, lse, dod, scale=scale, soft_cap=cap, seg_q=seg_q,
+                            seg_kv=seg_kv, q_offset=q_offset, **mk)
+    torch.cuda.synchronize()
+    rdq, rdk, rdv = attention_bwd_ref(as_f64(q), as_f64(k), as_f64(v), as_f64(do), scale=scale,
+                                      soft_cap=cap, seg_q=seg_q, seg_kv=seg_kv,
+                                      q_offset=q_offset, **mk)
+    e = (_check("dq", dq, rdq), _check("dk", dk, rdk), _check("dv", dv, rdv))
+    _announce(f"  relative max-abs errors dq {e[0]:.3g} dk {e[1]:.3g} dv {e[2]:.3g}")
+
+
+CASES = [
+    # (B, Hq, Hkv, L, d, mask kwargs, soft_cap, segments (lo, hi) or None)
+    (1, 2, 2, 256, 128, dict(causal=True), 0.0, None),
+    (2, 4, 2, 700, 128, dict(causal=True, window_left=200), 0.0, None),
+    (1, 4, 1, 600, 64, dict(causal=True), 20.0, (40, 250)),
+    (1, 2, 2, 333, 128, dict(), 0.0, None),
+    (1, 2, 1, 300, 64, dict(window_left=70, window_right=33), 3.0, None),
+    (1, 8, 2, 2048, 128, dict(causal=True), 0.0, None),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"B{c[0]}H{c[1]}/{c[2]}-L{c[3]}-d{c[4]}"
+                         + ("-cap" if c[6] else "") + ("-seg" if c[7] else "") + "-"
+                         + "-".join(sorted(c[5])))
+def test_backward_every_element(case):
+    B, Hq, Hkv, L, d, mk, cap, segs = case
+    _announce(f"backward {case}")
+    seg = None if segs is None else segment_ids(L, 500 + L, *segs)
+    _run_case(B, Hq, Hkv, L, L, d, mk, cap, 500 + L + d, seg_q=seg)
+
+
+def test_backward_decode_positions_and_empty_rows():
+    """Query rows at key positions q_offset + i, with L_q != L_kv; in the
+    second case rows past position 949 see no key (zero gradients)."""
+    _announce("backward decode Lq=40 Lkv=900 off=860")
+    _run_case(1, 4, 2, 40, 900, 128, dict(causal=True), 0.0, 61, q_offset=860)
+    _announce("backward rows without keys Lq=64 Lkv=700 off=900")
+    _run_case(1, 2, 2, 64, 700, 64, dict(causal=True, window_left=250), 0.0, 62, q_offset=900)
+
+
+def test_backward_per_batch_segments():
+    """Different document boundaries per batch element (the binding runs one
+    table per batch element)."""
+    _announce("backward per-batch segments")
+    L = 500
+    seg = np.stack([segment_ids(L, 71, 30, 200), segment_ids(L, 72, 50, 300)])
+    _run_case(2, 2, 1, L, L, 64, dict(causal=True), 0.0, 73, seg_q=seg)
+
+
+def test_backward_deterministic():
+    """No atomics: two calls give bit-identical gradients."""
+    q, k, v = (stored(a, "bf16").cuda() for a in draw_qkv(1, 4, 2, 900, 128, 128, 81))
+    do = torch.randn(1, 4, 900, 128, generator=torch.Generator().manual_seed(3)).to(torch.bfloat16).cuda()
+    o, lse = splash_fwd(q, k, v, causal=True)
+    g1 = splash_bwd(q, k, v, o, lse, do, causal=True)
+    g2 = splash_bwd(q, k, v, o, lse, do, causal=True)
+    torch.cuda.synchronize()
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
