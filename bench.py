@@ -106,6 +106,40 @@ def cpu_baseline(w, q, k, v, seg, budget_s):
                       f"rows each (against {w.keys} keys), float64 numpy, {dt:.1f} s"}
 
 
+def cpu_baseline_bwd(w, q, k, v, seg, budget_s):
+    """The float64 backward oracle on the host over whole (batch, head) pairs
+    in order (each with its own K/V head and a seeded upstream gradient),
+    adding heads until about budget_s of work; returns the baseline dict."""
+    import numpy as np
+    from oracle import attention_bwd_ref
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    qf, kf, vf = q.float().numpy(), k.float().numpy(), v.float().numpy()
+    group = w.Hq // w.Hkv
+    rng = np.random.default_rng(w.seed + 2)
+    pairs = unmasked_pairs(None, w, seg)
+    done = 0
+    t0 = time.perf_counter()
+    while done < w.B * w.Hq and (time.perf_counter() - t0) < budget_s:
+        b, h = divmod(done, w.Hq)
+        kh = h // group
+        do = rng.standard_normal((1, 1, w.L, w.d_v))
+        attention_bwd_ref(qf[b:b + 1, h:h + 1], kf[b:b + 1, kh:kh + 1], vf[b:b + 1, kh:kh + 1], do,
+                          scale=w.softmax_scale, soft_cap=w.soft_cap, causal=w.causal,
+                          window_left=w.window_left, window_right=w.window_right, seg_q=seg,
+                          q_offset=w.q_offset)
+        done += 1
+    dt = time.perf_counter() - t0
+    flop = 2.0 * (3 * w.d_qk + 2 * w.d_v) * pairs * done
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"backward of {done} of {w.B * w.Hq} (batch, head) pairs in order, all "
+                      f"{w.L} rows each, float64 numpy, {dt:.1f} s"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -119,6 +153,9 @@ def main():
     ap.add_argument("--n-split", type=int, default=None,
                     help="split-KV: chunks per row merged through their lse (bf16; 1 = plain "
                          "forward); default: the workload's own (1 except for decoding)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward (dq, dk, dv from o, lse and a random upstream "
+                         "gradient) instead of the forward")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run one device-to-device copy of this many MiB "
                          "(a plain copy of known size, for scaling HBM counters)")
@@ -158,8 +195,20 @@ def main():
                          dtype=torch.uint8, device=dev)
         kw.update(n_split=args.n_split, workspace=ws)
 
-    for _ in range(args.warmup):
+    if args.backward:
+        from block_sparse_flash_amd import splash_bwd
+        if w.dtype != "bf16" or args.n_split != 1:
+            raise SystemExit("--backward runs bf16 workloads without split-KV")
         splash_fwd(qd, kd, vd, **kw)
+        g = torch.Generator().manual_seed(w.seed + 1)
+        dod = torch.randn(out.shape, generator=g).to(torch.bfloat16).to(dev)
+        bkw = dict(scale=w.softmax_scale, soft_cap=w.soft_cap, seg_q=seg, tables=tabs,
+                   q_offset=w.q_offset, **mask_kw)
+        step = lambda: splash_bwd(qd, kd, vd, out, lse, dod, **bkw)
+    else:
+        step = lambda: splash_fwd(qd, kd, vd, **kw)
+    for _ in range(args.warmup):
+        step()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
     ev0 = torch.cuda.Event(enable_timing=True)
@@ -168,7 +217,7 @@ def main():
     wall0 = time.perf_counter()
     ev0.record(stream)
     for _ in range(args.steps):
-        splash_fwd(qd, kd, vd, **kw)
+        step()
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -176,12 +225,15 @@ def main():
     ms_per_step = ms_events / args.steps
 
     pairs = unmasked_pairs(tabs, w, seg)
-    flop_per_step = 2.0 * (w.d_qk + w.d_v) * pairs * w.B * w.Hq
+    # Algorithmic FLOP per unmasked pair: forward S = QK^T and PV; backward
+    # S, dP = dO V^T, dV = P^T dO, dK = dS^T Q and dQ = dS K.
+    flop_pair = 2.0 * (3 * w.d_qk + 2 * w.d_v) if args.backward else 2.0 * (w.d_qk + w.d_v)
+    flop_per_step = flop_pair * pairs * w.B * w.Hq
     tflops = flop_per_step / (ms_per_step * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
-    traffic = committed_traffic(w.name, w.dtype)
+    traffic = None if args.backward else committed_traffic(w.name, w.dtype)
     decode = w.keys != w.L or w.q_offset != 0
-    if decode:
+    if decode and not args.backward:
         # Decoding: a few query rows against a long K/V cache; the forward
         # streams K and V once per K/V head and is bound by HBM.  Algorithmic
         # bytes: K and V of every K/V head, q and o of every query head, lse.
@@ -199,7 +251,7 @@ def main():
 
     cpu = None
     if args.cpu_budget > 0:
-        cpu = cpu_baseline(w, q, k, v, seg, args.cpu_budget)
+        cpu = (cpu_baseline_bwd if args.backward else cpu_baseline)(w, q, k, v, seg, args.cpu_budget)
 
     mask = "causal" if w.causal else "dense"
     if w.window_left >= 0 or w.window_right >= 0:
@@ -207,7 +259,9 @@ def main():
     if w.segments:
         mask += f"+segments U[{w.seg_min},{w.seg_max}]"
     rec = {
-        "metric": "effective attention TFLOP/s (unmasked FLOPs) and % of bf16 MFMA peak",
+        "metric": ("effective attention backward TFLOP/s (unmasked FLOPs) and % of bf16 MFMA peak"
+                   if args.backward else
+                   "effective attention TFLOP/s (unmasked FLOPs) and % of bf16 MFMA peak"),
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -224,7 +278,7 @@ def main():
                    "d_qk": w.d_qk, "d_v": w.d_v, "mask": mask, "soft_cap": w.soft_cap,
                    "scale": w.softmax_scale, "block_q": bq, "block_kv": bkv,
                    "mask_mode": args.mask_mode, "max_logit": args.max_logit,
-                   "n_split": args.n_split,
+                   "n_split": args.n_split, "pass": "backward" if args.backward else "forward",
                    "parallelism": "single GPU"},
         "pct_of_peak": round(100.0 * tflops / peak, 2),
         "unmasked_tflop_per_step": flop_per_step / 1e12,

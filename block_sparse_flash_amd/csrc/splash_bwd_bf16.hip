@@ -24,15 +24,16 @@
 //     key per lane and 16 rows per lane; those accumulator items, rounded to
 //     bf16, are directly the A operand of dV += P^T dO and dK += dS^T Q (the
 //     MFMA's reduction index runs over the rows in the order the accumulator
-//     holds them), and the B operands come from transposed copies of Q and
-//     dO in LDS.  The two row halves are summed through LDS at the end.
+//     holds them), and the B operands are read transposed from the row-major
+//     Q and dO tiles with ds_read_b64_tr_b16 (four consecutive rows of one
+//     column per lane, the row grouping the accumulator implies).  The two
+//     row halves are summed through LDS at the end.
 //   * dq kernel: one work-group (8 waves, 32 rows each) per (query head,
 //     256-row q block) walks the row's active kv blocks; S^T = K Q^T and
 //     dP^T = V dO^T hold one row per lane, and dS^T feeds dQ += dS K the same
-//     way, with K transposed in LDS.
-//   * LDS tiles are padded (row-major rows by 16 bytes, transposed rows to
-//     68 elements) so that the 32 lanes of an operand read fall in distinct
-//     banks.
+//     way, with K read transposed.
+//   * LDS tiles are row-major with rows padded by 16 bytes, so that the 16
+//     lanes of a ds_read_b128 operand read fall in distinct banks.
 //   * Gradients are accumulated and written in float32.
 
 #include <hip/hip_runtime.h>
@@ -49,10 +50,10 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) uint16_t lds_u16;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
-typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 typedef __attribute__((address_space(3))) float lds_f32;
 typedef __attribute__((address_space(3))) int32_t lds_i32;
@@ -60,7 +61,6 @@ typedef __attribute__((address_space(3))) int32_t lds_i32;
 constexpr int BQ = kBf16BlockQ;   // rows per q block of the tables
 constexpr int BK = kBf16BlockKV;  // keys per kv block of the tables
 constexpr int SUB = 64;           // rows per sub-tile in the dk/dv kernel
-constexpr int TP = 68;            // row stride (elements) of transposed tiles
 constexpr float kLog2e = 1.4426950408889634f;
 
 // Row stride (elements) of a row-major tile with D columns.
@@ -75,11 +75,17 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t x) { return __uint_as_floa
 
 __device__ __forceinline__ bf16x8 ld_op(const lds_u16* ptr) { return *reinterpret_cast<const lds_bf16x8*>(ptr); }
 
-// Two 4-element runs (8 bytes each) of a transposed tile as one operand.
-__device__ __forceinline__ bf16x8 ld_op2(const lds_u16* lo, const lds_u16* hi) {
-  const u32x2 a = *reinterpret_cast<const lds_u32x2*>(lo);
-  const u32x2 b = *reinterpret_cast<const lds_u32x2*>(hi);
-  const u32x4 v = {a[0], a[1], b[0], b[1]};
+// Operand of 8 rows of one column from a row-major tile: in each group of
+// 16 lanes, lane j addresses row base + j / 4 at columns 4 (j % 4) .. + 3 of
+// the group's 16 columns, and ds_read_b64_tr_b16 hands lane i of the group
+// rows base .. base + 3 of column i; `lo` and `hi` are the lane's addresses
+// in the two 4-row runs (rows base and base + 8).
+__device__ __forceinline__ bf16x8 ld_tr(const lds_u16* lo, const lds_u16* hi) {
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)lo);
+  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)hi);
+  const u32x2 a2 = __builtin_bit_cast(u32x2, a);
+  const u32x2 b2 = __builtin_bit_cast(u32x2, b);
+  const u32x4 v = {a2[0], a2[1], b2[0], b2[1]};
   return __builtin_bit_cast(bf16x8, v);
 }
 
@@ -94,11 +100,9 @@ __device__ __forceinline__ bool pair_ok(const BwdParams& p, int qi, int key) {
 }
 
 // Copies rows row0 .. row0 + 63 of a row-major [n_valid, D] bf16 matrix
-// into LDS (zeros past n_valid): row-major with stride rs<D>() into `rm`
-// and/or transposed ([D][TP]) into `tr`.
-template <int D, int NTHR, bool RM, bool TR>
-__device__ __forceinline__ void load_tile(const uint16_t* g, int row0, int n_valid, lds_u16* rm,
-                                          lds_u16* tr, int tid) {
+// into LDS (zeros past n_valid), row-major with stride rs<D>().
+template <int D, int NTHR>
+__device__ __forceinline__ void load_tile(const uint16_t* g, int row0, int n_valid, lds_u16* rm, int tid) {
   constexpr int CH = D / 8;
   constexpr int TOTAL = 64 * CH;
   static_assert(TOTAL % NTHR == 0, "whole chunks per thread");
@@ -109,14 +113,39 @@ __device__ __forceinline__ void load_tile(const uint16_t* g, int row0, int n_val
     const int c = x - r * CH;
     u32x4 val = {0u, 0u, 0u, 0u};
     if (row0 + r < n_valid) val = *reinterpret_cast<const u32x4*>(g + (int64_t)(row0 + r) * D + c * 8);
-    if constexpr (RM) *reinterpret_cast<lds_u32x4*>(rm + r * rs<D>() + c * 8) = val;
-    if constexpr (TR) {
-      const u16x8 e = __builtin_bit_cast(u16x8, val);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) tr[(c * 8 + i) * TP + r] = e[i];
-    }
+    *reinterpret_cast<lds_u32x4*>(rm + r * rs<D>() + c * 8) = val;
   }
 }
+
+// Rows row0 .. row0 + 63 of a row-major [n_valid, D] bf16 matrix staged in
+// registers (zeros past n_valid): fetched from global memory while the
+// previous tile is being used, stored to LDS after the next barrier.
+template <int D, int NTHR>
+struct TileRegs {
+  static constexpr int CH = D / 8;
+  static constexpr int N = 64 * CH / NTHR;
+  static_assert(64 * CH % NTHR == 0, "whole chunks per thread");
+  u32x4 v[N];
+  __device__ __forceinline__ void fetch(const uint16_t* g, int row0, int n_valid, int tid) {
+#pragma unroll
+    for (int it = 0; it < N; ++it) {
+      const int x = it * NTHR + tid;
+      const int r = x / CH;
+      const int c = x - r * CH;
+      v[it] = u32x4{0u, 0u, 0u, 0u};
+      if (row0 + r < n_valid) v[it] = *reinterpret_cast<const u32x4*>(g + (int64_t)(row0 + r) * D + c * 8);
+    }
+  }
+  __device__ __forceinline__ void store(lds_u16* rm, int tid) const {
+#pragma unroll
+    for (int it = 0; it < N; ++it) {
+      const int x = it * NTHR + tid;
+      const int r = x / CH;
+      const int c = x - r * CH;
+      *reinterpret_cast<lds_u32x4*>(rm + r * rs<D>() + c * 8) = v[it];
+    }
+  }
+};
 
 // Probability and score gradient of one (row, key) pair from its raw dot
 // product s, the row's lse (log2 units), its D and dP.
@@ -161,16 +190,14 @@ struct DkdvLds {
   static constexpr int K_OFF = 0;                          // K [64][RK]
   static constexpr int V_OFF = K_OFF + 64 * RK * 2;        // V [64][RV]
   static constexpr int Q_OFF = V_OFF + 64 * RV * 2;        // Q [64][RK]
-  static constexpr int QT_OFF = Q_OFF + 64 * RK * 2;       // Q^T [DQK][TP]
-  static constexpr int O_OFF = QT_OFF + DQK * TP * 2;      // dO [64][RV]
-  static constexpr int OT_OFF = O_OFF + 64 * RV * 2;       // dO^T [DV][TP]
-  static constexpr int LSE_OFF = OT_OFF + DV * TP * 2;     // lse * log2(e) [64]
+  static constexpr int O_OFF = Q_OFF + 64 * RK * 2;        // dO [64][RV]
+  static constexpr int LSE_OFF = O_OFF + 64 * RV * 2;      // lse * log2(e) [64]
   static constexpr int D_OFF = LSE_OFF + 64 * 4;           // D [64]
   static constexpr int SEG_OFF = D_OFF + 64 * 4;           // row segment ids [64]
   static constexpr int BYTES = SEG_OFF + 64 * 4;
-  // The final row-half reduction reuses [Q_OFF, LSE_OFF).
+  // The final row-half reduction reuses the tiles [0, LSE_OFF).
   static constexpr int RED_BYTES = 2 * (DQK / 32 + DV / 32) * 16 * 64 * 4;
-  static_assert(RED_BYTES <= LSE_OFF - Q_OFF, "reduction fits the Q/dO area");
+  static_assert(RED_BYTES <= LSE_OFF, "reduction fits the tile area");
   static_assert(BYTES <= 163840, "fits the LDS of a CU");
 };
 
@@ -185,9 +212,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
   lds_u16* Ks = (lds_u16*)(lds + M::K_OFF);
   lds_u16* Vs = (lds_u16*)(lds + M::V_OFF);
   lds_u16* Qs = (lds_u16*)(lds + M::Q_OFF);
-  lds_u16* QT = (lds_u16*)(lds + M::QT_OFF);
   lds_u16* Os = (lds_u16*)(lds + M::O_OFF);
-  lds_u16* OT = (lds_u16*)(lds + M::OT_OFF);
   lds_f32* lse2s = (lds_f32*)(lds + M::LSE_OFF);
   lds_f32* Ds = (lds_f32*)(lds + M::D_OFF);
   lds_i32* segqs = (lds_i32*)(lds + M::SEG_OFF);
@@ -199,6 +224,10 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
   const int hi = lane >> 5;
   const int kh = wave & 1;   // key half of the block
   const int rh = wave >> 1;  // row half of each sub-tile
+  // Transposed-read address of this lane: row 4 hi + (lane % 16) / 4 of a
+  // 16-row step, columns 16 ((lane / 16) % 2) + 4 (lane % 4) of a 32-column tile.
+  const int trow = 4 * hi + ((lane & 15) >> 2);
+  const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
   const int c = blockIdx.x % p.n_kv_blocks;
   const int bk = blockIdx.x / p.n_kv_blocks;  // b * Hkv + kv head
@@ -207,8 +236,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
   const int key0 = c * BK;
   const uint16_t* kg = static_cast<const uint16_t*>(p.k) + (int64_t)bk * p.Lkv * DQK;
   const uint16_t* vg = static_cast<const uint16_t*>(p.v) + (int64_t)bk * p.Lkv * DV;
-  load_tile<DQK, 256, true, false>(kg, key0, p.Lkv, Ks, nullptr, tid);
-  load_tile<DV, 256, true, false>(vg, key0, p.Lkv, Vs, nullptr, tid);
+  load_tile<DQK, 256>(kg, key0, p.Lkv, Ks, tid);
+  load_tile<DV, 256>(vg, key0, p.Lkv, Vs, tid);
 
   const bool has_seg = p.seg_q != nullptr;
   const int my_key = key0 + 32 * kh + l32;
@@ -223,82 +252,120 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
 
   const int x0 = p.col_ptr[c];
   const int x1 = p.col_ptr[c + 1];
-  for (int g = 0; g < p.group; ++g) {
-    const int head = b * p.Hq + kvh * p.group + g;
-    const uint16_t* qg = static_cast<const uint16_t*>(p.q) + (int64_t)head * p.L * DQK;
-    const uint16_t* og = static_cast<const uint16_t*>(p.dout) + (int64_t)head * p.L * DV;
-    const float* lse = p.lse + (int64_t)head * p.L;
-    const float* dl = p.delta + (int64_t)head * p.L;
-    const int32_t* sq = has_seg ? p.seg_q + (int64_t)b * p.L : nullptr;
-    for (int x = x0; x < x1; ++x) {
-      const int r = p.col_rows[x];
-      for (int sub = 0; sub < BQ / SUB; ++sub) {
-        const int row0 = r * BQ + sub * SUB;
-        if (row0 >= p.L) break;
-        // Sub-tiles whose positions allow no pair with this block are skipped.
-        const int pa = p.q_off + row0;
-        const int pz = pa + SUB - 1;
-        if (p.causal && pz < key0) continue;
-        if (p.window_left >= 0 && pa - (key0 + BK - 1) > p.window_left) continue;
-        if (p.window_right >= 0 && key0 - pz > p.window_right) continue;
-        __syncthreads();  // the previous sub-tile is consumed
-        load_tile<DQK, 256, true, true>(qg, row0, p.L, Qs, QT, tid);
-        load_tile<DV, 256, true, true>(og, row0, p.L, Os, OT, tid);
-        if (tid < SUB) {
-          const int qi = row0 + tid;
-          const bool in = qi < p.L;
-          lse2s[tid] = in ? lse[qi] * kLog2e : INFINITY;
-          Ds[tid] = in ? dl[qi] : 0.0f;
-          segqs[tid] = (has_seg && in) ? sq[qi] : 0;
-        }
-        __syncthreads();
+  const int32_t* sq = has_seg ? p.seg_q + (int64_t)b * p.L : nullptr;
+  // Cursor over the work-group's sub-tiles: query head cg of the group,
+  // entry cx of the column, sub-tile cs of that q block.  Sub-tiles whose
+  // positions allow no pair with this kv block are skipped.
+  int cg = 0, cx = x0, cs = 0;
+  auto next = [&](int* g_out, int* row0_out) __attribute__((always_inline)) -> bool {
+    while (cg < p.group) {
+      if (cx >= x1) {
+        ++cg;
+        cx = x0;
+        cs = 0;
+        continue;
+      }
+      if (cs >= BQ / SUB) {
+        ++cx;
+        cs = 0;
+        continue;
+      }
+      const int row0 = p.col_rows[cx] * BQ + cs * SUB;
+      ++cs;
+      if (row0 >= p.L) {
+        cs = BQ / SUB;
+        continue;
+      }
+      const int pa = p.q_off + row0;
+      const int pz = pa + SUB - 1;
+      if (p.causal && pz < key0) continue;
+      if (p.window_left >= 0 && pa - (key0 + BK - 1) > p.window_left) continue;
+      if (p.window_right >= 0 && key0 - pz > p.window_right) continue;
+      *g_out = cg;
+      *row0_out = row0;
+      return true;
+    }
+    return false;
+  };
+  // The next sub-tile's Q, dO, lse, D and segment ids are fetched into
+  // registers while the current one is computed.
+  TileRegs<DQK, 256> q_next;
+  TileRegs<DV, 256> o_next;
+  float lse_next = 0.0f, d_next = 0.0f;
+  int seg_next = 0;
+  auto fetch = [&](int g, int row0) __attribute__((always_inline)) {
+    const int64_t head = b * p.Hq + kvh * p.group + g;
+    q_next.fetch(static_cast<const uint16_t*>(p.q) + head * p.L * DQK, row0, p.L, tid);
+    o_next.fetch(static_cast<const uint16_t*>(p.dout) + head * p.L * DV, row0, p.L, tid);
+    if (tid < SUB) {
+      const int qi = row0 + tid;
+      const bool in = qi < p.L;
+      lse_next = in ? p.lse[head * p.L + qi] * kLog2e : INFINITY;
+      d_next = in ? p.delta[head * p.L + qi] : 0.0f;
+      seg_next = (has_seg && in) ? sq[qi] : 0;
+    }
+  };
+  int next_g = 0, next_row0 = 0;
+  bool have = next(&next_g, &next_row0);
+  if (have) fetch(next_g, next_row0);
+  while (have) {
+    const int row0 = next_row0;
+    __syncthreads();  // the previous sub-tile is consumed
+    q_next.store(Qs, tid);
+    o_next.store(Os, tid);
+    if (tid < SUB) {
+      lse2s[tid] = lse_next;
+      Ds[tid] = d_next;
+      segqs[tid] = seg_next;
+    }
+    __syncthreads();
+    have = next(&next_g, &next_row0);
+    if (have) fetch(next_g, next_row0);
 
-        // S = Q K^T and dP = dO V^T: rows 32 rh + items, key 32 kh + l32.
-        f32x16 s = f32x16{}, dp = f32x16{};
+    // S = Q K^T and dP = dO V^T: rows 32 rh + items, key 32 kh + l32.
+    f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-        for (int st = 0; st < DQK / 16; ++st)
-          s = mfma(ld_op(Qs + (32 * rh + l32) * RK + 16 * st + 8 * hi),
-                   ld_op(Ks + (32 * kh + l32) * RK + 16 * st + 8 * hi), s);
+    for (int st = 0; st < DQK / 16; ++st)
+      s = mfma(ld_op(Qs + (32 * rh + l32) * RK + 16 * st + 8 * hi),
+               ld_op(Ks + (32 * kh + l32) * RK + 16 * st + 8 * hi), s);
 #pragma unroll
-        for (int st = 0; st < DV / 16; ++st)
-          dp = mfma(ld_op(Os + (32 * rh + l32) * RV + 16 * st + 8 * hi),
-                    ld_op(Vs + (32 * kh + l32) * RV + 16 * st + 8 * hi), dp);
+    for (int st = 0; st < DV / 16; ++st)
+      dp = mfma(ld_op(Os + (32 * rh + l32) * RV + 16 * st + 8 * hi),
+                ld_op(Vs + (32 * kh + l32) * RV + 16 * st + 8 * hi), dp);
 
-        float pv[16], dsv[16];
+    float pv[16], dsv[16];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int rl = 32 * rh + 8 * (e / 4) + 4 * hi + (e % 4);
-          const bool ok = pair_ok(p, row0 + rl, my_key) & (!has_seg || segqs[rl] == kseg);
-          p_and_ds<CAP>(p, ok, s[e], lse2s[rl], dp[e], Ds[rl], &pv[e], &dsv[e]);
-        }
-        // dV += P^T dO, dK += dS^T Q over this wave's 32 rows (two k-steps).
+    for (int e = 0; e < 16; ++e) {
+      const int rl = 32 * rh + 8 * (e / 4) + 4 * hi + (e % 4);
+      const bool ok = pair_ok(p, row0 + rl, my_key) & (!has_seg || segqs[rl] == kseg);
+      p_and_ds<CAP>(p, ok, s[e], lse2s[rl], dp[e], Ds[rl], &pv[e], &dsv[e]);
+    }
+    // dV += P^T dO, dK += dS^T Q over this wave's 32 rows (two k-steps).
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          bf16x8 pa8, da8;
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 pa8, da8;
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            pa8[j] = (__bf16)pv[8 * ks + j];
-            da8[j] = (__bf16)dsv[8 * ks + j];
-          }
-          const int rr = 32 * rh + 16 * ks + 4 * hi;
+      for (int j = 0; j < 8; ++j) {
+        pa8[j] = (__bf16)pv[8 * ks + j];
+        da8[j] = (__bf16)dsv[8 * ks + j];
+      }
+      const int rr = 32 * rh + 16 * ks + trow;
 #pragma unroll
-          for (int et = 0; et < NV; ++et) {
-            const lds_u16* t = OT + (32 * et + l32) * TP + rr;
-            dvacc[et] = mfma(pa8, ld_op2(t, t + 8), dvacc[et]);
-          }
+      for (int et = 0; et < NV; ++et) {
+        const lds_u16* t = Os + rr * RV + 32 * et + tcol;
+        dvacc[et] = mfma(pa8, ld_tr(t, t + 8 * RV), dvacc[et]);
+      }
 #pragma unroll
-          for (int dt = 0; dt < NQ; ++dt) {
-            const lds_u16* t = QT + (32 * dt + l32) * TP + rr;
-            dkacc[dt] = mfma(da8, ld_op2(t, t + 8), dkacc[dt]);
-          }
-        }
+      for (int dt = 0; dt < NQ; ++dt) {
+        const lds_u16* t = Qs + rr * RK + 32 * dt + tcol;
+        dkacc[dt] = mfma(da8, ld_tr(t, t + 8 * RK), dkacc[dt]);
       }
     }
   }
 
   // Sum the two row halves: waves with rh = 1 park their sums in LDS.
   __syncthreads();
-  lds_f32* red = (lds_f32*)(lds + M::Q_OFF) + kh * (NQ + NV) * 16 * 64;
+  lds_f32* red = (lds_f32*)lds + kh * (NQ + NV) * 16 * 64;
   if (rh == 1) {
 #pragma unroll
     for (int t = 0; t < NQ; ++t)
@@ -334,8 +401,7 @@ struct DqLds {
   static constexpr int RV = rs<DV>();
   static constexpr int K_OFF = 0;                      // K [64][RK]
   static constexpr int V_OFF = K_OFF + 64 * RK * 2;    // V [64][RV]
-  static constexpr int KT_OFF = V_OFF + 64 * RV * 2;   // K^T [DQK][TP]
-  static constexpr int SEG_OFF = KT_OFF + DQK * TP * 2;  // key segment ids [64]
+  static constexpr int SEG_OFF = V_OFF + 64 * RV * 2;  // key segment ids [64]
   static constexpr int BYTES = SEG_OFF + 64 * 4;
   static_assert(BYTES <= 65536, "default LDS allocation");
 };
@@ -350,7 +416,6 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
   lds_u8* lds = (lds_u8*)smem;
   lds_u16* Ks = (lds_u16*)(lds + M::K_OFF);
   lds_u16* Vs = (lds_u16*)(lds + M::V_OFF);
-  lds_u16* KT = (lds_u16*)(lds + M::KT_OFF);
   lds_i32* segks = (lds_i32*)(lds + M::SEG_OFF);
 
   const int tid = threadIdx.x;
@@ -358,6 +423,8 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
+  const int trow = 4 * hi + ((lane & 15) >> 2);  // transposed-read address (see the dk/dv kernel)
+  const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
   const int r = blockIdx.x % p.n_q_blocks;
   const int head = blockIdx.x / p.n_q_blocks;  // b * Hq + h
@@ -398,13 +465,26 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
 
   const int x0 = p.row_ptr[r];
   const int x1 = p.row_ptr[r + 1];
+  // The next block's K, V and key segment ids are fetched into registers
+  // while the current one is computed.
+  TileRegs<DQK, 512> k_next;
+  TileRegs<DV, 512> v_next;
+  int seg_next = 0;
+  auto fetch = [&](int x) __attribute__((always_inline)) {
+    const int key0 = p.active_cols[x] * BK;
+    k_next.fetch(kg, key0, p.Lkv, tid);
+    v_next.fetch(vg, key0, p.Lkv, tid);
+    if (tid < BK) seg_next = (has_seg && key0 + tid < p.Lkv) ? segk[key0 + tid] : 0;
+  };
+  if (x0 < x1) fetch(x0);
   for (int x = x0; x < x1; ++x) {
     const int key0 = p.active_cols[x] * BK;
     __syncthreads();  // the previous block is consumed
-    load_tile<DQK, 512, true, true>(kg, key0, p.Lkv, Ks, KT, tid);
-    load_tile<DV, 512, true, false>(vg, key0, p.Lkv, Vs, nullptr, tid);
-    if (tid < BK) segks[tid] = (has_seg && key0 + tid < p.Lkv) ? segk[key0 + tid] : 0;
+    k_next.store(Ks, tid);
+    v_next.store(Vs, tid);
+    if (tid < BK) segks[tid] = seg_next;
     __syncthreads();
+    if (x + 1 < x1) fetch(x + 1);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       // S^T = K Q^T and dP^T = V dO^T: keys 32t + items, row l32.
@@ -428,11 +508,11 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
         bf16x8 da8;
 #pragma unroll
         for (int j = 0; j < 8; ++j) da8[j] = (__bf16)dsv[8 * ks + j];
-        const int kk = 32 * t + 16 * ks + 4 * hi;
+        const int kk = 32 * t + 16 * ks + trow;
 #pragma unroll
         for (int dt = 0; dt < NQ; ++dt) {
-          const lds_u16* tp = KT + (32 * dt + l32) * TP + kk;
-          dqacc[dt] = mfma(da8, ld_op2(tp, tp + 8), dqacc[dt]);
+          const lds_u16* tp = Ks + kk * RK + 32 * dt + tcol;
+          dqacc[dt] = mfma(da8, ld_tr(tp, tp + 8 * RK), dqacc[dt]);
         }
       }
     }
