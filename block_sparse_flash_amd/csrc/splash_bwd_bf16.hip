@@ -89,6 +89,29 @@ __device__ __forceinline__ bf16x8 ld_tr(const lds_u16* lo, const lds_u16* hi) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// Work-group w -> (unit, index inside the unit) for n_units units of n_per
+// items each.  Consecutive work-group ids go round-robin over the 8 XCDs;
+// when the unit count divides over them, all items of a unit (one head's
+// blocks, which read the same Q/dO or K/V) run on one XCD and share its L2;
+// with fewer units than XCDs (a divisor of 8), each unit gets 8 / n_units
+// XCDs of its own.
+__device__ __forceinline__ void xcd_map(int w, int n_units, int n_per, int* unit, int* idx) {
+  const int xcd = w % kNumXcd;
+  const int slot = w / kNumXcd;
+  if (n_units % kNumXcd == 0) {
+    const int u = slot / n_per;
+    *unit = u * kNumXcd + xcd;
+    *idx = slot - u * n_per;
+  } else if (kNumXcd % n_units == 0 && (n_units * n_per) % kNumXcd == 0) {
+    const int share = kNumXcd / n_units;  // XCDs per unit
+    *unit = xcd % n_units;
+    *idx = slot * share + xcd / n_units;
+  } else {
+    *unit = w / n_per;
+    *idx = w - *unit * n_per;
+  }
+}
+
 // Whether query row qi may attend key `key` by position (segments apart).
 __device__ __forceinline__ bool pair_ok(const BwdParams& p, int qi, int key) {
   const int pos = p.q_off + qi;
@@ -229,8 +252,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
   const int trow = 4 * hi + ((lane & 15) >> 2);
   const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
-  const int c = blockIdx.x % p.n_kv_blocks;
-  const int bk = blockIdx.x / p.n_kv_blocks;  // b * Hkv + kv head
+  int c, bk;  // kv block, b * Hkv + kv head
+  xcd_map(blockIdx.x, p.B * p.Hkv, p.n_kv_blocks, &bk, &c);
   const int b = bk / p.Hkv;
   const int kvh = bk - b * p.Hkv;
   const int key0 = c * BK;
@@ -426,8 +449,8 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
   const int trow = 4 * hi + ((lane & 15) >> 2);  // transposed-read address (see the dk/dv kernel)
   const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
-  const int r = blockIdx.x % p.n_q_blocks;
-  const int head = blockIdx.x / p.n_q_blocks;  // b * Hq + h
+  int r, head;  // q block, b * Hq + h
+  xcd_map(blockIdx.x, p.B * p.Hq, p.n_q_blocks, &head, &r);
   const int b = head / p.Hq;
   const int h = head - b * p.Hq;
   const int bk = b * p.Hkv + h / p.group;
