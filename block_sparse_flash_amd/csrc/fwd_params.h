@@ -15,9 +15,15 @@ struct FwdParams {
   int32_t B, Hq, Hkv, L, group;  // L: query rows; group = Hq / Hkv
   int32_t Lkv;            // key/value positions
   int32_t q_off;          // query row i sits at key position q_off + i
+  // Packed GQA rows: when row_period > 0 the query heads of a K/V group are
+  // packed into one row space (Hq, L above are then Hkv and group * L):
+  // row R is row R % row_period of query head R / row_period, at key
+  // position q_off + R % row_period, and every row uses table row 0.
+  int32_t row_period;
+  int32_t Lseg;           // rows per batch element of seg_q
   // mask
   int32_t causal, window_left, window_right;
-  const int32_t* seg_q;   // [B, L] or null
+  const int32_t* seg_q;   // [B, Lseg] or null
   const int32_t* seg_kv;  // [B, Lkv] or null (then seg_q is used, Lkv = L)
   int32_t mask_stored;    // 1: partial blocks read patterns
   // tables

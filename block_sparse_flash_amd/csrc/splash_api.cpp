@@ -174,7 +174,21 @@ int prepare(const splash_fwd_args* args, const char* fn, splash::FwdParams* out)
   p.n_split = 1;
   p.ws_o = nullptr;
   p.ws_lse = nullptr;
-  choose_xcd_units(a, &p);
+  p.row_period = 0;
+  p.Lseg = a.L;
+  splash_fwd_args placed = a;
+  if (a.dtype == SPLASH_BF16 && p.group > 1 && a.L < bq) {
+    // All query rows fit one table row: pack the query heads of each K/V
+    // group into one row space ([B, Hq, L, d] is [B, Hkv, group L, d]), so
+    // that an item's row tile holds group * L rows instead of L.
+    p.row_period = a.L;
+    p.L = p.group * a.L;
+    p.Hq = a.Hkv;
+    p.group = 1;
+    p.n_q_blocks = static_cast<int32_t>((static_cast<int64_t>(p.L) + bq - 1) / bq);
+    placed.Hq = a.Hkv;
+  }
+  choose_xcd_units(placed, &p);
   *out = p;
   return SPLASH_OK;
 }

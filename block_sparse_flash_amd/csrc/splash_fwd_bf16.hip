@@ -237,7 +237,7 @@ __device__ __forceinline__ void lds_barrier() {
 // One item: the 256 query rows of q-block row r of query head `head`
 // (flattened b * Hq + h), over chunk `split` of the row's active kv blocks
 // (the whole row when there is no split).
-template <int DQK, int DV, bool CAP, bool SPLIT>
+template <int DQK, int DV, bool CAP, bool SPLIT, bool PACK>
 __device__ __forceinline__ void item_fwd(const FwdParams& p, int head, int r, int split) {
   using C = Cfg<DQK, DV>;
   constexpr int KS = C::KS;
@@ -261,7 +261,10 @@ __device__ __forceinline__ void item_fwd(const FwdParams& p, int head, int r, in
   const int Lk = p.Lkv;   // key positions
   const int qw = r * BM + wave * 32;  // first query row of this wave
   const int qi = qw + l32;            // this lane's query row
-  const int qp = p.q_off + qi;        // its key position (causal, window)
+  // Position of the row inside its query head (packed GQA rows repeat with
+  // the period) and its key position for the causal and window tests.
+  const int qrow = PACK ? qi % p.row_period : qi;
+  const int qp = p.q_off + qrow;
 
   const uint16_t* qg = static_cast<const uint16_t*>(p.q) + (int64_t)head * L * DQK;
   const uint16_t* kg = static_cast<const uint16_t*>(p.k) + (int64_t)kvh * Lk * DQK;
@@ -304,22 +307,24 @@ __device__ __forceinline__ void item_fwd(const FwdParams& p, int head, int r, in
   sfor<0, DT>([&](auto i_) { oacc[SIDX(i_)] = f32x16{}; });
 
   const bool has_seg = p.seg_q != nullptr;
-  const int32_t* segq = has_seg ? p.seg_q + (int64_t)b * L : nullptr;
+  const int32_t* segq = has_seg ? p.seg_q + (int64_t)b * (PACK ? p.Lseg : L) : nullptr;
   const int32_t* segk = has_seg ? (p.seg_kv ? p.seg_kv + (int64_t)b * Lk : segq) : nullptr;
-  const int my_seg = (has_seg && qi < L) ? segq[qi] : 0;
+  const int my_seg = (has_seg && qi < L) ? segq[qrow] : 0;
   // Allowed key interval of this lane's row before the segment test.
   int klo = 0, khi = Lk - 1;
   if (p.causal) khi = min(khi, qp);
   if (p.window_left >= 0) klo = max(klo, qp - p.window_left);
   if (p.window_right >= 0) khi = min(khi, qp + p.window_right);
-  // Key positions of this wave's first and last valid query rows.
-  const int qa = p.q_off + qw;
-  const int qb = p.q_off + min(qw + 31, L - 1);
+  // Key positions bounding this wave's valid query rows (packed rows: the
+  // whole period).
+  const int qa = p.q_off + (PACK ? 0 : qw);
+  const int qb = p.q_off + (PACK ? p.row_period - 1 : min(qw + 31, L - 1));
 
   // Blocks [row_ptr[r] + lo, row_ptr[r] + hi) of the active list: chunk
   // `split` of n_split near-equal contiguous chunks.
-  const int row0 = ld_table(p.row_ptr, r);
-  const int n_row = ld_table(p.row_ptr, r + 1) - row0;
+  const int tab_r = PACK ? 0 : r;  // table row of these query rows
+  const int row0 = ld_table(p.row_ptr, tab_r);
+  const int n_row = ld_table(p.row_ptr, tab_r + 1) - row0;
   const int lo = SPLIT ? (int)(((int64_t)n_row * split) / p.n_split) : 0;
   const int hi_blk = SPLIT ? (int)(((int64_t)n_row * (split + 1)) / p.n_split) : n_row;
   const int g0 = row0 + lo;
@@ -342,8 +347,10 @@ __device__ __forceinline__ void item_fwd(const FwdParams& p, int head, int r, in
     const int ka = c * BN;
     const int kz = ka + BN - 1;
     if (p.mask_stored) {
+      // Pattern row = the row inside the table's q block (packed rows: the
+      // row inside its query head, all of them in table row 0).
       const uint8_t* prow = p.patterns + (int64_t)ld_table(p.mask_next, g0 + g) * (BM * BN) +
-                            (wave * 32 + l32) * BN;
+                            (PACK ? qrow : wave * 32 + l32) * BN;
       sfor<0, 8>([&](auto i_) {
         constexpr int t = SIDX(i_) / 4;
         constexpr int q4 = SIDX(i_) % 4;
@@ -830,7 +837,7 @@ __device__ __forceinline__ int item_of_round(int k, int w, int G, bool snake) {
   return k * G + w;
 }
 
-template <int DQK, int DV, bool CAP, bool SPLIT>
+template <int DQK, int DV, bool CAP, bool SPLIT, bool PACK>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void splash_fwd_bf16_kernel(FwdParams p) {
   const int w = blockIdx.x;
@@ -846,7 +853,7 @@ void splash_fwd_bf16_kernel(FwdParams p) {
     const int split = SPLIT ? t / T0 : 0;
     int head, rank;
     map_workgroup(p, t - split * T0, &head, &rank);
-    item_fwd<DQK, DV, CAP, SPLIT>(p, head, ld_table(p.row_order, rank), split);
+    item_fwd<DQK, DV, CAP, SPLIT, PACK>(p, head, PACK ? rank : ld_table(p.row_order, rank), split);
   }
 }
 
@@ -855,13 +862,13 @@ void splash_fwd_bf16_kernel(FwdParams p) {
 // balanced; with segment ids, rows mix partial and full blocks unevenly and
 // the hardware's dynamic dispatch of one work-group per item balances better
 // (a grid of one work-group per item is the same kernel with one round).
-template <int DQK, int DV, bool CAP, bool SPLIT>
+template <int DQK, int DV, bool CAP, bool SPLIT, bool PACK>
 hipError_t launch(const FwdParams& p, int n_cu, hipStream_t s) {
   const int64_t n_items = (int64_t)p.B * p.Hq * p.n_q_blocks * (SPLIT ? p.n_split : 1);
   const bool persistent = p.seg_q == nullptr;
   const int64_t grid = (persistent && n_items > n_cu) ? n_cu : n_items;
   const int bytes = Cfg<DQK, DV>::LDS_BYTES;
-  auto fn = splash_fwd_bf16_kernel<DQK, DV, CAP, SPLIT>;
+  auto fn = splash_fwd_bf16_kernel<DQK, DV, CAP, SPLIT, PACK>;
   if (bytes > 65536) {
     // Opt in to more than 64 KiB of dynamic LDS (gfx950 has 160 KiB per CU).
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
@@ -872,11 +879,20 @@ hipError_t launch(const FwdParams& p, int n_cu, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int DQK, int DV>
+template <int DQK, int DV, bool PACK>
 hipError_t launch_cap(const FwdParams& p, int n_cu, hipStream_t s) {
   if (p.ws_o)
-    return p.soft_cap > 0.0f ? launch<DQK, DV, true, true>(p, n_cu, s) : launch<DQK, DV, false, true>(p, n_cu, s);
-  return p.soft_cap > 0.0f ? launch<DQK, DV, true, false>(p, n_cu, s) : launch<DQK, DV, false, false>(p, n_cu, s);
+    return p.soft_cap > 0.0f ? launch<DQK, DV, true, true, PACK>(p, n_cu, s)
+                             : launch<DQK, DV, false, true, PACK>(p, n_cu, s);
+  return p.soft_cap > 0.0f ? launch<DQK, DV, true, false, PACK>(p, n_cu, s)
+                           : launch<DQK, DV, false, false, PACK>(p, n_cu, s);
+}
+
+// Packed GQA rows (row_period > 0) use their own instances, so that the
+// unpacked kernels keep their registers.
+template <int DQK, int DV>
+hipError_t launch_pack(const FwdParams& p, int n_cu, hipStream_t s) {
+  return p.row_period > 0 ? launch_cap<DQK, DV, true>(p, n_cu, s) : launch_cap<DQK, DV, false>(p, n_cu, s);
 }
 
 // Compute units of the current device (cached per device; concurrent first
@@ -897,12 +913,12 @@ int device_cus() {
 
 hipError_t launch_fwd_bf16(const FwdParams& p, int d_qk, int d_v, hipStream_t s) {
   const int n_cu = device_cus();
-  if (d_qk == 128 && d_v == 128) return launch_cap<128, 128>(p, n_cu, s);
-  if (d_qk == 192 && d_v == 128) return launch_cap<192, 128>(p, n_cu, s);
-  if (d_qk == 64 && d_v == 64) return launch_cap<64, 64>(p, n_cu, s);
-  if (d_qk == 128 && d_v == 64) return launch_cap<128, 64>(p, n_cu, s);
-  if (d_qk == 64 && d_v == 128) return launch_cap<64, 128>(p, n_cu, s);
-  if (d_qk == 192 && d_v == 64) return launch_cap<192, 64>(p, n_cu, s);
+  if (d_qk == 128 && d_v == 128) return launch_pack<128, 128>(p, n_cu, s);
+  if (d_qk == 192 && d_v == 128) return launch_pack<192, 128>(p, n_cu, s);
+  if (d_qk == 64 && d_v == 64) return launch_pack<64, 64>(p, n_cu, s);
+  if (d_qk == 128 && d_v == 64) return launch_pack<128, 64>(p, n_cu, s);
+  if (d_qk == 64 && d_v == 128) return launch_pack<64, 128>(p, n_cu, s);
+  if (d_qk == 192 && d_v == 64) return launch_pack<192, 64>(p, n_cu, s);
   return hipErrorInvalidValue;
 }
 

@@ -94,7 +94,7 @@ EXTRA_WORKLOADS = {
     # the last 16 positions; split-KV into 16 chunks per row.
     "decode_gqa_bf16_Lq16_Lkv32768": Workload(
         "decode_gqa_bf16_Lq16_Lkv32768", "bf16", 8, 32, 8, 16, 128, 128,
-        causal=True, seed=7, L_kv=32768, q_offset=32768 - 16, n_split=16),
+        causal=True, seed=7, L_kv=32768, q_offset=32768 - 16, n_split=4),
 }
 ALL_WORKLOADS = {**WORKLOADS, **EXTRA_WORKLOADS}
 

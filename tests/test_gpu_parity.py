@@ -64,6 +64,10 @@ SMALL = [
     ("bf16", 1, 3, 1, 450, 128, 64, dict(segs=(10, 200)), 0.0, "computed"),
     ("bf16", 1, 2, 2, 130, 64, 128, dict(causal=True), 0.0, "computed"),
     ("bf16", 1, 2, 2, 96, 192, 64, dict(causal=True, window_left=5), 0.0, "computed"),
+    # GQA with fewer than 256 rows: the query heads of a group share a row tile
+    ("bf16", 2, 8, 2, 100, 128, 128, dict(causal=True, segs=(10, 40)), 0.0, "computed"),
+    ("bf16", 1, 8, 2, 200, 64, 64, dict(window_left=30), 2.0, "stored"),
+    ("bf16", 1, 6, 1, 50, 192, 128, dict(causal=True), 0.0, "computed"),
 ]
 
 
