@@ -56,6 +56,10 @@ typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 typedef __attribute__((address_space(3))) float lds_f32;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+typedef __attribute__((address_space(3))) i32x4 lds_i32x4;
 typedef __attribute__((address_space(3))) int32_t lds_i32;
 
 constexpr int BQ = kBf16BlockQ;   // rows per q block of the tables
@@ -112,14 +116,14 @@ __device__ __forceinline__ void xcd_map(int w, int n_units, int n_per, int* unit
   }
 }
 
-// Whether query row qi may attend key `key` by position (segments apart).
-__device__ __forceinline__ bool pair_ok(const BwdParams& p, int qi, int key) {
-  const int pos = p.q_off + qi;
-  bool ok = (qi < p.L) & (key < p.Lkv);
-  if (p.causal) ok = ok & (key <= pos);
-  if (p.window_left >= 0) ok = ok & (pos - key <= p.window_left);
-  if (p.window_right >= 0) ok = ok & (key - pos <= p.window_right);
-  return ok;
+// Whether every pair of query rows [r0, r0 + nr) and keys [k0, k0 + nk) is
+// allowed (no segment ids): then no element mask is needed.
+__device__ __forceinline__ bool all_allowed(const BwdParams& p, int r0, int nr, int k0, int nk) {
+  const int pa = p.q_off + r0;  // smallest row position
+  const int pz = pa + nr - 1;   // largest
+  const int kz = k0 + nk - 1;   // largest key
+  return p.seg_q == nullptr && r0 + nr <= p.L && kz < p.Lkv && (!p.causal || kz <= pa) &&
+         (p.window_left < 0 || pz - k0 <= p.window_left) && (p.window_right < 0 || kz - pa <= p.window_right);
 }
 
 // Copies rows row0 .. row0 + 63 of a row-major [n_valid, D] bf16 matrix
@@ -266,6 +270,12 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
   const int my_key = key0 + 32 * kh + l32;
   const int32_t* segk = has_seg ? (p.seg_kv ? p.seg_kv + (int64_t)b * p.Lkv : p.seg_q + (int64_t)b * p.L) : nullptr;
   const int kseg = (has_seg && my_key < p.Lkv) ? segk[my_key] : 0;
+  // Rows allowed to see this lane's key by position: causal pos >= key,
+  // window pos - key <= left and key - pos <= right, pos = q_off + row.
+  int rlo = 0, rhi = my_key < p.Lkv ? p.L - 1 : -1;
+  if (p.causal) rlo = max(rlo, my_key - p.q_off);
+  if (p.window_right >= 0) rlo = max(rlo, my_key - p.window_right - p.q_off);
+  if (p.window_left >= 0) rhi = min(rhi, my_key + p.window_left - p.q_off);
 
   f32x16 dkacc[NQ], dvacc[NV];
 #pragma unroll
@@ -356,12 +366,27 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
       dp = mfma(ld_op(Os + (32 * rh + l32) * RV + 16 * st + 8 * hi),
                 ld_op(Vs + (32 * kh + l32) * RV + 16 * st + 8 * hi), dp);
 
+    // Row data of the 16 rows 32 rh + 8 (e / 4) + 4 hi + e % 4 (four runs of 4).
     float pv[16], dsv[16];
+    const bool all_ok = all_allowed(p, row0 + 32 * rh, 32, key0 + 32 * kh, 32);  // wave-uniform
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int rl = 32 * rh + 8 * (e / 4) + 4 * hi + (e % 4);
-      const bool ok = pair_ok(p, row0 + rl, my_key) & (!has_seg || segqs[rl] == kseg);
-      p_and_ds<CAP>(p, ok, s[e], lse2s[rl], dp[e], Ds[rl], &pv[e], &dsv[e]);
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int rl0 = 32 * rh + 8 * q4 + 4 * hi;
+      const f32x4 l4 = *reinterpret_cast<const lds_f32x4*>(lse2s + rl0);
+      const f32x4 d4 = *reinterpret_cast<const lds_f32x4*>(Ds + rl0);
+      if (all_ok) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          p_and_ds<CAP>(p, true, s[4 * q4 + j], l4[j], dp[4 * q4 + j], d4[j], &pv[4 * q4 + j], &dsv[4 * q4 + j]);
+      } else {
+        const i32x4 s4 = *reinterpret_cast<const lds_i32x4*>(segqs + rl0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int row = row0 + rl0 + j;
+          const bool ok = (row >= rlo) & (row <= rhi) & (!has_seg || s4[j] == kseg);
+          p_and_ds<CAP>(p, ok, s[4 * q4 + j], l4[j], dp[4 * q4 + j], d4[j], &pv[4 * q4 + j], &dsv[4 * q4 + j]);
+        }
+      }
     }
     // dV += P^T dO, dK += dS^T Q over this wave's 32 rows (two k-steps).
 #pragma unroll
@@ -481,6 +506,12 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
   const bool has_seg = p.seg_q != nullptr;
   const int qseg = (has_seg && in) ? p.seg_q[(int64_t)b * p.L + qi] : 0;
   const int32_t* segk = has_seg ? (p.seg_kv ? p.seg_kv + (int64_t)b * p.Lkv : p.seg_q + (int64_t)b * p.L) : nullptr;
+  // Keys allowed to this lane's row by position (before segment ids).
+  const int qpos = p.q_off + qi;
+  int klo = 0, khi = in ? p.Lkv - 1 : -1;
+  if (p.causal) khi = min(khi, qpos);
+  if (p.window_left >= 0) klo = max(klo, qpos - p.window_left);
+  if (p.window_right >= 0) khi = min(khi, qpos + p.window_right);
 
   f32x16 dqacc[NQ];
 #pragma unroll
@@ -522,7 +553,8 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int kl = 32 * t + 8 * (e / 4) + 4 * hi + (e % 4);
-        const bool ok = pair_ok(p, qi, key0 + kl) & (!has_seg || segks[kl] == qseg);
+        const int key = key0 + kl;
+        const bool ok = (key >= klo) & (key <= khi) & (!has_seg || segks[kl] == qseg);
         p_and_ds<CAP>(p, ok, s[e], lse2, dp[e], dlt, &pv[e], &dsv[e]);
       }
       // dQ += dS K over this tile's 32 keys (two k-steps).

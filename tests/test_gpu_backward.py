@@ -109,3 +109,27 @@ def test_backward_deterministic():
     torch.cuda.synchronize()
     for a, b in zip(g1, g2):
         assert torch.equal(a, b)
+
+
+def test_backward_full_size_sampled_heads():
+    """The bench's backward workload (dense causal L=4096, B=2, Hq=Hkv=32,
+    d=128) at full size: every gradient element of three heads against the
+    oracle (with Hq = Hkv a head's dq, dk and dv depend on that head only)."""
+    from block_sparse_flash_amd.inputs import ALL_WORKLOADS, make_inputs
+    w = ALL_WORKLOADS["causal_mha_bf16_L4096_d128"]
+    _announce(f"backward full size {w.name}")
+    q, k, v, _ = make_inputs(w)
+    g = torch.Generator().manual_seed(w.seed + 1)
+    do = torch.randn((w.B, w.Hq, w.L, w.d_v), generator=g).to(torch.bfloat16)
+    qd, kd, vd, dod = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    o, lse = splash_fwd(qd, kd, vd, causal=True)
+    dq, dk, dv = splash_bwd(qd, kd, vd, o, lse, dod, causal=True)
+    torch.cuda.synchronize()
+    for b, h in [(0, 0), (1, 17), (1, 31)]:
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        rdq, rdk, rdv = attention_bwd_ref(as_f64(q[sl]), as_f64(k[sl]), as_f64(v[sl]), as_f64(do[sl]),
+                                          scale=w.softmax_scale, causal=True)
+        e = (_check("dq", dq[sl], rdq), _check("dk", dk[sl], rdk), _check("dv", dv[sl], rdv))
+        _announce(f"  head ({b}, {h}): relative max-abs errors dq {e[0]:.3g} dk {e[1]:.3g} dv {e[2]:.3g}")
+    for t in (dq, dk, dv):
+        assert bool(torch.isfinite(t).all())
