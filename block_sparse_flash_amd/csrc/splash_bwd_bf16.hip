@@ -116,6 +116,32 @@ __device__ __forceinline__ void xcd_map(int w, int n_units, int n_per, int* unit
   }
 }
 
+// Runs N unrolled steps: step i's operands are loaded by ld(i) DIST steps
+// before use(i, operands) consumes them, with scheduling fences so that the
+// compiler keeps the loads that far ahead (left alone it moves every LDS
+// read to just before its MFMA, which then waits out the LDS latency).
+template <int N, int DIST, typename Ld, typename Use>
+__device__ __forceinline__ void pipelined(Ld ld, Use use) {
+  using Op = decltype(ld(0));
+  Op buf[DIST + 1];
+#pragma unroll
+  for (int i = 0; i < DIST && i < N; ++i) buf[i] = ld(i);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    if (i + DIST < N) buf[(i + DIST) % (DIST + 1)] = ld(i + DIST);
+    __builtin_amdgcn_sched_barrier(0);
+    use(i, buf[i % (DIST + 1)]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+struct Op2 {
+  bf16x8 a, b;
+};
+struct Op4 {
+  bf16x8 a, b, c, d;
+};
+
 // Whether every pair of query rows [r0, r0 + nr) and keys [k0, k0 + nk) is
 // allowed (no segment ids): then no element mask is needed.
 __device__ __forceinline__ bool all_allowed(const BwdParams& p, int r0, int nr, int k0, int nk) {
@@ -355,16 +381,21 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
     have = next(&next_g, &next_row0);
     if (have) fetch(next_g, next_row0);
 
-    // S = Q K^T and dP = dO V^T: rows 32 rh + items, key 32 kh + l32.
+    // S = Q K^T and dP = dO V^T (two interleaved accumulation chains): rows
+    // 32 rh + items, key 32 kh + l32.
     f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-    for (int st = 0; st < DQK / 16; ++st)
-      s = mfma(ld_op(Qs + (32 * rh + l32) * RK + 16 * st + 8 * hi),
-               ld_op(Ks + (32 * kh + l32) * RK + 16 * st + 8 * hi), s);
-#pragma unroll
-    for (int st = 0; st < DV / 16; ++st)
-      dp = mfma(ld_op(Os + (32 * rh + l32) * RV + 16 * st + 8 * hi),
-                ld_op(Vs + (32 * kh + l32) * RV + 16 * st + 8 * hi), dp);
+    static_assert(DQK == DV, "S and dP take the same number of k-steps");
+    pipelined<DQK / 16, 2>(
+        [&](int st) {
+          return Op4{ld_op(Qs + (32 * rh + l32) * RK + 16 * st + 8 * hi),
+                     ld_op(Ks + (32 * kh + l32) * RK + 16 * st + 8 * hi),
+                     ld_op(Os + (32 * rh + l32) * RV + 16 * st + 8 * hi),
+                     ld_op(Vs + (32 * kh + l32) * RV + 16 * st + 8 * hi)};
+        },
+        [&](int, const Op4& o) {
+          s = mfma(o.a, o.b, s);
+          dp = mfma(o.c, o.d, dp);
+        });
 
     // Row data of the 16 rows 32 rh + 8 (e / 4) + 4 hi + e % 4 (four runs of 4).
     float pv[16], dsv[16];
@@ -388,27 +419,30 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
         }
       }
     }
-    // dV += P^T dO, dK += dS^T Q over this wave's 32 rows (two k-steps).
+    // dV += P^T dO, dK += dS^T Q over this wave's 32 rows: two k-steps
+    // (ks) of NV dV tiles and NQ dK tiles each.
+    bf16x8 pa8[2], da8[2];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bf16x8 pa8, da8;
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        pa8[j] = (__bf16)pv[8 * ks + j];
-        da8[j] = (__bf16)dsv[8 * ks + j];
+        pa8[ks][j] = (__bf16)pv[8 * ks + j];
+        da8[ks][j] = (__bf16)dsv[8 * ks + j];
       }
-      const int rr = 32 * rh + 16 * ks + trow;
-#pragma unroll
-      for (int et = 0; et < NV; ++et) {
-        const lds_u16* t = Os + rr * RV + 32 * et + tcol;
-        dvacc[et] = mfma(pa8, ld_tr(t, t + 8 * RV), dvacc[et]);
-      }
-#pragma unroll
-      for (int dt = 0; dt < NQ; ++dt) {
-        const lds_u16* t = Qs + rr * RK + 32 * dt + tcol;
-        dkacc[dt] = mfma(da8, ld_tr(t, t + 8 * RK), dkacc[dt]);
-      }
-    }
+    pipelined<2 * (NV + NQ), 4>(
+        [&](int i) {
+          const int ks = i / (NV + NQ), j = i % (NV + NQ);
+          const int rr = 32 * rh + 16 * ks + trow;
+          const lds_u16* t = j < NV ? Os + rr * RV + 32 * j + tcol : Qs + rr * RK + 32 * (j - NV) + tcol;
+          return ld_tr(t, t + 8 * (j < NV ? RV : RK));
+        },
+        [&](int i, const bf16x8& b) {
+          const int ks = i / (NV + NQ), j = i % (NV + NQ);
+          if (j < NV)
+            dvacc[j] = mfma(pa8[ks], b, dvacc[j]);
+          else
+            dkacc[j - NV] = mfma(da8[ks], b, dkacc[j - NV]);
+        });
   }
 
   // Sum the two row halves: waves with rh = 1 park their sums in LDS.
@@ -541,14 +575,18 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
     if (x + 1 < x1) fetch(x + 1);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      // S^T = K Q^T and dP^T = V dO^T: keys 32t + items, row l32.
+      // S^T = K Q^T and dP^T = V dO^T (interleaved chains): keys 32t + items, row l32.
       f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-      for (int st = 0; st < DQK / 16; ++st)
-        s = mfma(ld_op(Ks + (32 * t + l32) * RK + 16 * st + 8 * hi), qf[st], s);
-#pragma unroll
-      for (int st = 0; st < DV / 16; ++st)
-        dp = mfma(ld_op(Vs + (32 * t + l32) * RV + 16 * st + 8 * hi), df[st], dp);
+      static_assert(DQK == DV, "S and dP take the same number of k-steps");
+      pipelined<DQK / 16, 1>(
+          [&](int st) {
+            return Op2{ld_op(Ks + (32 * t + l32) * RK + 16 * st + 8 * hi),
+                       ld_op(Vs + (32 * t + l32) * RV + 16 * st + 8 * hi)};
+          },
+          [&](int st, const Op2& o) {
+            s = mfma(o.a, qf[st], s);
+            dp = mfma(o.b, df[st], dp);
+          });
       float pv[16], dsv[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
@@ -557,18 +595,18 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
         const bool ok = (key >= klo) & (key <= khi) & (!has_seg || segks[kl] == qseg);
         p_and_ds<CAP>(p, ok, s[e], lse2, dp[e], dlt, &pv[e], &dsv[e]);
       }
-      // dQ += dS K over this tile's 32 keys (two k-steps).
+      // dQ += dS K over this tile's 32 keys: two k-steps of NQ tiles.
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         bf16x8 da8;
 #pragma unroll
         for (int j = 0; j < 8; ++j) da8[j] = (__bf16)dsv[8 * ks + j];
-        const int kk = 32 * t + 16 * ks + trow;
-#pragma unroll
-        for (int dt = 0; dt < NQ; ++dt) {
-          const lds_u16* tp = Ks + kk * RK + 32 * dt + tcol;
-          dqacc[dt] = mfma(da8, ld_tr(tp, tp + 8 * RK), dqacc[dt]);
-        }
+        pipelined<NQ, 2>(
+            [&](int dt) {
+              const lds_u16* tp = Ks + (32 * t + 16 * ks + trow) * RK + 32 * dt + tcol;
+              return ld_tr(tp, tp + 8 * RK);
+            },
+            [&](int dt, const bf16x8& b) { dqacc[dt] = mfma(da8, b, dqacc[dt]); });
       }
     }
   }
