@@ -67,9 +67,28 @@ constexpr int BK = kBf16BlockKV;  // keys per kv block of the tables
 constexpr int SUB = 64;           // rows per sub-tile in the dk/dv kernel
 constexpr float kLog2e = 1.4426950408889634f;
 
-// Row stride (elements) of a row-major tile with D columns.
-template <int D>
-constexpr int rs() { return D + 8; }
+// LDS layout of a row-major tile with D bf16 columns, in 16-byte chunks.
+// Two reads must be bank-conflict free: an operand read, where 16 lanes
+// take one chunk of 16 consecutive rows, and a transposing read, where 32
+// lanes take 64 bytes of each of 4 consecutive rows.  With 256-byte rows
+// (D = 128) chunk c of row r is stored at chunk c ^ 4 (r % 4) ^ (r / 4) % 4:
+// 16 consecutive rows get 16 distinct chunks, and 4 consecutive rows put
+// each 64-byte group into a different quarter of the banks.  Other tiles
+// (and kernels that cannot spare the registers for the address arithmetic)
+// pad each row by 16 bytes instead.
+template <int D, bool SWIZZLE>
+struct Lay {
+  static constexpr bool SWZ = SWIZZLE && D == 128;
+  static constexpr int ROW = SWZ ? D : D + 8;  // elements per row
+  // Element offset of chunk c of row r.
+  __device__ static __forceinline__ int off(int r, int c) {
+    return r * ROW + 8 * (SWZ ? (c ^ ((r & 3) << 2) ^ ((r >> 2) & 3)) : c);
+  }
+  // Element offset of element `col` of row r (col % 8 stays in its chunk).
+  __device__ static __forceinline__ int at(int r, int col) {
+    return SWZ ? off(r, col >> 3) + (col & 7) : r * ROW + col;
+  }
+};
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -153,8 +172,8 @@ __device__ __forceinline__ bool all_allowed(const BwdParams& p, int r0, int nr, 
 }
 
 // Copies rows row0 .. row0 + 63 of a row-major [n_valid, D] bf16 matrix
-// into LDS (zeros past n_valid), row-major with stride rs<D>().
-template <int D, int NTHR>
+// into LDS (zeros past n_valid), laid out by Lay<D, SWZ>.
+template <int D, int NTHR, bool SWZ>
 __device__ __forceinline__ void load_tile(const uint16_t* g, int row0, int n_valid, lds_u16* rm, int tid) {
   constexpr int CH = D / 8;
   constexpr int TOTAL = 64 * CH;
@@ -166,14 +185,14 @@ __device__ __forceinline__ void load_tile(const uint16_t* g, int row0, int n_val
     const int c = x - r * CH;
     u32x4 val = {0u, 0u, 0u, 0u};
     if (row0 + r < n_valid) val = *reinterpret_cast<const u32x4*>(g + (int64_t)(row0 + r) * D + c * 8);
-    *reinterpret_cast<lds_u32x4*>(rm + r * rs<D>() + c * 8) = val;
+    *reinterpret_cast<lds_u32x4*>(rm + Lay<D, SWZ>::off(r, c)) = val;
   }
 }
 
 // Rows row0 .. row0 + 63 of a row-major [n_valid, D] bf16 matrix staged in
 // registers (zeros past n_valid): fetched from global memory while the
 // previous tile is being used, stored to LDS after the next barrier.
-template <int D, int NTHR>
+template <int D, int NTHR, bool SWZ>
 struct TileRegs {
   static constexpr int CH = D / 8;
   static constexpr int N = 64 * CH / NTHR;
@@ -195,7 +214,7 @@ struct TileRegs {
       const int x = it * NTHR + tid;
       const int r = x / CH;
       const int c = x - r * CH;
-      *reinterpret_cast<lds_u32x4*>(rm + r * rs<D>() + c * 8) = v[it];
+      *reinterpret_cast<lds_u32x4*>(rm + Lay<D, SWZ>::off(r, c)) = v[it];
     }
   }
 };
@@ -238,8 +257,8 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
 
 template <int DQK, int DV>
 struct DkdvLds {
-  static constexpr int RK = rs<DQK>();
-  static constexpr int RV = rs<DV>();
+  static constexpr int RK = Lay<DQK, true>::ROW;
+  static constexpr int RV = Lay<DV, true>::ROW;
   static constexpr int K_OFF = 0;                          // K [64][RK]
   static constexpr int V_OFF = K_OFF + 64 * RK * 2;        // V [64][RV]
   static constexpr int Q_OFF = V_OFF + 64 * RV * 2;        // Q [64][RK]
@@ -257,7 +276,8 @@ struct DkdvLds {
 template <int DQK, int DV, bool CAP>
 __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
   using M = DkdvLds<DQK, DV>;
-  constexpr int RK = M::RK, RV = M::RV;
+  using LQ = Lay<DQK, true>;
+  using LV = Lay<DV, true>;
   constexpr int NQ = DQK / 32, NV = DV / 32;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   typedef __attribute__((address_space(3))) uint8_t lds_u8;
@@ -289,8 +309,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
   const int key0 = c * BK;
   const uint16_t* kg = static_cast<const uint16_t*>(p.k) + (int64_t)bk * p.Lkv * DQK;
   const uint16_t* vg = static_cast<const uint16_t*>(p.v) + (int64_t)bk * p.Lkv * DV;
-  load_tile<DQK, 256>(kg, key0, p.Lkv, Ks, tid);
-  load_tile<DV, 256>(vg, key0, p.Lkv, Vs, tid);
+  load_tile<DQK, 256, true>(kg, key0, p.Lkv, Ks, tid);
+  load_tile<DV, 256, true>(vg, key0, p.Lkv, Vs, tid);
 
   const bool has_seg = p.seg_q != nullptr;
   const int my_key = key0 + 32 * kh + l32;
@@ -348,8 +368,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
   };
   // The next sub-tile's Q, dO, lse, D and segment ids are fetched into
   // registers while the current one is computed.
-  TileRegs<DQK, 256> q_next;
-  TileRegs<DV, 256> o_next;
+  TileRegs<DQK, 256, true> q_next;
+  TileRegs<DV, 256, true> o_next;
   float lse_next = 0.0f, d_next = 0.0f;
   int seg_next = 0;
   auto fetch = [&](int g, int row0) __attribute__((always_inline)) {
@@ -387,10 +407,10 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
     static_assert(DQK == DV, "S and dP take the same number of k-steps");
     pipelined<DQK / 16, 2>(
         [&](int st) {
-          return Op4{ld_op(Qs + (32 * rh + l32) * RK + 16 * st + 8 * hi),
-                     ld_op(Ks + (32 * kh + l32) * RK + 16 * st + 8 * hi),
-                     ld_op(Os + (32 * rh + l32) * RV + 16 * st + 8 * hi),
-                     ld_op(Vs + (32 * kh + l32) * RV + 16 * st + 8 * hi)};
+          return Op4{ld_op(Qs + LQ::off(32 * rh + l32, 2 * st + hi)),
+                     ld_op(Ks + LQ::off(32 * kh + l32, 2 * st + hi)),
+                     ld_op(Os + LV::off(32 * rh + l32, 2 * st + hi)),
+                     ld_op(Vs + LV::off(32 * kh + l32, 2 * st + hi))};
         },
         [&](int, const Op4& o) {
           s = mfma(o.a, o.b, s);
@@ -433,8 +453,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
         [&](int i) {
           const int ks = i / (NV + NQ), j = i % (NV + NQ);
           const int rr = 32 * rh + 16 * ks + trow;
-          const lds_u16* t = j < NV ? Os + rr * RV + 32 * j + tcol : Qs + rr * RK + 32 * (j - NV) + tcol;
-          return ld_tr(t, t + 8 * (j < NV ? RV : RK));
+          if (j < NV) return ld_tr(Os + LV::at(rr, 32 * j + tcol), Os + LV::at(rr + 8, 32 * j + tcol));
+          return ld_tr(Qs + LQ::at(rr, 32 * (j - NV) + tcol), Qs + LQ::at(rr + 8, 32 * (j - NV) + tcol));
         },
         [&](int i, const bf16x8& b) {
           const int ks = i / (NV + NQ), j = i % (NV + NQ);
@@ -479,8 +499,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
 
 template <int DQK, int DV>
 struct DqLds {
-  static constexpr int RK = rs<DQK>();
-  static constexpr int RV = rs<DV>();
+  static constexpr int RK = Lay<DQK, false>::ROW;
+  static constexpr int RV = Lay<DV, false>::ROW;
   static constexpr int K_OFF = 0;                      // K [64][RK]
   static constexpr int V_OFF = K_OFF + 64 * RK * 2;    // V [64][RV]
   static constexpr int SEG_OFF = V_OFF + 64 * RV * 2;  // key segment ids [64]
@@ -491,7 +511,7 @@ struct DqLds {
 template <int DQK, int DV, bool CAP>
 __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
   using M = DqLds<DQK, DV>;
-  constexpr int RK = M::RK, RV = M::RV;
+  constexpr int RK = M::RK, RV = M::RV;  // plain rows (Lay<D, false>)
   constexpr int NQ = DQK / 32;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   typedef __attribute__((address_space(3))) uint8_t lds_u8;
@@ -555,8 +575,8 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
   const int x1 = p.row_ptr[r + 1];
   // The next block's K, V and key segment ids are fetched into registers
   // while the current one is computed.
-  TileRegs<DQK, 512> k_next;
-  TileRegs<DV, 512> v_next;
+  TileRegs<DQK, 512, false> k_next;
+  TileRegs<DV, 512, false> v_next;
   int seg_next = 0;
   auto fetch = [&](int x) __attribute__((always_inline)) {
     const int key0 = p.active_cols[x] * BK;
