@@ -90,6 +90,16 @@ struct Lay {
   }
 };
 
+// Raw buffer resource over `bytes` bytes from `base` (a wave-uniform
+// address): loads past the end return zero, with no branch per load.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), (short)0,
+                                           __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000);
+}
+
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -198,14 +208,15 @@ struct TileRegs {
   static constexpr int N = 64 * CH / NTHR;
   static_assert(64 * CH % NTHR == 0, "whole chunks per thread");
   u32x4 v[N];
-  __device__ __forceinline__ void fetch(const uint16_t* g, int row0, int n_valid, int tid) {
+  // `rs` covers the n_valid rows of the matrix: rows past them read as zero.
+  __device__ __forceinline__ void fetch(__amdgpu_buffer_rsrc_t rs, int row0, int tid) {
 #pragma unroll
     for (int it = 0; it < N; ++it) {
       const int x = it * NTHR + tid;
       const int r = x / CH;
       const int c = x - r * CH;
-      v[it] = u32x4{0u, 0u, 0u, 0u};
-      if (row0 + r < n_valid) v[it] = *reinterpret_cast<const u32x4*>(g + (int64_t)(row0 + r) * D + c * 8);
+      v[it] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            rs, (uint32_t)(((row0 + r) * D + c * 8) * 2), 0, 0));
     }
   }
   __device__ __forceinline__ void store(lds_u16* rm, int tid) const {
@@ -374,8 +385,10 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
   int seg_next = 0;
   auto fetch = [&](int g, int row0) __attribute__((always_inline)) {
     const int64_t head = b * p.Hq + kvh * p.group + g;
-    q_next.fetch(static_cast<const uint16_t*>(p.q) + head * p.L * DQK, row0, p.L, tid);
-    o_next.fetch(static_cast<const uint16_t*>(p.dout) + head * p.L * DV, row0, p.L, tid);
+    q_next.fetch(buffer_rsrc(static_cast<const uint16_t*>(p.q) + head * p.L * DQK, (uint32_t)p.L * DQK * 2),
+                 row0, tid);
+    o_next.fetch(buffer_rsrc(static_cast<const uint16_t*>(p.dout) + head * p.L * DV, (uint32_t)p.L * DV * 2),
+                 row0, tid);
     if (tid < SUB) {
       const int qi = row0 + tid;
       const bool in = qi < p.L;
@@ -578,10 +591,12 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
   TileRegs<DQK, 512, false> k_next;
   TileRegs<DV, 512, false> v_next;
   int seg_next = 0;
+  const __amdgpu_buffer_rsrc_t k_rs = buffer_rsrc(kg, (uint32_t)p.Lkv * DQK * 2);
+  const __amdgpu_buffer_rsrc_t v_rs = buffer_rsrc(vg, (uint32_t)p.Lkv * DV * 2);
   auto fetch = [&](int x) __attribute__((always_inline)) {
     const int key0 = p.active_cols[x] * BK;
-    k_next.fetch(kg, key0, p.Lkv, tid);
-    v_next.fetch(vg, key0, p.Lkv, tid);
+    k_next.fetch(k_rs, key0, tid);
+    v_next.fetch(v_rs, key0, tid);
     if (tid < BK) seg_next = (has_seg && key0 + tid < p.Lkv) ? segk[key0 + tid] : 0;
   };
   if (x0 < x1) fetch(x0);
