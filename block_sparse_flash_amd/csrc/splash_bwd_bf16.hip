@@ -512,8 +512,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
 
 template <int DQK, int DV>
 struct DqLds {
-  static constexpr int RK = Lay<DQK, false>::ROW;
-  static constexpr int RV = Lay<DV, false>::ROW;
+  static constexpr int RK = Lay<DQK, true>::ROW;
+  static constexpr int RV = Lay<DV, true>::ROW;
   static constexpr int K_OFF = 0;                      // K [64][RK]
   static constexpr int V_OFF = K_OFF + 64 * RK * 2;    // V [64][RV]
   static constexpr int SEG_OFF = V_OFF + 64 * RV * 2;  // key segment ids [64]
@@ -524,7 +524,8 @@ struct DqLds {
 template <int DQK, int DV, bool CAP>
 __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
   using M = DqLds<DQK, DV>;
-  constexpr int RK = M::RK, RV = M::RV;  // plain rows (Lay<D, false>)
+  using LQ = Lay<DQK, true>;
+  using LV = Lay<DV, true>;
   constexpr int NQ = DQK / 32;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   typedef __attribute__((address_space(3))) uint8_t lds_u8;
@@ -588,8 +589,8 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
   const int x1 = p.row_ptr[r + 1];
   // The next block's K, V and key segment ids are fetched into registers
   // while the current one is computed.
-  TileRegs<DQK, 512, false> k_next;
-  TileRegs<DV, 512, false> v_next;
+  TileRegs<DQK, 512, true> k_next;
+  TileRegs<DV, 512, true> v_next;
   int seg_next = 0;
   const __amdgpu_buffer_rsrc_t k_rs = buffer_rsrc(kg, (uint32_t)p.Lkv * DQK * 2);
   const __amdgpu_buffer_rsrc_t v_rs = buffer_rsrc(vg, (uint32_t)p.Lkv * DV * 2);
@@ -615,8 +616,8 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
       static_assert(DQK == DV, "S and dP take the same number of k-steps");
       pipelined<DQK / 16, 1>(
           [&](int st) {
-            return Op2{ld_op(Ks + (32 * t + l32) * RK + 16 * st + 8 * hi),
-                       ld_op(Vs + (32 * t + l32) * RV + 16 * st + 8 * hi)};
+            return Op2{ld_op(Ks + LQ::off(32 * t + l32, 2 * st + hi)),
+                       ld_op(Vs + LV::off(32 * t + l32, 2 * st + hi))};
           },
           [&](int st, const Op2& o) {
             s = mfma(o.a, qf[st], s);
@@ -638,8 +639,8 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
         for (int j = 0; j < 8; ++j) da8[j] = (__bf16)dsv[8 * ks + j];
         pipelined<NQ, 2>(
             [&](int dt) {
-              const lds_u16* tp = Ks + (32 * t + 16 * ks + trow) * RK + 32 * dt + tcol;
-              return ld_tr(tp, tp + 8 * RK);
+              const int kr = 32 * t + 16 * ks + trow;
+              return ld_tr(Ks + LQ::at(kr, 32 * dt + tcol), Ks + LQ::at(kr + 8, 32 * dt + tcol));
             },
             [&](int dt, const bf16x8& b) { dqacc[dt] = mfma(da8, b, dqacc[dt]); });
       }
