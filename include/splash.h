@@ -1,8 +1,8 @@
 /*
- * splash.h - C ABI of the block-sparse (Splash) attention forward for
- * AMD Instinct MI355X (gfx950).
+ * splash.h - C ABI of block-sparse (Splash) attention, forward and
+ * backward, for AMD Instinct MI355X (gfx950).
  *
- * Two operations cross this boundary:
+ * These operations cross this boundary:
  *
  *   attn_mask_compile  host-side preprocessing of a causal / local-window /
  *                      segment-id mask (and their AND) into the MaskInfo
@@ -36,6 +36,18 @@
  *                      inference) and the joto.ai page, section "LSE and
  *                      online softmax" (split-K: lse = log sum_s e^{lse_s},
  *                      o = sum_s e^{lse_s - lse} o_s).
+ *
+ *   splash_attn_bwd    the gradients dq, dk, dv of the forward's o, with
+ *                      the probabilities rebuilt on chip from the stored lse
+ *                      (Lecture 13 section 6.3: the forward keeps lse for the
+ *                      backward; joto.ai page, section "LSE and online
+ *                      softmax": p is recomputed from q, k and lse).  Its K/V
+ *                      side walks the table by kv-block column
+ *                      (attn_mask_columns).
+ *
+ * Query rows may sit at key positions q_offset + i against a longer key
+ * sequence (decoding, chunked prefill): splash_mask_desc.q_offset and
+ * splash_fwd_args.L_kv / q_offset.
  *
  * Conventions for every call:
  *   - Return value: SPLASH_OK (0) or one of the SPLASH_E* codes below.  On an
