@@ -19,15 +19,17 @@
 //     walks the block's column of the table (the q blocks that read it) for
 //     every query head of the GQA group, in 64-row sub-tiles, so dk and dv
 //     are summed in registers with no atomics.  Wave w owns keys
-//     32 (w % 2) .. + 31 and rows 32 (w / 2) .. + 31 of each sub-tile.
-//     S = Q K^T and dP = dO V^T come out of v_mfma_f32_32x32x16_bf16 with one
-//     key per lane and 16 rows per lane; those accumulator items, rounded to
-//     bf16, are directly the A operand of dV += P^T dO and dK += dS^T Q (the
-//     MFMA's reduction index runs over the rows in the order the accumulator
-//     holds them), and the B operands are read transposed from the row-major
-//     Q and dO tiles with ds_read_b64_tr_b16 (four consecutive rows of one
-//     column per lane, the row grouping the accumulator implies).  The two
-//     row halves are summed through LDS at the end.
+//     32 (w % 2) .. + 31 and accumulates dV (w < 2) or dK (w >= 2) over all
+//     rows: 64 accumulator registers per wave, so two waves fit per SIMD
+//     (both dK and dV in one wave take 128, and then only one fits).
+//     S = Q K^T (and dP = dO V^T in the dK waves) come out of
+//     v_mfma_f32_32x32x16_bf16 with one key per lane and 16 rows per lane;
+//     those accumulator items, rounded to bf16, are directly the A operand
+//     of dV += P^T dO or dK += dS^T Q (the MFMA's reduction index runs over
+//     the rows in the order the accumulator holds them), and the B operands
+//     are read transposed from the row-major Q and dO tiles with
+//     ds_read_b64_tr_b16 (four consecutive rows of one column per lane, the
+//     row grouping the accumulator implies).
 //   * dq kernel: one work-group (8 waves, 32 rows each) per (query head,
 //     256-row q block) walks the row's active kv blocks; S^T = K Q^T and
 //     dP^T = V dO^T hold one row per lane, and dS^T feeds dQ += dS K the same
@@ -278,14 +280,12 @@ struct DkdvLds {
   static constexpr int D_OFF = LSE_OFF + 64 * 4;           // D [64]
   static constexpr int SEG_OFF = D_OFF + 64 * 4;           // row segment ids [64]
   static constexpr int BYTES = SEG_OFF + 64 * 4;
-  // The final row-half reduction reuses the tiles [0, LSE_OFF).
-  static constexpr int RED_BYTES = 2 * (DQK / 32 + DV / 32) * 16 * 64 * 4;
-  static_assert(RED_BYTES <= LSE_OFF, "reduction fits the tile area");
   static_assert(BYTES <= 163840, "fits the LDS of a CU");
 };
 
 template <int DQK, int DV, bool CAP>
-__global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dkdv_kernel(BwdParams p) {
   using M = DkdvLds<DQK, DV>;
   using LQ = Lay<DQK, true>;
   using LV = Lay<DV, true>;
@@ -306,8 +306,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
-  const int kh = wave & 1;   // key half of the block
-  const int rh = wave >> 1;  // row half of each sub-tile
+  const int kh = wave & 1;              // key half of the block
+  const bool dk_wave = (wave >> 1) != 0;  // wave-uniform: accumulates dK (else dV)
   // Transposed-read address of this lane: row 4 hi + (lane % 16) / 4 of a
   // 16-row step, columns 16 ((lane / 16) % 2) + 4 (lane % 4) of a 32-column tile.
   const int trow = 4 * hi + ((lane & 15) >> 2);
@@ -334,11 +334,10 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
   if (p.window_right >= 0) rlo = max(rlo, my_key - p.window_right - p.q_off);
   if (p.window_left >= 0) rhi = min(rhi, my_key + p.window_left - p.q_off);
 
-  f32x16 dkacc[NQ], dvacc[NV];
+  static_assert(DQK == DV, "one accumulator shape for dK and dV");
+  f32x16 acc[NQ];  // dK or dV of this wave's 32 keys
 #pragma unroll
-  for (int i = 0; i < NQ; ++i) dkacc[i] = f32x16{};
-#pragma unroll
-  for (int i = 0; i < NV; ++i) dvacc[i] = f32x16{};
+  for (int i = 0; i < NQ; ++i) acc[i] = f32x16{};
 
   const int x0 = p.col_ptr[c];
   const int x1 = p.col_ptr[c + 1];
@@ -414,98 +413,89 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
     have = next(&next_g, &next_row0);
     if (have) fetch(next_g, next_row0);
 
-    // S = Q K^T and dP = dO V^T (two interleaved accumulation chains): rows
-    // 32 rh + items, key 32 kh + l32.
-    f32x16 s = f32x16{}, dp = f32x16{};
-    static_assert(DQK == DV, "S and dP take the same number of k-steps");
-    pipelined<DQK / 16, 2>(
-        [&](int st) {
-          return Op4{ld_op(Qs + LQ::off(32 * rh + l32, 2 * st + hi)),
-                     ld_op(Ks + LQ::off(32 * kh + l32, 2 * st + hi)),
-                     ld_op(Os + LV::off(32 * rh + l32, 2 * st + hi)),
-                     ld_op(Vs + LV::off(32 * kh + l32, 2 * st + hi))};
-        },
-        [&](int, const Op4& o) {
-          s = mfma(o.a, o.b, s);
-          dp = mfma(o.c, o.d, dp);
-        });
-
-    // Row data of the 16 rows 32 rh + 8 (e / 4) + 4 hi + e % 4 (four runs of 4).
-    float pv[16], dsv[16];
-    const bool all_ok = all_allowed(p, row0 + 32 * rh, 32, key0 + 32 * kh, 32);  // wave-uniform
+    // Two row tiles of 32 rows each.  S = Q K^T (and dP = dO V^T in the dK
+    // waves, as a second interleaved chain): one key per lane, rows
+    // 32 rt + items.
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int rl0 = 32 * rh + 8 * q4 + 4 * hi;
-      const f32x4 l4 = *reinterpret_cast<const lds_f32x4*>(lse2s + rl0);
-      const f32x4 d4 = *reinterpret_cast<const lds_f32x4*>(Ds + rl0);
-      if (all_ok) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          p_and_ds<CAP>(p, true, s[4 * q4 + j], l4[j], dp[4 * q4 + j], d4[j], &pv[4 * q4 + j], &dsv[4 * q4 + j]);
+    for (int rt = 0; rt < 2; ++rt) {
+      f32x16 s = f32x16{}, dp = f32x16{};
+      if (dk_wave) {
+        pipelined<DQK / 16, 0>(
+            [&](int st) {
+              return Op4{ld_op(Qs + LQ::off(32 * rt + l32, 2 * st + hi)),
+                         ld_op(Ks + LQ::off(32 * kh + l32, 2 * st + hi)),
+                         ld_op(Os + LV::off(32 * rt + l32, 2 * st + hi)),
+                         ld_op(Vs + LV::off(32 * kh + l32, 2 * st + hi))};
+            },
+            [&](int, const Op4& o) {
+              s = mfma(o.a, o.b, s);
+              dp = mfma(o.c, o.d, dp);
+            });
       } else {
-        const i32x4 s4 = *reinterpret_cast<const lds_i32x4*>(segqs + rl0);
+        pipelined<DQK / 16, 0>(
+            [&](int st) {
+              return Op2{ld_op(Qs + LQ::off(32 * rt + l32, 2 * st + hi)),
+                         ld_op(Ks + LQ::off(32 * kh + l32, 2 * st + hi))};
+            },
+            [&](int, const Op2& o) { s = mfma(o.a, o.b, s); });
+      }
+
+      // Row data of the 16 rows 32 rt + 8 (e / 4) + 4 hi + e % 4 (four runs of 4).
+      float pv[16], dsv[16];
+      const bool all_ok = all_allowed(p, row0 + 32 * rt, 32, key0 + 32 * kh, 32);  // wave-uniform
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int row = row0 + rl0 + j;
-          const bool ok = (row >= rlo) & (row <= rhi) & (!has_seg || s4[j] == kseg);
-          p_and_ds<CAP>(p, ok, s[4 * q4 + j], l4[j], dp[4 * q4 + j], d4[j], &pv[4 * q4 + j], &dsv[4 * q4 + j]);
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int rl0 = 32 * rt + 8 * q4 + 4 * hi;
+        const f32x4 l4 = *reinterpret_cast<const lds_f32x4*>(lse2s + rl0);
+        const f32x4 d4 = *reinterpret_cast<const lds_f32x4*>(Ds + rl0);
+        if (all_ok) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            p_and_ds<CAP>(p, true, s[4 * q4 + j], l4[j], dp[4 * q4 + j], d4[j], &pv[4 * q4 + j], &dsv[4 * q4 + j]);
+        } else {
+          const i32x4 s4 = *reinterpret_cast<const lds_i32x4*>(segqs + rl0);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int row = row0 + rl0 + j;
+            const bool ok = (row >= rlo) & (row <= rhi) & (!has_seg || s4[j] == kseg);
+            p_and_ds<CAP>(p, ok, s[4 * q4 + j], l4[j], dp[4 * q4 + j], d4[j], &pv[4 * q4 + j], &dsv[4 * q4 + j]);
+          }
         }
       }
-    }
-    // dV += P^T dO, dK += dS^T Q over this wave's 32 rows: two k-steps
-    // (ks) of NV dV tiles and NQ dK tiles each.
-    bf16x8 pa8[2], da8[2];
+      // dV += P^T dO (dV waves) or dK += dS^T Q (dK waves) over these 32
+      // rows: two k-steps (ks) of NQ tiles.
+      bf16x8 a8[2];
+      if (dk_wave) {
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+        for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        pa8[ks][j] = (__bf16)pv[8 * ks + j];
-        da8[ks][j] = (__bf16)dsv[8 * ks + j];
+          for (int j = 0; j < 8; ++j) a8[ks][j] = (__bf16)dsv[8 * ks + j];
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) a8[ks][j] = (__bf16)pv[8 * ks + j];
       }
-    pipelined<2 * (NV + NQ), 4>(
-        [&](int i) {
-          const int ks = i / (NV + NQ), j = i % (NV + NQ);
-          const int rr = 32 * rh + 16 * ks + trow;
-          if (j < NV) return ld_tr(Os + LV::at(rr, 32 * j + tcol), Os + LV::at(rr + 8, 32 * j + tcol));
-          return ld_tr(Qs + LQ::at(rr, 32 * (j - NV) + tcol), Qs + LQ::at(rr + 8, 32 * (j - NV) + tcol));
-        },
-        [&](int i, const bf16x8& b) {
-          const int ks = i / (NV + NQ), j = i % (NV + NQ);
-          if (j < NV)
-            dvacc[j] = mfma(pa8[ks], b, dvacc[j]);
-          else
-            dkacc[j - NV] = mfma(da8[ks], b, dkacc[j - NV]);
-        });
+      const lds_u16* src = dk_wave ? Qs : Os;  // B operand rows: Q for dK, dO for dV
+      pipelined<2 * NQ, 1>(
+          [&](int i) {
+            const int rr = 32 * rt + 16 * (i / NQ) + trow;
+            const int col = 32 * (i % NQ) + tcol;
+            return ld_tr(src + LQ::at(rr, col), src + LQ::at(rr + 8, col));
+          },
+          [&](int i, const bf16x8& bo) { acc[i % NQ] = mfma(a8[i / NQ], bo, acc[i % NQ]); });
+    }
   }
 
-  // Sum the two row halves: waves with rh = 1 park their sums in LDS.
-  __syncthreads();
-  lds_f32* red = (lds_f32*)lds + kh * (NQ + NV) * 16 * 64;
-  if (rh == 1) {
+  // Each wave writes its 32 keys: dK (times the scale) or dV.
+  float* outg = (dk_wave ? p.dk : p.dv) + (int64_t)bk * p.Lkv * DQK;
+  const float osc = dk_wave ? p.scale : 1.0f;
 #pragma unroll
-    for (int t = 0; t < NQ; ++t)
+  for (int e = 0; e < 16; ++e) {
+    const int key = key0 + 32 * kh + 8 * (e / 4) + 4 * hi + (e % 4);
+    if (key < p.Lkv) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) red[(t * 16 + e) * 64 + lane] = dkacc[t][e];
-#pragma unroll
-    for (int t = 0; t < NV; ++t)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) red[((NQ + t) * 16 + e) * 64 + lane] = dvacc[t][e];
-  }
-  __syncthreads();
-  if (rh == 0) {
-    float* dkg = p.dk + (int64_t)bk * p.Lkv * DQK;
-    float* dvg = p.dv + (int64_t)bk * p.Lkv * DV;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int key = key0 + 32 * kh + 8 * (e / 4) + 4 * hi + (e % 4);
-      if (key < p.Lkv) {
-#pragma unroll
-        for (int t = 0; t < NQ; ++t)
-          dkg[(int64_t)key * DQK + 32 * t + l32] = p.scale * (dkacc[t][e] + red[(t * 16 + e) * 64 + lane]);
-#pragma unroll
-        for (int t = 0; t < NV; ++t)
-          dvg[(int64_t)key * DV + 32 * t + l32] = dvacc[t][e] + red[((NQ + t) * 16 + e) * 64 + lane];
-      }
+      for (int t = 0; t < NQ; ++t) outg[(int64_t)key * DQK + 32 * t + l32] = osc * acc[t][e];
     }
   }
 }
