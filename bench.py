@@ -28,11 +28,17 @@ PEAK_HBM_GBS = 8000.0                           # HBM3E
 KERNEL_SOURCES = {"bf16": "splash_fwd_bf16.hip", "f32": "splash_fwd_f32.hip"}
 
 
-def unmasked_pairs(tabs, w, seg):
+def unmasked_pairs(tabs, w, seg, causal_only=False):
     """Exact count of allowed (query, key) pairs per (b, h), from the mask
     definition, summed row by row with interval arithmetic (segments: the
     allowed keys of a row are the part of its interval inside its segment,
-    segments being contiguous here)."""
+    segments being contiguous here).  ``causal_only``: the same shape under
+    the causal mask alone."""
+    return int(pairs_per_row(w, None if causal_only else seg, causal_only).sum())
+
+
+def pairs_per_row(w, seg, causal_only=False):
+    """Allowed keys of every query row (numpy int64 [L])."""
     import numpy as np
     L = w.L
     i = w.q_offset + np.arange(L, dtype=np.int64)   # key positions of the query rows
@@ -40,9 +46,9 @@ def unmasked_pairs(tabs, w, seg):
     hi = np.full(L, w.keys - 1, np.int64)
     if w.causal:
         hi = np.minimum(hi, i)
-    if w.window_left >= 0:
+    if w.window_left >= 0 and not causal_only:
         lo = np.maximum(lo, i - w.window_left)
-    if w.window_right >= 0:
+    if w.window_right >= 0 and not causal_only:
         hi = np.minimum(hi, i + w.window_right)
     if seg is not None:
         seg = np.asarray(seg)
@@ -51,7 +57,7 @@ def unmasked_pairs(tabs, w, seg):
         ends = np.searchsorted(seg, seg, side="right") - 1
         lo = np.maximum(lo, starts)
         hi = np.minimum(hi, ends)
-    return int(np.maximum(hi - lo + 1, 0).sum())
+    return np.maximum(hi - lo + 1, 0)
 
 
 def kernel_sha(dtype):
@@ -77,67 +83,170 @@ def committed_traffic(workload, dtype):
     return float(tb.group(1))
 
 
-def cpu_baseline(w, q, k, v, seg, budget_s):
-    """The float64 oracle on the host over whole (batch, head) pairs, in
-    order, adding heads until about budget_s of work or the whole workload;
-    returns the baseline dict."""
-    from oracle import attention_ref
+def host_cpu():
+    """(usable cores, CPU model name) of this host."""
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
+    return n, model
+
+
+# Inputs of the oracle workers: set in the parent before the pool forks, so
+# the children share them copy-on-write (no pickling of the arrays).
+_ORACLE = {}
+
+
+def _limit_threads():
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
     except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
-    qf, kf, vf = q.float().numpy(), k.float().numpy(), v.float().numpy()
-    pairs = unmasked_pairs(None, w, seg)
-    done = 0
+        pass
+
+
+def _oracle_fwd_item(item):
+    """One work item of the forward baseline: rows [r0, r1) of head (b, h)."""
+    from oracle import attention_ref
+    b, h, r0, r1 = item
+    w, seg = _ORACLE["w"], _ORACLE["seg"]
     t0 = time.perf_counter()
-    while done < w.B * w.Hq and (time.perf_counter() - t0) < budget_s:
-        b, h = divmod(done, w.Hq)
-        attention_ref(qf, kf, vf, scale=w.softmax_scale, soft_cap=w.soft_cap,
-                      causal=w.causal, window_left=w.window_left,
-                      window_right=w.window_right, seg_q=seg, heads=[(b, h)],
-                      q_offset=w.q_offset)
-        done += 1
-    dt = time.perf_counter() - t0
-    flop = 2.0 * (w.d_qk + w.d_v) * pairs * done
-    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"{done} of {w.B * w.Hq} (batch, head) pairs in order, all {w.L} "
-                      f"rows each (against {w.keys} keys), float64 numpy, {dt:.1f} s"}
+    attention_ref(_ORACLE["q"], _ORACLE["k"], _ORACLE["v"], scale=w.softmax_scale,
+                  soft_cap=w.soft_cap, causal=w.causal, window_left=w.window_left,
+                  window_right=w.window_right, seg_q=seg, heads=[(b, h)],
+                  rows=list(range(r0, r1)), q_offset=w.q_offset)
+    return time.perf_counter() - t0
 
 
-def cpu_baseline_bwd(w, q, k, v, seg, budget_s):
-    """The float64 backward oracle on the host over whole (batch, head) pairs
-    in order (each with its own K/V head and a seeded upstream gradient),
-    adding heads until about budget_s of work; returns the baseline dict."""
+def _oracle_bwd_item(item):
+    """One work item of the backward baseline: the gradients of head (b, h)
+    alone (its own K/V head, a seeded upstream gradient)."""
     import numpy as np
     from oracle import attention_bwd_ref
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
-    qf, kf, vf = q.float().numpy(), k.float().numpy(), v.float().numpy()
-    group = w.Hq // w.Hkv
-    rng = np.random.default_rng(w.seed + 2)
-    pairs = unmasked_pairs(None, w, seg)
-    done = 0
+    b, h = item
+    w, seg = _ORACLE["w"], _ORACLE["seg"]
+    kh = h // (w.Hq // w.Hkv)
+    do = np.random.default_rng(w.seed + 2 + b * w.Hq + h).standard_normal((1, 1, w.L, w.d_v))
+    q, k, v = _ORACLE["q"], _ORACLE["k"], _ORACLE["v"]
     t0 = time.perf_counter()
-    while done < w.B * w.Hq and (time.perf_counter() - t0) < budget_s:
-        b, h = divmod(done, w.Hq)
-        kh = h // group
-        do = rng.standard_normal((1, 1, w.L, w.d_v))
-        attention_bwd_ref(qf[b:b + 1, h:h + 1], kf[b:b + 1, kh:kh + 1], vf[b:b + 1, kh:kh + 1], do,
-                          scale=w.softmax_scale, soft_cap=w.soft_cap, causal=w.causal,
-                          window_left=w.window_left, window_right=w.window_right, seg_q=seg,
-                          q_offset=w.q_offset)
-        done += 1
-    dt = time.perf_counter() - t0
-    flop = 2.0 * (3 * w.d_qk + 2 * w.d_v) * pairs * done
-    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+    attention_bwd_ref(q[b:b + 1, h:h + 1], k[b:b + 1, kh:kh + 1], v[b:b + 1, kh:kh + 1], do,
+                      scale=w.softmax_scale, soft_cap=w.soft_cap, causal=w.causal,
+                      window_left=w.window_left, window_right=w.window_right, seg_q=seg,
+                      q_offset=w.q_offset)
+    return time.perf_counter() - t0
+
+
+def cpu_baseline(w, q, k, v, seg, budget_s, backward=False, max_workers=16):
+    """The float64 oracle as it stands, timed on the host: a process pool
+    (one single-threaded BLAS per worker, as many workers as usable cores,
+    at most ``max_workers``) over work items of the same workload - row
+    panels of 512 rows of a (batch, head) for the forward, whole (batch,
+    head) gradients for the backward.  One item is timed first to size the
+    sample to about ``budget_s`` seconds of wall time; the sample is then
+    timed with perf_counter around the pool (input generation excluded).
+    Returns the baseline dict (None when one backward head would not fit in
+    memory)."""
+    import multiprocessing as mp
+    import numpy as np
+    nproc, model = host_cpu()
+    workers = max(1, min(nproc, max_workers))
+    if backward and w.L * w.keys * 8 * 12 > (4 << 30):
+        return None
+    _ORACLE.update(w=w, seg=seg, q=q.float().numpy(), k=k.float().numpy(), v=v.float().numpy())
+    rows = pairs_per_row(w, seg)
+    flop_pair = 2.0 * ((3 * w.d_qk + 2 * w.d_v) if backward else (w.d_qk + w.d_v))
+    if backward:
+        items = [(b, h) for b in range(w.B) for h in range(w.Hq)]
+        item_flop = lambda it: flop_pair * float(rows.sum())
+        fn = _oracle_bwd_item
+    else:
+        panel = 512
+        # Every (batch, head) cut into row panels, in a fixed pseudo-random
+        # order: the oracle's work per panel is the same (it scores all keys),
+        # and a sample drawn this way carries the workload's mix of unmasked
+        # pairs per panel.
+        items = [(b, h, r0, min(r0 + panel, w.L)) for b in range(w.B) for h in range(w.Hq)
+                 for r0 in range(0, w.L, panel)]
+        items = [items[i] for i in np.random.default_rng(0).permutation(len(items))]
+        item_flop = lambda it: flop_pair * float(rows[it[2]:it[3]].sum())
+        fn = _oracle_fwd_item
+    _limit_threads()
+    t1 = fn(items[0])          # serial probe (warm caches, size the sample)
+    n = int(min(len(items), max(workers, round(budget_s * workers / max(t1, 1e-3)))))
+    n = max(1, (n // workers) * workers) if n >= workers else n
+    sample = items[:n]
+    ctx = mp.get_context("fork")
+    with ctx.Pool(workers, initializer=_limit_threads) as pool:
+        t0 = time.perf_counter()
+        pool.map(fn, sample, chunksize=1)
+        dt = time.perf_counter() - t0
+    flop = sum(item_flop(it) for it in sample)
+    _ORACLE.clear()
+    what = (f"backward of {n} of {len(items)} (batch, head) pairs" if backward else
+            f"{n} of {len(items)} work items (512-row panels of a (batch, head), against all "
+            f"{w.keys} keys)")
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": workers,
             "kind": "oracle",
-            "sample": f"backward of {done} of {w.B * w.Hq} (batch, head) pairs in order, all "
-                      f"{w.L} rows each, float64 numpy, {dt:.1f} s"}
+            "sample": f"{what}, float64 numpy, {workers} single-threaded worker processes, "
+                      f"{dt:.1f} s wall; effective FLOPs = unmasked pairs x {int(flop_pair)}",
+            "nproc": nproc, "cpu_model": model}
+
+
+def median_min(xs):
+    """(median, min) of a non-empty list."""
+    srt = sorted(xs)
+    return 0.5 * (srt[(len(srt) - 1) // 2] + srt[len(srt) // 2]), srt[0]
+
+
+def time_steps(step, stream, steps, warmup):
+    """Run ``warmup`` untimed steps, then ``steps`` timed ones with a HIP
+    event pair around each call (on the launch stream) and one pair around
+    all of them.  Returns (total ms, per-call ms list, wall s)."""
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev0.record(stream)
+    for a, b in ev:
+        a.record(stream)
+        step()
+        b.record(stream)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    return ev0.elapsed_time(ev1), [a.elapsed_time(b) for a, b in ev], wall
+
+
+def time_cold(step, stream, dev, scratch_mib=512):
+    """One call right after writing a scratch buffer of ``scratch_mib`` MiB
+    (which evicts the inputs from the L2 and the last-level cache); ms."""
+    import torch
+    scratch = torch.empty(scratch_mib << 20, dtype=torch.uint8, device=dev)
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    scratch.fill_(1)
+    a.record(stream)
+    step()
+    b.record(stream)
+    torch.cuda.synchronize()
+    del scratch
+    return a.elapsed_time(b)
 
 
 def main():
@@ -160,7 +269,10 @@ def main():
                     help="after timing, run one device-to-device copy of this many MiB "
                          "(a plain copy of known size, for scaling HBM counters)")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
-                    help="seconds of oracle work for cpu_baseline (0: skip)")
+                    help="seconds (wall) of oracle work for cpu_baseline (0: skip)")
+    ap.add_argument("--no-sparsity", action="store_true",
+                    help="skip the causal-only timing of masked workloads")
+    ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache call")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -175,9 +287,17 @@ def main():
     w = ALL_WORKLOADS[args.workload]
     if args.n_split is None:
         args.n_split = w.n_split
+    q, k, v, seg = make_inputs(w)
+    if args.backward and (w.dtype != "bf16" or args.n_split != 1):
+        raise SystemExit("--backward runs bf16 workloads without split-KV")
+    # The oracle baseline runs first, before this process touches the GPU,
+    # so that its worker processes fork from a process without a device.
+    cpu = None
+    if args.cpu_budget > 0:
+        cpu = cpu_baseline(w, q, k, v, seg, args.cpu_budget, backward=args.backward)
+
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
-    q, k, v, seg = make_inputs(w)
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
     bq, bkv = fwd_tile(w.dtype, w.d_qk, w.d_v)
     mask_kw = dict(causal=w.causal, window_left=w.window_left, window_right=w.window_right)
@@ -197,8 +317,6 @@ def main():
 
     if args.backward:
         from block_sparse_flash_amd import splash_bwd
-        if w.dtype != "bf16" or args.n_split != 1:
-            raise SystemExit("--backward runs bf16 workloads without split-KV")
         splash_fwd(qd, kd, vd, **kw)
         g = torch.Generator().manual_seed(w.seed + 1)
         dod = torch.randn(out.shape, generator=g).to(torch.bfloat16).to(dev)
@@ -207,22 +325,11 @@ def main():
         step = lambda: splash_bwd(qd, kd, vd, out, lse, dod, **bkw)
     else:
         step = lambda: splash_fwd(qd, kd, vd, **kw)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_events = ev0.elapsed_time(ev1)
-    ms_per_step = ms_events / args.steps
+    ms_total, per_call, wall = time_steps(step, stream, args.steps, args.warmup)
+    ms_per_step = ms_total / args.steps
+    ms_median, ms_min = median_min(per_call)
+    ms_cold = None if args.no_cold else time_cold(step, stream, dev)
 
     pairs = unmasked_pairs(tabs, w, seg)
     # Algorithmic FLOP per unmasked pair: forward S = QK^T and PV; backward
@@ -249,9 +356,24 @@ def main():
                     "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
                     "frac": round(tflops / peak, 4), "traffic": traffic}
 
-    cpu = None
-    if args.cpu_budget > 0:
-        cpu = (cpu_baseline_bwd if args.backward else cpu_baseline)(w, q, k, v, seg, args.cpu_budget)
+    # Skipped-block speedup against mask sparsity (Lecture 13 section 6.4):
+    # the same shape and inputs under the causal mask alone.
+    sparsity = None
+    masked = w.window_left >= 0 or w.window_right >= 0 or w.segments
+    if masked and w.causal and not decode and not args.no_sparsity and not args.backward:
+        ctabs = compile_mask(w.L, bq, bkv, L_kv=w.keys, causal=True, q_offset=w.q_offset)
+        ckw = dict(kw, tables=ctabs, seg_q=None, window_left=-1, window_right=-1)
+        cstep = lambda: splash_fwd(qd, kd, vd, **ckw)
+        c_steps = max(1, min(args.steps, 20))
+        c_total, _, _ = time_steps(cstep, stream, c_steps, min(args.warmup, 3))
+        c_ms = c_total / c_steps
+        pairs_c = unmasked_pairs(None, w, seg, causal_only=True)
+        sparsity = {"t_causal_ms": round(c_ms, 5), "t_masked_ms": round(ms_per_step, 5),
+                    "speedup": round(c_ms / ms_per_step, 3),
+                    "active_blocks_causal": ctabs.n_active, "active_blocks_masked": tabs.n_active,
+                    "block_ratio": round(ctabs.n_active / max(1, tabs.n_active), 3),
+                    "pair_ratio": round(pairs_c / max(1, pairs), 3),
+                    "block": [bq, bkv], "causal_steps": c_steps}
 
     mask = "causal" if w.causal else "dense"
     if w.window_left >= 0 or w.window_right >= 0:
@@ -268,6 +390,10 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
+        "ms_median": round(ms_median, 5),
+        "ms_min": round(ms_min, 5),
+        "ms_cold": None if ms_cold is None else round(ms_cold, 5),
+        "value_median": round(flop_per_step / (ms_median * 1e-3) / 1e12, 2),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -285,7 +411,11 @@ def main():
         "active_blocks": tabs.n_active, "partial_blocks": tabs.n_partial,
         "mask_compile_ms": round(mask_ms, 3),
         "wall_s_timed_region": round(wall, 4),
+        "timing": "HIP events on the launch stream around each call and around all "
+                  "calls; inputs resident, no cache flush (ms_cold: one call after "
+                  "writing 512 MiB of scratch)",
         "roofline": roofline,
+        "sparsity": sparsity,
         "cpu_baseline": cpu,
     }
     if args.copy_calibration_mib > 0:

@@ -32,6 +32,42 @@ def _seg_array(seg, L):
     return a
 
 
+def _mask_key(causal, window_left, window_right, seg_q, seg_kv, q_offset):
+    """What a table was compiled for: the mask parameters and a digest of
+    the segment ids (key ids default to the query ids)."""
+    import hashlib
+    digest = None
+    if seg_q is not None:
+        h = hashlib.sha256()
+        sq = np.ascontiguousarray(np.asarray(seg_q).reshape(-1), dtype=np.int32)
+        skv = sq if seg_kv is None else np.ascontiguousarray(np.asarray(seg_kv).reshape(-1), dtype=np.int32)
+        h.update(sq.tobytes())
+        h.update(b"|")
+        h.update(skv.tobytes())
+        digest = h.hexdigest()
+    return (bool(causal), int(window_left), int(window_right), digest, int(q_offset))
+
+
+def _check_tables(tabs, bq, bkv, L, L_kv, key):
+    got = (tabs.block_q, tabs.block_kv, tabs.L_q, tabs.L_kv, tabs.q_offset)
+    if got != (bq, bkv, L, L_kv, key[4]):
+        raise ValueError(f"tables were compiled for (block_q, block_kv, L_q, L_kv, q_offset)="
+                         f"{got}; need {(bq, bkv, L, L_kv, key[4])}")
+    if tabs.mask_key is not None and tabs.mask_key != key:
+        names = ("causal", "window_left", "window_right", "segment ids", "q_offset")
+        diff = [n for n, a, b in zip(names, tabs.mask_key, key) if a != b]
+        raise ValueError("tables were compiled for another mask (differs in " + ", ".join(diff) + ")")
+
+
+def _check_out(t, name, shape, dtype, device):
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != device or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)} on {device}; "
+                         f"got {t.dtype} {tuple(t.shape)} on {t.device}"
+                         + ("" if t.is_contiguous() else " (not contiguous)"))
+
+
 @dataclass
 class MaskTables:
     """Host copy of the MaskInfo execution table (see include/splash.h)."""
@@ -55,6 +91,9 @@ class MaskTables:
     row_order: np.ndarray
     partial_mask_blocks: np.ndarray
     q_offset: int = 0
+    # (causal, window_left, window_right, segment-id digest, q_offset) the
+    # tables were compiled for; calls with another mask are refused.
+    mask_key: Optional[tuple] = None
     _device: dict = field(default_factory=dict, repr=False)
     _columns: Optional[dict] = field(default=None, repr=False)
 
@@ -139,7 +178,8 @@ def compile_mask(L_q: int, block_q: int, block_kv: int, *, L_kv: Optional[int] =
     arrays["block_mask"] = arrays["block_mask"].reshape(nq, nkv)
     arrays["partial_mask_blocks"] = arrays["partial_mask_blocks"].reshape(npat, block_q, block_kv)
     return MaskTables(L_q, L_kv, block_q, block_kv, nq, nkv, na, sizes.n_partial, npat, **arrays,
-                      q_offset=int(q_offset))
+                      q_offset=int(q_offset),
+                      mask_key=_mask_key(causal, window_left, window_right, sq, skv, q_offset))
 
 
 def fwd_tile(dtype: str, d_qk: int, d_v: int):
@@ -223,6 +263,8 @@ def splash_fwd(q, k, v, *, scale: Optional[float] = None, soft_cap: float = 0.0,
         seg_q_dev = rows_q.contiguous().to(q.device)
         seg_kv_dev = None if rows_kv is None else rows_kv.contiguous().to(q.device)
 
+    _check_out(out, "out", (B, Hq, L, d_v), q.dtype, q.device)
+    _check_out(lse, "lse", (B, Hq, L), torch.float32, q.device)
     if out is None:
         out = torch.empty((B, Hq, L, d_v), dtype=q.dtype, device=q.device)
     if lse is None and return_lse:
@@ -235,6 +277,8 @@ def splash_fwd(q, k, v, *, scale: Optional[float] = None, soft_cap: float = 0.0,
         need = split_workspace_bytes(n_split, 1 if per_batch else B, Hq, L, d_v)
         if workspace is None:
             workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        if workspace.device != q.device or not workspace.is_contiguous():
+            raise ValueError(f"workspace must be a contiguous tensor on {q.device}")
         have = workspace.numel() * workspace.element_size()
         if have < need:
             raise ValueError(f"workspace holds {have} bytes, {need} needed")
@@ -250,10 +294,10 @@ def splash_fwd(q, k, v, *, scale: Optional[float] = None, soft_cap: float = 0.0,
                                 q_offset=q_offset)
         else:
             tabs = tables
-        got = (tabs.block_q, tabs.block_kv, tabs.L_q, tabs.L_kv, tabs.q_offset)
-        if got != (bq, bkv, L, L_kv, q_offset):
-            raise ValueError(f"tables were compiled for (block_q, block_kv, L_q, L_kv, q_offset)="
-                             f"{got}; need {(bq, bkv, L, L_kv, q_offset)}")
+            ids_q = None if seg_q_dev is None else seg_q_dev[0].cpu().numpy()
+            ids_kv = None if seg_kv_dev is None else seg_kv_dev[0].cpu().numpy()
+        _check_tables(tabs, bq, bkv, L, L_kv,
+                      _mask_key(causal, window_left, window_right, ids_q, ids_kv, q_offset))
         dev = tabs.device(q.device)
         if bsel is None:
             qb, kb, vb, ob = q, k, v, out
@@ -357,18 +401,17 @@ def splash_bwd(q, k, v, o, lse, dout, *, scale: Optional[float] = None, soft_cap
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     for bsel in (range(B) if per_batch else [None]):
+        b0 = bsel or 0
+        ids_q = None if sq is None else sq[b0].cpu().numpy()
+        ids_kv = None if skv is None else skv[b0].cpu().numpy()
         if tables is None or per_batch:
-            b0 = bsel or 0
             tabs = compile_mask(L, bq, bkv, L_kv=L_kv, causal=causal, window_left=window_left,
                                 window_right=window_right, q_offset=q_offset,
-                                seg_q=None if sq is None else sq[b0].cpu().numpy(),
-                                seg_kv=None if skv is None else skv[b0].cpu().numpy())
+                                seg_q=ids_q, seg_kv=ids_kv)
         else:
             tabs = tables
-        got = (tabs.block_q, tabs.block_kv, tabs.L_q, tabs.L_kv, tabs.q_offset)
-        if got != (bq, bkv, L, L_kv, q_offset):
-            raise ValueError(f"tables were compiled for (block_q, block_kv, L_q, L_kv, q_offset)="
-                             f"{got}; need {(bq, bkv, L, L_kv, q_offset)}")
+        _check_tables(tabs, bq, bkv, L, L_kv,
+                      _mask_key(causal, window_left, window_right, ids_q, ids_kv, q_offset))
         dev = tabs.device(q.device)
         cdev = tabs.device_columns(q.device)
         sl = slice(None) if bsel is None else slice(bsel, bsel + 1)

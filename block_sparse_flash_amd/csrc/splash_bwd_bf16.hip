@@ -662,9 +662,9 @@ hipError_t launch_all(const BwdParams& p, hipStream_t s) {
     const int bytes = DkdvLds<DQK, DV>::BYTES;
     auto fn = bwd_dkdv_kernel<DQK, DV, CAP>;
     if (bytes > 65536) {
-      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-      (void)hipGetLastError();
+      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+      if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(fn, dim3((unsigned)n_kv_items), dim3(256), bytes, s, p);
     const hipError_t e = hipGetLastError();

@@ -871,9 +871,9 @@ hipError_t launch(const FwdParams& p, int n_cu, hipStream_t s) {
   auto fn = splash_fwd_bf16_kernel<DQK, DV, CAP, SPLIT, PACK>;
   if (bytes > 65536) {
     // Opt in to more than 64 KiB of dynamic LDS (gfx950 has 160 KiB per CU).
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-    (void)hipGetLastError();
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(NT), bytes, s, p);
   return hipGetLastError();

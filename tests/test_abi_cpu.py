@@ -351,3 +351,29 @@ def test_backward_null_args_and_noop():
     assert lib.splash_attn_bwd(None, None) == 1
     assert lib.splash_attn_bwd(ctypes.byref(_good_bwd(B=0)), None) == 0
     assert lib.splash_last_error() == b""
+
+
+def test_tables_refuse_another_mask():
+    """Tables remember the mask they were compiled for (Lecture 13 section
+    6.2: the table is computed once for one mask); the binding refuses them
+    for a call with another causal flag, window or segment ids."""
+    from block_sparse_flash_amd.api import _check_tables, _mask_key
+    L = 700
+    bq, bkv = fwd_tile("bf16", 128, 128)
+    seg = segment_ids(L, 3, 40, 300)
+    t = compile_mask(L, bq, bkv, causal=True, window_left=100, seg_q=seg)
+    same = _mask_key(True, 100, -1, seg, None, 0)
+    _check_tables(t, bq, bkv, L, L, same)
+    # explicit key ids equal to the query ids are the same mask
+    _check_tables(t, bq, bkv, L, L, _mask_key(True, 100, -1, seg, seg.copy(), 0))
+    other_seg = seg.copy()
+    other_seg[L // 2:] += 1
+    for key, what in [(_mask_key(False, 100, -1, seg, None, 0), "causal"),
+                      (_mask_key(True, 99, -1, seg, None, 0), "window_left"),
+                      (_mask_key(True, 100, 5, seg, None, 0), "window_right"),
+                      (_mask_key(True, 100, -1, None, None, 0), "segment ids"),
+                      (_mask_key(True, 100, -1, other_seg, None, 0), "segment ids")]:
+        with pytest.raises(ValueError, match=what):
+            _check_tables(t, bq, bkv, L, L, key)
+    with pytest.raises(ValueError, match="block_q"):
+        _check_tables(t, bq, bkv, L + 1, L + 1, same)

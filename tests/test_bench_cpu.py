@@ -15,10 +15,13 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def _bench():
-    spec = importlib.util.spec_from_file_location("bench", os.path.join(ROOT, "bench.py"))
-    mod = importlib.util.module_from_spec(spec)
-    spec.loader.exec_module(mod)
-    return mod
+    import sys
+    if "bench" not in sys.modules:
+        spec = importlib.util.spec_from_file_location("bench", os.path.join(ROOT, "bench.py"))
+        mod = importlib.util.module_from_spec(spec)
+        sys.modules["bench"] = mod   # the oracle pool's workers are looked up by module name
+        spec.loader.exec_module(mod)
+    return sys.modules["bench"]
 
 
 def _allowed_count(w, seg):
@@ -52,3 +55,36 @@ def test_bench_refuses_more_than_one_gpu():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_median_min():
+    b = _bench()
+    assert b.median_min([3.0, 1.0, 2.0]) == (2.0, 1.0)
+    assert b.median_min([4.0, 1.0, 2.0, 3.0]) == (2.5, 1.0)
+
+
+def test_causal_only_pairs_of_masked_workloads():
+    """The sparsity leg's causal-only pair count is the causal count of the
+    same shape: L (L + 1) / 2 per (b, h)."""
+    b = _bench()
+    for name in ("gqa_window_bf16_L32768", "gqa_docs_cap_bf16_L32768"):
+        w = ALL_WORKLOADS[name]
+        seg = segment_ids(w.L, w.seed, w.seg_min, w.seg_max) if w.segments else None
+        assert b.unmasked_pairs(None, w, seg, causal_only=True) == w.L * (w.L + 1) // 2
+        assert b.unmasked_pairs(None, w, seg) < w.L * (w.L + 1) // 2
+
+
+def test_cpu_baseline_pool_bookkeeping():
+    """The oracle baseline runs as a pool of single-threaded workers and
+    reports the cores it used, the host's core count and CPU model, and an
+    effective rate over the unmasked FLOPs of the sample it timed."""
+    from block_sparse_flash_amd.inputs import make_inputs
+    b = _bench()
+    w = ALL_WORKLOADS["causal_f32_L256_d64"]
+    q, k, v, seg = make_inputs(w)
+    r = b.cpu_baseline(w, q, k, v, seg, budget_s=0.5, max_workers=2)
+    assert r["kind"] == "oracle" and r["unit"] == "TFLOP/s" and r["value"] > 0
+    assert r["cores"] == min(2, r["nproc"]) and r["nproc"] >= 1 and isinstance(r["cpu_model"], str)
+    assert "work items" in r["sample"]
+    rb = b.cpu_baseline(w, q, k, v, seg, budget_s=0.5, backward=True, max_workers=2)
+    assert rb["value"] > 0 and "backward" in rb["sample"]

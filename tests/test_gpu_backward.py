@@ -68,6 +68,9 @@ CASES = [
     (1, 2, 2, 333, 128, dict(), 0.0, None),
     (1, 2, 1, 300, 64, dict(window_left=70, window_right=33), 3.0, None),
     (1, 8, 2, 2048, 128, dict(causal=True), 0.0, None),
+    # d = 128 with documents and the cap (the build of the documents workload)
+    (1, 4, 1, 900, 128, dict(causal=True), 50.0, (40, 300)),
+    (1, 4, 2, 640, 128, dict(causal=True, window_left=150), 20.0, (30, 200)),
 ]
 
 
@@ -131,5 +134,46 @@ def test_backward_full_size_sampled_heads():
                                           scale=w.softmax_scale, causal=True)
         e = (_check("dq", dq[sl], rdq), _check("dk", dk[sl], rdk), _check("dv", dv[sl], rdv))
         _announce(f"  head ({b}, {h}): relative max-abs errors dq {e[0]:.3g} dk {e[1]:.3g} dv {e[2]:.3g}")
+    for t in (dq, dk, dv):
+        assert bool(torch.isfinite(t).all())
+
+
+def test_backward_documents_workload_whole_documents():
+    """The documents workload (GQA 16/4, L = 32768, causal AND segment ids,
+    cap 50) at full size.  Under the segment mask a document's keys are
+    reached only by its own rows, so every gradient element of a document
+    equals the backward of that document alone with a causal mask: checked
+    for two documents (the shortest one and the one holding row L/2) on the
+    query heads of two K/V heads."""
+    from block_sparse_flash_amd.inputs import ALL_WORKLOADS, make_inputs
+    w = ALL_WORKLOADS["gqa_docs_cap_bf16_L32768"]
+    _announce(f"backward full size {w.name}")
+    q, k, v, seg = make_inputs(w)
+    g = torch.Generator().manual_seed(w.seed + 1)
+    do = torch.randn((w.B, w.Hq, w.L, w.d_v), generator=g).to(torch.bfloat16)
+    qd, kd, vd, dod = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    mk = dict(causal=True, soft_cap=w.soft_cap, scale=w.softmax_scale, seg_q=seg)
+    o, lse = splash_fwd(qd, kd, vd, **mk)
+    dq, dk, dv = splash_bwd(qd, kd, vd, o, lse, dod, **mk)
+    torch.cuda.synchronize()
+    seg = np.asarray(seg)
+    starts = np.concatenate([[0], np.flatnonzero(np.diff(seg) != 0) + 1])
+    ends = np.concatenate([starts[1:], [w.L]])
+    lens = ends - starts
+    docs = sorted({int(np.argmin(lens)), int(seg[w.L // 2] - seg[0])})
+    group = w.Hq // w.Hkv
+    for di in docs:
+        s0, s1 = int(starts[di]), int(ends[di])
+        for kh in (0, w.Hkv - 1):
+            hs = slice(kh * group, (kh + 1) * group)
+            sub = lambda t, hsl: as_f64(t[:, hsl, s0:s1])
+            rdq, rdk, rdv = attention_bwd_ref(sub(q, hs), sub(k, slice(kh, kh + 1)),
+                                              sub(v, slice(kh, kh + 1)), sub(do, hs),
+                                              scale=w.softmax_scale, soft_cap=w.soft_cap,
+                                              causal=True)
+            e = (_check("dq", dq[:, hs, s0:s1], rdq), _check("dk", dk[:, kh:kh + 1, s0:s1], rdk),
+                 _check("dv", dv[:, kh:kh + 1, s0:s1], rdv))
+            _announce(f"  document {di} rows [{s0}, {s1}) K/V head {kh}: relative max-abs errors "
+                      f"dq {e[0]:.3g} dk {e[1]:.3g} dv {e[2]:.3g}")
     for t in (dq, dk, dv):
         assert bool(torch.isfinite(t).all())

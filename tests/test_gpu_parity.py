@@ -68,6 +68,13 @@ SMALL = [
     ("bf16", 2, 8, 2, 100, 128, 128, dict(causal=True, segs=(10, 40)), 0.0, "computed"),
     ("bf16", 1, 8, 2, 200, 64, 64, dict(window_left=30), 2.0, "stored"),
     ("bf16", 1, 6, 1, 50, 192, 128, dict(causal=True), 0.0, "computed"),
+    # 192-wide heads with a soft cap (the DeepSeek-V3 head shape, Lecture 13
+    # section 6.6, with the section 5.4 cap): plain, stored masks, packed rows
+    ("bf16", 1, 2, 2, 520, 192, 128, dict(causal=True), 30.0, "computed"),
+    ("bf16", 1, 4, 2, 777, 192, 128, dict(causal=True, segs=(40, 300)), 50.0, "stored"),
+    ("bf16", 1, 2, 1, 300, 192, 64, dict(window_left=70, window_right=33), 5.0, "computed"),
+    ("bf16", 1, 6, 1, 50, 192, 128, dict(causal=True), 20.0, "computed"),
+    ("bf16", 1, 8, 2, 100, 192, 64, dict(causal=True, segs=(10, 40)), 10.0, "computed"),
 ]
 
 
@@ -203,6 +210,8 @@ SPLIT_CASES = [
     (2, 2, 2, 520, 192, 128, dict(causal=True), 0.0, 4),
     (1, 2, 1, 300, 64, 64, dict(window_left=70, window_right=33), 3.0, 7),
     (1, 2, 2, 640, 64, 128, dict(), 0.0, 64),   # more chunks than blocks: empty chunks
+    (1, 2, 2, 600, 192, 128, dict(causal=True), 30.0, 3),
+    (1, 4, 1, 500, 192, 64, dict(causal=True, segs=(40, 200)), 20.0, 2),
 ]
 
 
@@ -299,6 +308,11 @@ def test_decode_mismatched_tables_rejected():
     t = compile_mask(8, bq, bkv, L_kv=600, causal=True, q_offset=500)
     with pytest.raises(ValueError):
         splash_fwd(q.cuda(), k.cuda(), v.cuda(), causal=True, q_offset=592, tables=t)
+    with pytest.raises(ValueError, match="another mask"):
+        splash_fwd(q.cuda(), k.cuda(), v.cuda(), causal=True, window_left=64, q_offset=500, tables=t)
+    with pytest.raises(ValueError, match="out must be"):
+        splash_fwd(q.cuda(), k.cuda(), v.cuda(), causal=True, q_offset=500, tables=t,
+                   out=torch.empty((1, 2, 8, 64), dtype=torch.bfloat16, device="cuda"))
     o, _ = splash_fwd(q.cuda(), k.cuda(), v.cuda(), causal=True, q_offset=500, tables=t)
     torch.cuda.synchronize()
     assert torch.isfinite(o.float()).all()
@@ -405,6 +419,13 @@ def test_full_size_workloads_sampled(name, n_split):
     pick = sorted(set([0, n_heads - 1] + rng.integers(0, n_heads, size=2).tolist()))
     heads = [(hh // w.Hq, hh % w.Hq) for hh in pick]
     rows = _sample_rows(w.L, bq, rng)
+    if seg is not None:
+        # Both sides of every document boundary (Lecture 13 section 6.4: the
+        # segment mask ANDed with the causal one), where a row's allowed keys
+        # start over.
+        starts = np.flatnonzero(np.diff(np.asarray(seg)) != 0) + 1
+        near = np.concatenate([starts - 2, starts - 1, starts, starts + 1, starts + 63])
+        rows = np.union1d(rows, near[(near >= 0) & (near < w.L)])
     qf, kf, vf = q.float().numpy(), k.float().numpy(), v.float().numpy()
     o_ref, lse_ref = attention_ref(qf, kf, vf, scale=w.softmax_scale, soft_cap=w.soft_cap,
                                    causal=w.causal, window_left=w.window_left,
