@@ -343,13 +343,13 @@ __device__ __forceinline__ void item_fwd(const FwdParams& p, int head, int r, in
 
   // Element mask of a partial block for this wave: item E of tile t is key
   // k0 + 32t + 8(E/4) + 4hi + E%4 of query qi.
-  auto apply_mask = [&](f32x16* sv, int g, int c) __attribute__((always_inline)) {
+  auto apply_mask = [&](f32x16* sv, int pat, int c) __attribute__((always_inline)) {
     const int ka = c * BN;
     const int kz = ka + BN - 1;
     if (p.mask_stored) {
       // Pattern row = the row inside the table's q block (packed rows: the
       // row inside its query head, all of them in table row 0).
-      const uint8_t* prow = p.patterns + (int64_t)ld_table(p.mask_next, g0 + g) * (BM * BN) +
+      const uint8_t* prow = p.patterns + (int64_t)pat * (BM * BN) +
                             (PACK ? qrow : wave * 32 + l32) * BN;
       sfor<0, 8>([&](auto i_) {
         constexpr int t = SIDX(i_) / 4;
@@ -581,6 +581,10 @@ __device__ __forceinline__ void item_fwd(const FwdParams& p, int head, int r, in
           oacc[dt] = mfma(opnd[m], pb[tc / 2][tc % 2], oacc[dt]);
         }
       };
+      // The matrix wave wins the SIMD's issue arbitration over the softmax
+      // wave sharing its SIMD, so its MFMAs and operand reads are not held
+      // behind vector instructions (about 1.5% on dense causal).
+      __builtin_amdgcn_s_setprio(3);
       sfor<0, (DIST < O::N ? DIST : O::N)>([&](auto m_) { read_opnd(m_); });
       sfor<0, O::N>([&](auto m_) __attribute__((always_inline)) {
         constexpr int m = SIDX(m_);
@@ -591,6 +595,7 @@ __device__ __forceinline__ void item_fwd(const FwdParams& p, int head, int r, in
           __builtin_amdgcn_sched_barrier(0);
         }
       });
+      __builtin_amdgcn_s_setprio(0);
       // The scores stay in this half-step (not sunk past the barrier).
       if constexpr (NQ > 0) {
         const f32x16 a0 = sacc[0], a1 = sacc[1];
@@ -634,7 +639,7 @@ __device__ __forceinline__ void item_fwd(const FwdParams& p, int head, int r, in
       });
       return (ps[0] + ps[1]) + (ps[2] + ps[3]);
     };
-    auto sm = [&](int i, auto copy, auto ncopy_tag) __attribute__((always_inline)) {
+    auto sm = [&](int i, int mn, int ci, auto copy, auto ncopy_tag) __attribute__((always_inline)) {
       f32x16* sv = sacc;
       if constexpr (CAP) {
         // z = log2(e) cap tanh(y), tanh y = 1 - 2 / (e^{2y} + 1): keep u = 1 / (e^{2y} + 1).
@@ -647,11 +652,11 @@ __device__ __forceinline__ void item_fwd(const FwdParams& p, int head, int r, in
       }
       // Partial block <=> it has a pattern (mask_next >= 0); after the cap,
       // which would map a masked -inf to -cap.
-      if (ld_table(p.mask_next, g0 + i) >= 0) {
+      if (mn >= 0) {
         if (seg_lds)
-          apply_mask_seg_lds(sv, colc(i), i % 3);
+          apply_mask_seg_lds(sv, ci, i % 3);
         else
-          apply_mask(sv, i, colc(i));
+          apply_mask(sv, mn, ci);
       }
       float ps = exps(sv, mc, copy, ncopy_tag);
       {
@@ -718,49 +723,84 @@ __device__ __forceinline__ void item_fwd(const FwdParams& p, int head, int r, in
     //   192-wide heads: by group 1 during its SM(i), since the copy addresses
     //     do not fit beside the wider Q fragments in the matrix phase.
     constexpr bool kCopyInMM = DQK <= 128;
+    // Table entries (mask_next of block i, active columns i .. i+3) are read
+    // one softmax phase ahead: the scalar loads for step i+1 are issued at the
+    // start of SM(i) and complete at its closing barrier.  A scalar load in
+    // flight while a phase waits for its LDS reads would force a full wait
+    // (both share one counter and scalar loads return out of order).
+    struct TabWin {
+      int mn, c0, c1, c2, c3;   // mask_next[i], cols[i .. i+3] (clamped to the row)
+    };
+    auto tab_start = [&]() __attribute__((always_inline)) {
+      TabWin t{ld_table(p.mask_next, g0), colc(0), colc(1), colc(2), colc(3)};
+      // Resolved here, before the loop (the compiler does not see the waits
+      // inside the barrier assembly and would otherwise wait for them in the
+      // loop, after the next step's loads were issued).
+      asm volatile("" ::"s"(t.mn), "s"(t.c0), "s"(t.c1), "s"(t.c2), "s"(t.c3));
+      return t;
+    };
+    // Issue the loads that advance the window from step i to i+1.
+    auto tab_issue = [&](int i, int* nmn, int* c4) __attribute__((always_inline)) {
+      *nmn = ld_table(p.mask_next, g0 + min(i + 1, n - 1));
+      *c4 = colc(i + 4);
+    };
+    // Their values are needed before the barrier (which waits for them anyway).
+    auto tab_advance = [&](TabWin& t, int nmn, int c4) __attribute__((always_inline)) {
+      asm volatile("" ::"s"(nmn), "s"(c4));
+      t = TabWin{nmn, t.c1, t.c2, t.c3, c4};
+    };
     auto run = [&](auto g1_tag) __attribute__((always_inline)) {
       constexpr bool G1 = SIDX(g1_tag) != 0;
+      TabWin tw = tab_start();
       if constexpr (G1) {
-        g1_load_k(cols[0], 0);
-        seg_copy(cols[0], 0);
+        g1_load_k(tw.c0, 0);
+        seg_copy(tw.c0, 0);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       }
       lds_barrier();
       if constexpr (G1) {
         if (n > 1) {
-          g1_load_k(colc(1), 1);
-          seg_copy(colc(1), 1);
+          g1_load_k(tw.c1, 1);
+          seg_copy(tw.c1, 1);
         }
-        g1_load_v(cols[0], 0);
+        g1_load_v(tw.c0, 0);
         lds_barrier();   // group 1 starts one half-step late
       }
       mm(0, Idx<0>{}, Idx<1>{}, no_copy, Idx<0>{});
       for (int i = 0; i + 1 < n; ++i) {
+        int nmn, c4;
         if constexpr (!kCopyInMM) {
           wait_copies_and_barrier<0>();
+          tab_issue(i, &nmn, &c4);
           if constexpr (G1) {
-            const int ck = colc(i + 2), cv = colc(i + 1);
+            const int ck = tw.c2, cv = tw.c1;
             const int kbf = i & 1, vbf = (i + 1) & 1, sslot = (i + 2) % 3;
-            sm(i, [&](auto k_) __attribute__((always_inline)) { copy_part(k_, ck, kbf, cv, vbf, sslot); },
+            sm(i, tw.mn, tw.c0,
+               [&](auto k_) __attribute__((always_inline)) { copy_part(k_, ck, kbf, cv, vbf, sslot); },
                Idx<KL + VL>{});
           } else {
-            sm(i, no_copy, Idx<0>{});
+            sm(i, tw.mn, tw.c0, no_copy, Idx<0>{});
           }
+          tab_advance(tw, nmn, c4);
           lds_barrier();
           mm(i + 1, Idx<1>{}, Idx<1>{}, no_copy, Idx<0>{});
         } else if constexpr (G1) {
           wait_copies_and_barrier<0>();
-          sm(i, no_copy, Idx<0>{});
+          tab_issue(i, &nmn, &c4);
+          sm(i, tw.mn, tw.c0, no_copy, Idx<0>{});
+          tab_advance(tw, nmn, c4);
           lds_barrier();
           mm(i + 1, Idx<1>{}, Idx<1>{}, no_copy, Idx<0>{});
         } else {
           lds_barrier();
-          sm(i, no_copy, Idx<0>{});
+          tab_issue(i, &nmn, &c4);
+          sm(i, tw.mn, tw.c0, no_copy, Idx<0>{});
+          tab_advance(tw, nmn, c4);
           wait_copies_and_barrier<0>();
           // K_{i+2} (past the end: a repeat of K_{n-1} into the free buffer)
           // and V_{i+1}; the segment ids of block i+2 go to ring slot
           // (i+2) % 3, last read by SM(i-1) in half-steps 2i-1 and 2i.
-          const int ck = colc(i + 2), cv = colc(i + 1);
+          const int ck = tw.c1, cv = tw.c0;
           const int kbf = i & 1, vbf = (i + 1) & 1, sslot = (i + 2) % 3;
           mm(i + 1, Idx<1>{}, Idx<1>{},
              [&](auto k_) __attribute__((always_inline)) { copy_part(k_, ck, kbf, cv, vbf, sslot); },
@@ -771,7 +811,7 @@ __device__ __forceinline__ void item_fwd(const FwdParams& p, int head, int r, in
         wait_copies_and_barrier<0>();
       else
         lds_barrier();
-      sm(n - 1, no_copy, Idx<0>{});
+      sm(n - 1, tw.mn, tw.c0, no_copy, Idx<0>{});
       if constexpr (G1 || !kCopyInMM)
         lds_barrier();
       else
