@@ -25,7 +25,8 @@ sys.path.insert(0, ROOT)
 DEFAULT_WORKLOAD = "causal_mha_bf16_L4096_d128"
 PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}   # dense MFMA bf16; fp32 vector
 PEAK_HBM_GBS = 8000.0                           # HBM3E
-KERNEL_SOURCES = {"bf16": "splash_fwd_bf16.hip", "f32": "splash_fwd_f32.hip"}
+KERNEL_SOURCES = {"bf16": ("splash_fwd_bf16_kernel.h", "splash_fwd_bf16.hip"),
+                  "f32": ("splash_fwd_f32.hip",)}
 
 
 def unmasked_pairs(tabs, w, seg, causal_only=False):
@@ -63,7 +64,7 @@ def pairs_per_row(w, seg, causal_only=False):
 def kernel_sha(dtype):
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "block_sparse_flash_amd", "csrc")
-    for name in (KERNEL_SOURCES[dtype], "fwd_params.h"):
+    for name in (*KERNEL_SOURCES[dtype], "fwd_params.h"):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -273,6 +274,9 @@ def main():
     ap.add_argument("--no-sparsity", action="store_true",
                     help="skip the causal-only timing of masked workloads")
     ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache call")
+    ap.add_argument("--tile", default=None,
+                    help="forward tile BQxBKV (one of fwd_tiles); default: the workload's tuned "
+                         "tile, else the library's default")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -299,7 +303,12 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
-    bq, bkv = fwd_tile(w.dtype, w.d_qk, w.d_v)
+    if args.tile:
+        bq, bkv = (int(x) for x in args.tile.lower().split("x"))
+    elif w.tile and not args.backward and args.n_split == 1:
+        bq, bkv = w.tile
+    else:
+        bq, bkv = fwd_tile(w.dtype, w.d_qk, w.d_v)
     mask_kw = dict(causal=w.causal, window_left=w.window_left, window_right=w.window_right)
     t0 = time.perf_counter()
     tabs = compile_mask(w.L, bq, bkv, L_kv=w.keys, seg_q=seg, q_offset=w.q_offset, **mask_kw)
@@ -316,8 +325,10 @@ def main():
         kw.update(n_split=args.n_split, workspace=ws)
 
     if args.backward:
-        from block_sparse_flash_amd import splash_bwd
+        from block_sparse_flash_amd import bwd_tile, splash_bwd
         splash_fwd(qd, kd, vd, **kw)
+        bq, bkv = bwd_tile(w.dtype, w.d_qk, w.d_v)
+        tabs = compile_mask(w.L, bq, bkv, L_kv=w.keys, seg_q=seg, q_offset=w.q_offset, **mask_kw)
         g = torch.Generator().manual_seed(w.seed + 1)
         dod = torch.randn(out.shape, generator=g).to(torch.bfloat16).to(dev)
         bkw = dict(scale=w.softmax_scale, soft_cap=w.soft_cap, seg_q=seg, tables=tabs,

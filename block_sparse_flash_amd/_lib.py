@@ -27,8 +27,9 @@ SPLASH_MASK_STORED = 1
 
 # Every symbol include/splash.h declares.
 EXPORTED = ("splash_version", "splash_last_error", "attn_mask_compile",
-            "splash_fwd_tile", "splash_attn_fwd", "splash_split_workspace_bytes",
-            "splash_attn_fwd_split", "attn_mask_columns", "splash_attn_bwd")
+            "splash_fwd_tile", "splash_fwd_tiles", "splash_attn_fwd",
+            "splash_split_workspace_bytes", "splash_attn_fwd_split", "attn_mask_columns",
+            "splash_bwd_tile", "splash_attn_bwd")
 SPLASH_MAX_SPLIT = 64
 
 c_i32 = ctypes.c_int32
@@ -121,6 +122,12 @@ def load():
                                           ctypes.POINTER(MaskTablesC)]
         lib.splash_fwd_tile.restype = ctypes.c_int
         lib.splash_fwd_tile.argtypes = [c_i32, c_i32, c_i32,
+                                        ctypes.POINTER(c_i32), ctypes.POINTER(c_i32)]
+        lib.splash_fwd_tiles.restype = ctypes.c_int
+        lib.splash_fwd_tiles.argtypes = [c_i32, c_i32, c_i32, c_ptr, c_ptr, c_i32,
+                                         ctypes.POINTER(c_i32)]
+        lib.splash_bwd_tile.restype = ctypes.c_int
+        lib.splash_bwd_tile.argtypes = [c_i32, c_i32, c_i32,
                                         ctypes.POINTER(c_i32), ctypes.POINTER(c_i32)]
         lib.splash_attn_fwd.restype = ctypes.c_int
         lib.splash_attn_fwd.argtypes = [ctypes.POINTER(FwdArgs), c_ptr]

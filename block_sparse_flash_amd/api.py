@@ -190,6 +190,27 @@ def fwd_tile(dtype: str, d_qk: int, d_v: int):
     return bq.value, bkv.value
 
 
+def fwd_tiles(dtype: str, d_qk: int, d_v: int):
+    """Every (block_q, block_kv) the plain forward has a kernel for, the
+    default tile first (``splash_fwd_tiles``)."""
+    lib = _lib.load()
+    n = ctypes.c_int32()
+    _lib.check(lib.splash_fwd_tiles(_DTYPES[dtype], d_qk, d_v, None, None, 0, ctypes.byref(n)))
+    bq = np.zeros(n.value, np.int32)
+    bkv = np.zeros(n.value, np.int32)
+    _lib.check(lib.splash_fwd_tiles(_DTYPES[dtype], d_qk, d_v, _ptr(bq), _ptr(bkv), n.value,
+                                    ctypes.byref(n)))
+    return [(int(a), int(b)) for a, b in zip(bq, bkv)]
+
+
+def bwd_tile(dtype: str, d_qk: int, d_v: int):
+    """(block_q, block_kv) the backward's tables are compiled with."""
+    lib = _lib.load()
+    bq, bkv = ctypes.c_int32(), ctypes.c_int32()
+    _lib.check(lib.splash_bwd_tile(_DTYPES[dtype], d_qk, d_v, ctypes.byref(bq), ctypes.byref(bkv)))
+    return bq.value, bkv.value
+
+
 def _torch_dtype_name(t):
     import torch
     if t.dtype == torch.bfloat16:
@@ -240,7 +261,9 @@ def splash_fwd(q, k, v, *, scale: Optional[float] = None, soft_cap: float = 0.0,
     q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
     if scale is None:
         scale = 1.0 / float(d_qk) ** 0.5
-    bq, bkv = fwd_tile(dt, d_qk, d_v)
+    # Tables given: their tile (the library checks a kernel exists for it);
+    # else the default tile.
+    bq, bkv = (tables.block_q, tables.block_kv) if tables is not None else fwd_tile(dt, d_qk, d_v)
 
     seg_q_dev = seg_kv_dev = None
     per_batch = False
@@ -385,7 +408,7 @@ def splash_bwd(q, k, v, o, lse, dout, *, scale: Optional[float] = None, soft_cap
     q, k, v, o, dout, lse = (t.contiguous() for t in (q, k, v, o, dout, lse))
     if scale is None:
         scale = 1.0 / float(d_qk) ** 0.5
-    bq, bkv = fwd_tile("bf16", d_qk, d_v)
+    bq, bkv = bwd_tile("bf16", d_qk, d_v)
     if seg_q is None and seg_kv is not None:
         raise ValueError("seg_kv given without seg_q")
     if seg_q is not None and seg_kv is None and L_kv != L:

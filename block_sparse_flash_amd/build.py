@@ -26,6 +26,8 @@ SOURCES = [
     "splash_api.cpp",
     "splash_fwd_f32.hip",
     "splash_fwd_bf16.hip",
+    "splash_fwd_bf16_d192.hip",
+    "splash_fwd_bf16_d64.hip",
     "splash_split_merge.hip",
     "splash_bwd_api.cpp",
     "splash_bwd_bf16.hip",
@@ -54,8 +56,11 @@ def common_flags():
 # Per-source extra flags.  The bf16 kernel never produces NaN inside the
 # softmax (masked scores are -inf, all other values finite), so it is built
 # without IEEE NaN canonicalisation: fmaxf becomes a bare v_max3_f32.
+_FWD_FLAGS = ["-fno-honor-nans", "-mno-amdgpu-ieee"]
 EXTRA_FLAGS = {
-    "splash_fwd_bf16.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
+    "splash_fwd_bf16.hip": _FWD_FLAGS,
+    "splash_fwd_bf16_d192.hip": _FWD_FLAGS,
+    "splash_fwd_bf16_d64.hip": _FWD_FLAGS,
 }
 
 

@@ -26,7 +26,8 @@ struct FwdParams {
   const int32_t* seg_q;   // [B, Lseg] or null
   const int32_t* seg_kv;  // [B, Lkv] or null (then seg_q is used, Lkv = L)
   int32_t mask_stored;    // 1: partial blocks read patterns
-  // tables
+  // tables (compiled for block_q x block_kv blocks: the kernel's tile)
+  int32_t block_q, block_kv;
   int32_t n_q_blocks;
   const int32_t* row_ptr;
   const int32_t* row_order;
@@ -55,6 +56,10 @@ struct FwdParams {
 // Launchers (return the hipError_t of the launch).
 hipError_t launch_fwd_f32(const FwdParams& p, int d_qk, int d_v, hipStream_t s);
 hipError_t launch_fwd_bf16(const FwdParams& p, int d_qk, int d_v, hipStream_t s);
+// Its parts for 192-wide q/k heads and for the 64-wide head dims (64/64,
+// 64/128, 128/64), at the default tile; n_cu = compute units of the device.
+hipError_t launch_fwd_bf16_d192(const FwdParams& p, int d_v, int n_cu, hipStream_t s);
+hipError_t launch_fwd_bf16_d64(const FwdParams& p, int d_qk, int d_v, int n_cu, hipStream_t s);
 // Merge of the split-KV partials of p.ws_o / p.ws_lse into p.o (bf16) and
 // p.lse.
 hipError_t launch_split_merge_bf16(const FwdParams& p, int d_v, hipStream_t s);
@@ -62,8 +67,34 @@ hipError_t launch_split_merge_bf16(const FwdParams& p, int d_v, hipStream_t s);
 // Block sizes used by each kernel family.
 constexpr int kF32BlockQ = 64;
 constexpr int kF32BlockKV = 64;
-constexpr int kBf16BlockQ = 256;
-constexpr int kBf16BlockKV = 64;
+// The bf16 backward's tables.
+constexpr int kBwdBlockQ = 256;
+constexpr int kBwdBlockKV = 64;
+
+// A bf16 forward tile: bq query rows (32 per wave) by bkv keys per block.
+struct Tile {
+  int32_t bq, bkv;
+};
+// The tile every bf16 forward variant (split-KV, packed GQA rows) is built
+// for, per head dims: the fastest of the block-size sweep where it fits the
+// LDS (two 128-key K/V buffers of 192-wide heads do not).
+constexpr Tile bf16_default_tile(int d_qk, int d_v) {
+  return (d_qk <= 128 && d_v <= 128) ? Tile{256, 64} : Tile{256, 64};
+}
+// Tiles of the plain forward (no split-KV, no packing) of 128/128 heads:
+// the block-size sweep of 128 or 256 rows by 64 or 128 keys.
+constexpr Tile kSweepTiles[4] = {{256, 64}, {256, 128}, {128, 64}, {128, 128}};
+
+// Whether a bf16 forward instance exists for these head dims and tile;
+// `plain` = no split-KV and no packed rows.
+inline bool bf16_tile_built(int d_qk, int d_v, int bq, int bkv, bool plain) {
+  const Tile d = bf16_default_tile(d_qk, d_v);
+  if (bq == d.bq && bkv == d.bkv) return true;
+  if (!plain || d_qk != 128 || d_v != 128) return false;
+  for (const Tile& t : kSweepTiles)
+    if (t.bq == bq && t.bkv == bkv) return true;
+  return false;
+}
 
 // Number of XCDs of an MI355X; consecutive work-group ids are dispatched
 // round-robin over them.

@@ -56,8 +56,53 @@ extern "C" int splash_fwd_tile(int32_t dtype, int32_t d_qk, int32_t d_v, int32_t
   if (!dims_supported(dtype, d_qk, d_v))
     return splash::fail(SPLASH_EUNSUPPORTED, "splash_fwd_tile: head dims (%d, %d) not built for dtype %d",
                         d_qk, d_v, dtype);
-  *block_q = dtype == SPLASH_F32 ? splash::kF32BlockQ : splash::kBf16BlockQ;
-  *block_kv = dtype == SPLASH_F32 ? splash::kF32BlockKV : splash::kBf16BlockKV;
+  if (dtype == SPLASH_F32) {
+    *block_q = splash::kF32BlockQ;
+    *block_kv = splash::kF32BlockKV;
+  } else {
+    const splash::Tile t = splash::bf16_default_tile(d_qk, d_v);
+    *block_q = t.bq;
+    *block_kv = t.bkv;
+  }
+  return SPLASH_OK;
+}
+
+extern "C" int splash_fwd_tiles(int32_t dtype, int32_t d_qk, int32_t d_v, int32_t* block_q,
+                                int32_t* block_kv, int32_t capacity, int32_t* count) {
+  splash::clear_error();
+  if (!count || capacity < 0 || (capacity > 0 && (!block_q || !block_kv)))
+    return splash::fail(SPLASH_EINVAL, "splash_fwd_tiles: NULL output or negative capacity");
+  int32_t def_q = 0, def_kv = 0;
+  const int rc = splash_fwd_tile(dtype, d_qk, d_v, &def_q, &def_kv);
+  if (rc != SPLASH_OK) return rc;
+  int32_t n = 0;
+  auto put = [&](int32_t q, int32_t kv) {
+    if (n < capacity) {
+      block_q[n] = q;
+      block_kv[n] = kv;
+    }
+    ++n;
+  };
+  put(def_q, def_kv);
+  if (dtype == SPLASH_BF16)
+    for (const splash::Tile& t : splash::kSweepTiles)
+      if (!(t.bq == def_q && t.bkv == def_kv) && splash::bf16_tile_built(d_qk, d_v, t.bq, t.bkv, true))
+        put(t.bq, t.bkv);
+  *count = n;
+  return SPLASH_OK;
+}
+
+extern "C" int splash_bwd_tile(int32_t dtype, int32_t d_qk, int32_t d_v, int32_t* block_q,
+                               int32_t* block_kv) {
+  splash::clear_error();
+  if (!block_q || !block_kv) return splash::fail(SPLASH_EINVAL, "splash_bwd_tile: NULL output");
+  if (dtype != SPLASH_F32 && dtype != SPLASH_BF16)
+    return splash::fail(SPLASH_EDTYPE, "splash_bwd_tile: unknown dtype %d", dtype);
+  if (dtype != SPLASH_BF16 || !((d_qk == 64 && d_v == 64) || (d_qk == 128 && d_v == 128)))
+    return splash::fail(SPLASH_EUNSUPPORTED, "splash_bwd_tile: no backward for dtype %d, head dims (%d, %d)",
+                        dtype, d_qk, d_v);
+  *block_q = splash::kBwdBlockQ;
+  *block_kv = splash::kBwdBlockKV;
   return SPLASH_OK;
 }
 
@@ -66,7 +111,7 @@ namespace {
 // Validates *args (errors prefixed with `fn`) and fills *p for the launch.
 // Returns SPLASH_OK, an error code, or -1 for a problem with nothing to
 // compute (B, Hq or L equal to 0).
-int prepare(const splash_fwd_args* args, const char* fn, splash::FwdParams* out) {
+int prepare(const splash_fwd_args* args, const char* fn, bool split, splash::FwdParams* out) {
   if (!args) return splash::fail(SPLASH_EINVAL, "%s: NULL args", fn);
   const splash_fwd_args& a = *args;
   if (a.dtype != SPLASH_F32 && a.dtype != SPLASH_BF16)
@@ -105,9 +150,14 @@ int prepare(const splash_fwd_args* args, const char* fn, splash::FwdParams* out)
 
   int32_t bq = 0, bkv = 0;
   splash_fwd_tile(a.dtype, a.d_qk, a.d_v, &bq, &bkv);
-  if (a.block_q != bq || a.block_kv != bkv)
-    return splash::fail(SPLASH_ESHAPE, "%s: tables built for blocks %dx%d, kernel uses %dx%d", fn,
-                        a.block_q, a.block_kv, bq, bkv);
+  const bool default_tile = a.block_q == bq && a.block_kv == bkv;
+  if (!default_tile) {
+    if (a.dtype != SPLASH_BF16 || !splash::bf16_tile_built(a.d_qk, a.d_v, a.block_q, a.block_kv, !split))
+      return splash::fail(SPLASH_ESHAPE, "%s: no kernel for tables of %dx%d blocks (default tile %dx%d)", fn,
+                          a.block_q, a.block_kv, bq, bkv);
+    bq = a.block_q;
+    bkv = a.block_kv;
+  }
   const int64_t nq = (static_cast<int64_t>(a.L) + bq - 1) / bq;
   if (a.n_q_blocks != nq)
     return splash::fail(SPLASH_ESHAPE, "%s: n_q_blocks=%d but L=%d needs %lld", fn, a.n_q_blocks,
@@ -159,6 +209,8 @@ int prepare(const splash_fwd_args* args, const char* fn, splash::FwdParams* out)
   p.seg_q = a.seg_q;
   p.seg_kv = a.seg_kv;
   p.mask_stored = a.mask_mode == SPLASH_MASK_STORED ? 1 : 0;
+  p.block_q = bq;
+  p.block_kv = bkv;
   p.n_q_blocks = static_cast<int32_t>(nq);
   p.row_ptr = a.row_ptr;
   p.row_order = a.row_order;
@@ -177,7 +229,7 @@ int prepare(const splash_fwd_args* args, const char* fn, splash::FwdParams* out)
   p.row_period = 0;
   p.Lseg = a.L;
   splash_fwd_args placed = a;
-  if (a.dtype == SPLASH_BF16 && p.group > 1 && a.L < bq) {
+  if (a.dtype == SPLASH_BF16 && p.group > 1 && a.L < bq && default_tile) {
     // All query rows fit one table row: pack the query heads of each K/V
     // group into one row space ([B, Hq, L, d] is [B, Hkv, group L, d]), so
     // that an item's row tile holds group * L rows instead of L.
@@ -202,7 +254,7 @@ int64_t split_workspace_bytes(int64_t n_split, int64_t B, int64_t Hq, int64_t L,
 extern "C" int splash_attn_fwd(const splash_fwd_args* args, void* stream) {
   splash::clear_error();
   splash::FwdParams p{};
-  const int rc = prepare(args, "splash_attn_fwd", &p);
+  const int rc = prepare(args, "splash_attn_fwd", false, &p);
   if (rc == -1) return SPLASH_OK;
   if (rc != SPLASH_OK) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -229,7 +281,7 @@ extern "C" int splash_attn_fwd_split(const splash_fwd_args* args, int32_t n_spli
                                      int64_t workspace_bytes, void* stream) {
   splash::clear_error();
   splash::FwdParams p{};
-  const int rc = prepare(args, "splash_attn_fwd_split", &p);
+  const int rc = prepare(args, "splash_attn_fwd_split", true, &p);
   if (rc != SPLASH_OK && rc != -1) return rc;
   if (args->dtype != SPLASH_BF16)
     return splash::fail(SPLASH_EUNSUPPORTED, "splash_attn_fwd_split: bf16 only");

@@ -42,9 +42,9 @@ extern "C" int splash_attn_bwd(const splash_bwd_args* args, void* stream) {
   const int32_t Lkv = a.L_kv == 0 ? a.L : a.L_kv;
   if (a.seg_q && !a.seg_kv && Lkv != a.L)
     return splash::fail(SPLASH_EINVAL, "%s: seg_kv is NULL but L_kv (%d) != L (%d)", fn, Lkv, a.L);
-  if (a.block_q != splash::kBf16BlockQ || a.block_kv != splash::kBf16BlockKV)
+  if (a.block_q != splash::kBwdBlockQ || a.block_kv != splash::kBwdBlockKV)
     return splash::fail(SPLASH_ESHAPE, "%s: tables built for blocks %dx%d, kernels use %dx%d", fn, a.block_q,
-                        a.block_kv, splash::kBf16BlockQ, splash::kBf16BlockKV);
+                        a.block_kv, splash::kBwdBlockQ, splash::kBwdBlockKV);
   const int64_t nq = (static_cast<int64_t>(a.L) + a.block_q - 1) / a.block_q;
   const int64_t nkv = (static_cast<int64_t>(Lkv) + a.block_kv - 1) / a.block_kv;
   if (a.n_q_blocks != nq || a.n_kv_blocks != nkv)

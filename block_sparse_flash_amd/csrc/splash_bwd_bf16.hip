@@ -64,8 +64,8 @@ typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
 typedef __attribute__((address_space(3))) i32x4 lds_i32x4;
 typedef __attribute__((address_space(3))) int32_t lds_i32;
 
-constexpr int BQ = kBf16BlockQ;   // rows per q block of the tables
-constexpr int BK = kBf16BlockKV;  // keys per kv block of the tables
+constexpr int BQ = kBwdBlockQ;   // rows per q block of the tables
+constexpr int BK = kBwdBlockKV;  // keys per kv block of the tables
 constexpr int SUB = 64;           // rows per sub-tile in the dk/dv kernel
 constexpr float kLog2e = 1.4426950408889634f;
 

@@ -12,7 +12,7 @@ from __future__ import annotations
 
 import math
 from dataclasses import dataclass, asdict
-from typing import Optional
+from typing import Optional, Tuple
 
 import numpy as np
 
@@ -42,6 +42,7 @@ class Workload:
     L_kv: Optional[int] = None      # key positions; None: L
     q_offset: int = 0               # query row i sits at key position q_offset + i
     n_split: int = 1                # split-KV chunks the bench uses by default
+    tile: Optional[Tuple[int, int]] = None   # forward tile the bench uses (None: default)
 
     @property
     def softmax_scale(self) -> float:
@@ -67,19 +68,21 @@ WORKLOADS = {
         causal=True, seed=1),
     "causal_mha_bf16_L4096_d128": Workload(
         "causal_mha_bf16_L4096_d128", "bf16", 2, 32, 32, 4096, 128, 128,
-        causal=True, seed=2),
+        causal=True, seed=2, tile=(256, 128)),
     "causal_mha_bf16_L4096_d192": Workload(
         "causal_mha_bf16_L4096_d192", "bf16", 1, 128, 128, 4096, 192, 128,
         causal=True, seed=3),
     "gqa_window_bf16_L32768": Workload(
         "gqa_window_bf16_L32768", "bf16", 1, 32, 8, 32768, 128, 128,
-        causal=True, window_left=4095, seed=4),
+        causal=True, window_left=4095, seed=4, tile=(256, 128)),
     "gqa_docs_cap_bf16_L32768": Workload(
         "gqa_docs_cap_bf16_L32768", "bf16", 1, 16, 4, 32768, 128, 128,
         causal=True, segments=True, soft_cap=50.0, qk_std=math.sqrt(2.0),
         seed=5),
 }
 
+# The tiles above are the block-size sweep's fastest for each workload
+# (128 keys per block where no segment ids cut blocks into partial ones).
 WORKLOAD_ORDER = list(WORKLOADS)
 
 # A shape for the split-KV forward: two heads of causal attention at

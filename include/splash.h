@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define SPLASH_VERSION 104
+#define SPLASH_VERSION 105
 
 /* Largest n_split of splash_attn_fwd_split. */
 #define SPLASH_MAX_SPLIT 64
@@ -196,12 +196,27 @@ int attn_mask_columns(int32_t n_q_blocks, int32_t n_kv_blocks, int32_t n_active,
  * Forward.
  * ---------------------------------------------------------------------- */
 
-/* Block sizes (block_q, block_kv) that the forward kernel for this dtype and
- * head dimensions uses; the tables passed to splash_attn_fwd must be
- * compiled with exactly these.  Errors: SPLASH_EDTYPE, SPLASH_EUNSUPPORTED,
- * SPLASH_EINVAL (NULL outputs). */
+/* Default block sizes (block_q, block_kv) of the forward kernel for this
+ * dtype and head dimensions: the tile every forward variant is built for
+ * (split-KV, packed GQA rows), and the one to compile tables with.  Lecture
+ * 13 section 5.3 (block sizes of the tiled kernel) and 6.5 (the block-size
+ * trade-off).  Errors: SPLASH_EDTYPE, SPLASH_EUNSUPPORTED, SPLASH_EINVAL
+ * (NULL outputs). */
 int splash_fwd_tile(int32_t dtype, int32_t d_qk, int32_t d_v,
                     int32_t* block_q, int32_t* block_kv);
+
+/* Every (block_q, block_kv) for which splash_attn_fwd (no split-KV) has a
+ * kernel for this dtype and head dims, the default tile first: bf16 128/128
+ * heads also have the block-size sweep's other tiles of 128 or 256 query rows
+ * by 64 or 128 keys (Lecture 13 sections 5.3 and 6.5).  Writes up to
+ * `capacity` pairs to the host arrays block_q / block_kv and the total count
+ * to *count (call with capacity 0 to size them).  Tables of a non-default
+ * tile are accepted by splash_attn_fwd only; packed GQA rows are then not
+ * used.  Errors: as splash_fwd_tile, SPLASH_EINVAL (NULL count, negative
+ * capacity, NULL arrays with capacity > 0). */
+int splash_fwd_tiles(int32_t dtype, int32_t d_qk, int32_t d_v,
+                     int32_t* block_q, int32_t* block_kv, int32_t capacity,
+                     int32_t* count);
 
 typedef struct splash_fwd_args {
   int32_t dtype;         /* SPLASH_F32 or SPLASH_BF16: q, k, v and o */
@@ -231,8 +246,9 @@ typedef struct splash_fwd_args {
   const int32_t* seg_kv; /* device [B, L_kv] or NULL (NULL: same as seg_q) */
   /* Execution table (device copies of attn_mask_compile output for
    * L_q = L, this call's L_kv and q_offset and its block sizes). */
-  int32_t block_q;       /* must equal splash_fwd_tile's block_q */
-  int32_t block_kv;      /* must equal splash_fwd_tile's block_kv */
+  int32_t block_q;       /* a tile of splash_fwd_tiles (splash_attn_fwd) or
+                            splash_fwd_tile's (splash_attn_fwd_split) */
+  int32_t block_kv;
   int32_t n_q_blocks;    /* ceil(L / block_q) */
   int32_t n_active;
   int32_t n_patterns;
@@ -329,6 +345,13 @@ int splash_attn_fwd_split(const splash_fwd_args* args, int32_t n_split, void* wo
  * summed over the query heads of a K/V group for dk and dv.
  * ---------------------------------------------------------------------- */
 
+/* Block sizes (block_q, block_kv) of the backward kernels, which its tables
+ * (and their column view) must be compiled with; they may differ from the
+ * forward's default tile.  Errors: SPLASH_EDTYPE, SPLASH_EUNSUPPORTED (not
+ * bf16 with head dims (64, 64) or (128, 128)), SPLASH_EINVAL (NULL outputs). */
+int splash_bwd_tile(int32_t dtype, int32_t d_qk, int32_t d_v,
+                    int32_t* block_q, int32_t* block_kv);
+
 typedef struct splash_bwd_args {
   int32_t dtype;         /* SPLASH_BF16 (q, k, v, o, dout) */
   int32_t B, Hq, Hkv;    /* as in splash_fwd_args */
@@ -354,11 +377,11 @@ typedef struct splash_bwd_args {
   int32_t window_right;
   const int32_t* seg_q;  /* device [B, L] or NULL */
   const int32_t* seg_kv; /* device [B, L_kv] or NULL (NULL: same as seg_q) */
-  /* Tables for L_q = L, L_kv, q_offset at the forward's block sizes: the
+  /* Tables for L_q = L, L_kv, q_offset at the backward's block sizes: the
    * row-major list of attn_mask_compile and its column view from
    * attn_mask_columns, as device copies. */
-  int32_t block_q;       /* splash_fwd_tile's block_q for (bf16, d_qk, d_v) */
-  int32_t block_kv;      /* splash_fwd_tile's block_kv */
+  int32_t block_q;       /* splash_bwd_tile's block_q for (bf16, d_qk, d_v) */
+  int32_t block_kv;      /* splash_bwd_tile's block_kv */
   int32_t n_q_blocks;    /* ceil(L / block_q) */
   int32_t n_kv_blocks;   /* ceil(L_kv / block_kv) */
   int32_t n_active;

@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
     assert set(declared) == set(_lib.EXPORTED), declared
     for name in declared:
         assert hasattr(lib, name), name
-    assert lib.splash_version() == 104
+    assert lib.splash_version() == 105
 
 
 def _assert_tables_equal(t, ref):
@@ -162,6 +162,44 @@ def test_fwd_tile_errors_and_values():
     assert fwd_tile("f32", 64, 64) == (64, 64)
 
 
+def test_fwd_tiles_and_bwd_tile():
+    """The block-size sweep (Lecture 13 sections 5.3 and 6.5): 128/128 bf16
+    heads have kernels for 128 or 256 rows by 64 or 128 keys, the default
+    first; other head dims and f32 have their default tile only."""
+    from block_sparse_flash_amd import bwd_tile, fwd_tiles
+    lib = _lib.load()
+    t = fwd_tiles("bf16", 128, 128)
+    assert t[0] == fwd_tile("bf16", 128, 128)
+    assert sorted(t) == [(128, 64), (128, 128), (256, 64), (256, 128)]
+    for dims in [(192, 128), (192, 64), (64, 64), (128, 64), (64, 128)]:
+        assert fwd_tiles("bf16", *dims) == [fwd_tile("bf16", *dims)]
+    assert fwd_tiles("f32", 128, 128) == [(64, 64)]
+    n = ctypes.c_int32()
+    assert lib.splash_fwd_tiles(1, 128, 128, None, None, 0, ctypes.byref(n)) == 0 and n.value == 4
+    assert lib.splash_fwd_tiles(1, 128, 128, None, None, 2, ctypes.byref(n)) == 1
+    assert lib.splash_fwd_tiles(1, 128, 128, None, None, 0, None) == 1
+    assert lib.splash_fwd_tiles(1, 96, 128, None, None, 0, ctypes.byref(n)) == 4
+    assert bwd_tile("bf16", 128, 128) == (256, 64) and bwd_tile("bf16", 64, 64) == (256, 64)
+    a, b = ctypes.c_int32(), ctypes.c_int32()
+    assert lib.splash_bwd_tile(1, 192, 128, ctypes.byref(a), ctypes.byref(b)) == 4
+    assert lib.splash_bwd_tile(0, 128, 128, ctypes.byref(a), ctypes.byref(b)) == 4
+    assert lib.splash_bwd_tile(3, 128, 128, ctypes.byref(a), ctypes.byref(b)) == 3
+
+
+@pytest.mark.parametrize("bq,bkv,d,code", [
+    (256, 128, 128, 0), (128, 64, 128, 0), (128, 128, 128, 0),   # sweep tiles of 128/128
+    (256, 128, 64, 2), (128, 64, 64, 2),                         # not built for 64/64
+    (64, 64, 128, 2), (512, 64, 128, 2), (256, 32, 128, 2),
+])
+def test_forward_accepts_built_tiles_only(bq, bkv, d, code):
+    """Validation accepts tables of any tile with a kernel and rejects the
+    rest before touching device memory (the fake pointers are never read:
+    B = 0 makes an accepted call a no-op)."""
+    lib = _lib.load()
+    args = _good_args(B=0, d_qk=d, d_v=d, block_q=bq, block_kv=bkv, n_q_blocks=(256 + bq - 1) // bq)
+    assert lib.splash_attn_fwd(ctypes.byref(args), None) == code
+
+
 def _good_args(**over):
     """Arguments that pass validation (with fake, aligned device pointers);
     each test changes one field so that validation must reject it before
@@ -253,6 +291,7 @@ def test_split_workspace_bytes():
     (dict(), 2, 0x20008, 1 << 30, 1),                 # misaligned workspace
     (dict(Hq=3, Hkv=2), 2, 0x20000, 1 << 30, 2),      # errors of splash_attn_fwd apply
     (dict(scale=0.0), 2, 0x20000, 1 << 30, 1),
+    (dict(block_kv=128), 2, 0x20000, 1 << 30, 2),     # split-KV: default tile only
 ])
 def test_split_forward_validation_errors(over, n_split, ws, ws_bytes, code):
     lib = _lib.load()

@@ -99,6 +99,44 @@ def test_small_cases_every_element(case):
     _announce(f"  max-abs o {eo:.3g} lse {el:.3g}")
 
 
+TILE_CASES = [
+    # (B, Hq, Hkv, L, mask kwargs, soft_cap, mask_mode)
+    (1, 4, 2, 777, dict(causal=True, segs=(40, 300)), 50.0, "computed"),
+    (1, 4, 2, 777, dict(causal=True, segs=(40, 300)), 50.0, "stored"),
+    (2, 4, 4, 640, dict(), 0.0, "computed"),
+    (1, 4, 1, 1000, dict(causal=True, window_left=200), 0.0, "computed"),
+    (1, 2, 2, 300, dict(window_left=70, window_right=33), 3.0, "stored"),
+    (2, 36, 6, 1000, dict(causal=True, window_left=300), 0.0, "computed"),  # several rounds
+]
+SWEEP_TILES = [(256, 128), (128, 64), (128, 128)]
+
+
+@pytest.mark.parametrize("tile", SWEEP_TILES, ids=lambda t: f"{t[0]}x{t[1]}")
+@pytest.mark.parametrize("case", TILE_CASES, ids=lambda c: f"B{c[0]}H{c[1]}/{c[2]}-L{c[3]}-{c[6]}"
+                         + ("-cap" if c[5] else "") + "-" + "-".join(sorted(c[4])))
+def test_sweep_tiles_every_element(tile, case):
+    """The plain forward at the other tiles of the block-size sweep (Lecture
+    13 sections 5.3 and 6.5): tables compiled at that tile, every element
+    against the oracle."""
+    B, Hq, Hkv, L, mk, cap, mode = case
+    bq, bkv = tile
+    _announce(f"tile {bq}x{bkv} {case}")
+    seed = 3000 + L + Hq
+    q, k, v = (stored(a, "bf16") for a in draw_qkv(B, Hq, Hkv, L, 128, 128, seed, qk_std=1.5 if cap else 1.0))
+    mk = dict(mk)
+    seg = None
+    if "segs" in mk:
+        lo, hi = mk.pop("segs")
+        seg = segment_ids(L, seed, lo, hi)
+    t = compile_mask(L, bq, bkv, seg_q=seg, **mk)
+    scale = 1.0 / math.sqrt(128)
+    o, lse = _run(q, k, v, scale=scale, soft_cap=cap, seg_q=seg, mask_mode=mode, tables=t, **mk)
+    o_ref, lse_ref = attention_ref(as_f64(q), as_f64(k), as_f64(v), scale=scale,
+                                   soft_cap=cap, seg_q=seg, **mk)
+    eo, el = _compare(o, lse, o_ref, lse_ref, "bf16")
+    _announce(f"  max-abs o {eo:.3g} lse {el:.3g}")
+
+
 def _logit_extremes(q, k, scale, cap, mk, seg):
     """Largest allowed logit and smallest row maximum (float64)."""
     qf, kf = as_f64(q), as_f64(k)
@@ -405,7 +443,8 @@ def test_full_size_workloads_sampled(name, n_split):
     w = {**WORKLOADS, **EXTRA_WORKLOADS}[name]
     _announce(f"full-size {name} n_split={n_split}")
     q, k, v, seg = make_inputs(w)
-    bq, bkv = fwd_tile(w.dtype, w.d_qk, w.d_v)
+    # The tile the bench times this workload at.
+    bq, bkv = w.tile if (w.tile and n_split == 1) else fwd_tile(w.dtype, w.d_qk, w.d_v)
     tabs = compile_mask(w.L, bq, bkv, L_kv=w.keys, causal=w.causal, window_left=w.window_left,
                         window_right=w.window_right, seg_q=seg, q_offset=w.q_offset)
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
