@@ -28,9 +28,11 @@ SPLASH_MASK_STORED = 1
 # Every symbol include/splash.h declares.
 EXPORTED = ("splash_version", "splash_last_error", "attn_mask_compile",
             "splash_fwd_tile", "splash_fwd_tiles", "splash_attn_fwd",
-            "splash_split_workspace_bytes", "splash_attn_fwd_split", "attn_mask_columns",
+            "splash_split_workspace_bytes", "splash_attn_fwd_split",
+            "splash_attn_fwd_split_noalloc", "attn_mask_columns",
             "splash_bwd_tile", "splash_attn_bwd")
 SPLASH_MAX_SPLIT = 64
+SPLASH_STATIC_SCRATCH_BYTES = 16 << 20
 
 c_i32 = ctypes.c_int32
 c_ptr = ctypes.c_void_p
@@ -137,6 +139,8 @@ def load():
         lib.splash_attn_fwd_split.restype = ctypes.c_int
         lib.splash_attn_fwd_split.argtypes = [ctypes.POINTER(FwdArgs), c_i32, c_ptr,
                                               ctypes.c_int64, c_ptr]
+        lib.splash_attn_fwd_split_noalloc.restype = ctypes.c_int
+        lib.splash_attn_fwd_split_noalloc.argtypes = [ctypes.POINTER(FwdArgs), c_i32, c_ptr]
         lib.attn_mask_columns.restype = ctypes.c_int
         lib.attn_mask_columns.argtypes = [c_i32, c_i32, c_i32, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr]
         lib.splash_attn_bwd.restype = ctypes.c_int

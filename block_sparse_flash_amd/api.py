@@ -225,7 +225,7 @@ def splash_fwd(q, k, v, *, scale: Optional[float] = None, soft_cap: float = 0.0,
                seg_q=None, seg_kv=None, tables: Optional[MaskTables] = None,
                mask_mode: str = "computed", out=None, lse=None, return_lse: bool = True,
                max_logit: Optional[float] = None, n_split: int = 1, workspace=None,
-               q_offset: int = 0, stream=None):
+               q_offset: int = 0, no_alloc: bool = False, stream=None):
     """Block-sparse attention forward on the GPU.
 
     q [B, Hq, L, d_qk], k [B, Hkv, L_kv, d_qk], v [B, Hkv, L_kv, d_v]:
@@ -242,7 +242,10 @@ def splash_fwd(q, k, v, *, scale: Optional[float] = None, soft_cap: float = 0.0,
     row's active kv blocks are cut into that many chunks computed as separate
     items and merged through their log-sum-exp (``splash_attn_fwd_split``);
     ``workspace`` is a device tensor of at least ``split_workspace_bytes``
-    bytes, allocated here when omitted.
+    bytes, allocated here when omitted.  ``no_alloc`` (with ``n_split`` > 1):
+    the partials go to the library's static device scratch instead
+    (``splash_attn_fwd_split_noalloc``; no workspace, calls on one device
+    must not overlap).
     """
     import torch
     lib = _lib.load()
@@ -296,7 +299,9 @@ def splash_fwd(q, k, v, *, scale: Optional[float] = None, soft_cap: float = 0.0,
         stream = torch.cuda.current_stream(q.device).cuda_stream
 
     ws_ptr, ws_bytes = None, 0
-    if n_split != 1:
+    if no_alloc and (n_split == 1 or workspace is not None):
+        raise ValueError("no_alloc is for the split-KV forward (n_split > 1) without a workspace")
+    if n_split != 1 and not no_alloc:
         need = split_workspace_bytes(n_split, 1 if per_batch else B, Hq, L, d_v)
         if workspace is None:
             workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
@@ -349,6 +354,9 @@ def splash_fwd(q, k, v, *, scale: Optional[float] = None, soft_cap: float = 0.0,
             L_kv, int(q_offset))
         if n_split == 1:
             _lib.check(lib.splash_attn_fwd(ctypes.byref(args), ctypes.c_void_p(stream)))
+        elif no_alloc:
+            _lib.check(lib.splash_attn_fwd_split_noalloc(ctypes.byref(args), int(n_split),
+                                                         ctypes.c_void_p(stream)))
         else:
             _lib.check(lib.splash_attn_fwd_split(ctypes.byref(args), int(n_split),
                                                  ctypes.c_void_p(ws_ptr), ctypes.c_int64(ws_bytes),

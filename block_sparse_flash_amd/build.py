@@ -31,6 +31,7 @@ SOURCES = [
     "splash_split_merge.hip",
     "splash_bwd_api.cpp",
     "splash_bwd_bf16.hip",
+    "splash_noalloc.hip",
 ]
 
 ARCH = "gfx950"

@@ -53,9 +53,13 @@
  *   - Return value: SPLASH_OK (0) or one of the SPLASH_E* codes below.  On an
  *     error nothing is written to any output and no kernel is launched;
  *     splash_last_error() returns a message for the calling thread.
- *   - No call allocates memory that outlives it, keeps global state between
- *     calls (other than the per-thread error message) or throws across the
- *     ABI.  The caller owns every buffer.
+ *   - No call allocates memory that outlives it or throws across the ABI,
+ *     and the caller owns every buffer.  State kept between calls: the
+ *     per-thread error message, a per-device cache of the compute-unit count
+ *     (read once from the runtime), and splash_attn_fwd_split_noalloc's
+ *     static device scratch.  The environment variable SPLASH_XCD_MAP=0
+ *     turns off the XCD-aware work-group order of the forward (for
+ *     comparisons; results are identical).
  *   - "host" pointers are CPU memory; "device" pointers are HIP device memory
  *     on the current device.
  */
@@ -68,10 +72,14 @@
 extern "C" {
 #endif
 
-#define SPLASH_VERSION 105
+#define SPLASH_VERSION 106
 
 /* Largest n_split of splash_attn_fwd_split. */
 #define SPLASH_MAX_SPLIT 64
+
+/* Bytes of the static device scratch of splash_attn_fwd_split_noalloc
+ * (16 MiB per device). */
+#define SPLASH_STATIC_SCRATCH_BYTES (16 << 20)
 
 enum splash_status {
   SPLASH_OK = 0,
@@ -328,6 +336,21 @@ int splash_split_workspace_bytes(int32_t n_split, int32_t B, int32_t Hq, int32_t
  * ordered on one stream. */
 int splash_attn_fwd_split(const splash_fwd_args* args, int32_t n_split, void* workspace,
                           int64_t workspace_bytes, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, serving loops, harnesses that forbid it): splash_attn_fwd_split
+ * with the workspace replaced by a static device array of
+ * SPLASH_STATIC_SCRATCH_BYTES that the library holds on each device it runs
+ * on until the process ends.  The caller still passes every input and
+ * output; nothing is allocated.  The first call on a device looks up that
+ * device's array (with the device current).  Every call on a device shares
+ * its array: calls that overlap on one device (other streams, other host
+ * threads) race and give wrong results; calls ordered on one stream do not.
+ * Nothing in the array needs clearing between calls.  Errors: those of
+ * splash_attn_fwd_split, plus SPLASH_EINVAL when the partials
+ * (splash_split_workspace_bytes) exceed SPLASH_STATIC_SCRATCH_BYTES and
+ * SPLASH_EHIP when the array's address cannot be obtained. */
+int splash_attn_fwd_split_noalloc(const splash_fwd_args* args, int32_t n_split, void* stream);
 
 /* ------------------------------------------------------------------------
  * Backward.
