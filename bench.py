@@ -305,7 +305,7 @@ def main():
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
     if args.tile:
         bq, bkv = (int(x) for x in args.tile.lower().split("x"))
-    elif w.tile and not args.backward and args.n_split == 1:
+    elif w.tile and not args.backward:
         bq, bkv = w.tile
     else:
         bq, bkv = fwd_tile(w.dtype, w.d_qk, w.d_v)

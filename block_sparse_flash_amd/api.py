@@ -211,6 +211,15 @@ def bwd_tile(dtype: str, d_qk: int, d_v: int):
     return bq.value, bkv.value
 
 
+def pick_tile(dtype: str, d_qk: int, d_v: int, L: int, group: int):
+    """The tile ``splash_fwd`` compiles tables for when none are given: the
+    64-row decode tile for few query rows per K/V head (its query heads are
+    packed into one row space when L is below the tile), else the default."""
+    if L <= 64 and (64, 64) in fwd_tiles(dtype, d_qk, d_v):
+        return (64, 64)
+    return fwd_tile(dtype, d_qk, d_v)
+
+
 def _torch_dtype_name(t):
     import torch
     if t.dtype == torch.bfloat16:
@@ -266,7 +275,8 @@ def splash_fwd(q, k, v, *, scale: Optional[float] = None, soft_cap: float = 0.0,
         scale = 1.0 / float(d_qk) ** 0.5
     # Tables given: their tile (the library checks a kernel exists for it);
     # else the default tile.
-    bq, bkv = (tables.block_q, tables.block_kv) if tables is not None else fwd_tile(dt, d_qk, d_v)
+    bq, bkv = ((tables.block_q, tables.block_kv) if tables is not None
+               else pick_tile(dt, d_qk, d_v, L, Hq // max(Hkv, 1)))
 
     seg_q_dev = seg_kv_dev = None
     per_batch = False

@@ -84,13 +84,18 @@ constexpr Tile bf16_default_tile(int d_qk, int d_v) {
 // Tiles of the plain forward (no split-KV, no packing) of 128/128 heads:
 // the block-size sweep of 128 or 256 rows by 64 or 128 keys.
 constexpr Tile kSweepTiles[4] = {{256, 64}, {256, 128}, {128, 64}, {128, 128}};
+// The decode tile of 128/128 heads: 64 query rows (two waves) by 64 keys,
+// with every variant (split-KV, packed GQA rows), for shapes with few query
+// rows per K/V head, where a 256-row tile would be mostly padding.
+constexpr Tile kDecodeTile = {64, 64};
 
-// Whether a bf16 forward instance exists for these head dims and tile;
-// `plain` = no split-KV and no packed rows.
-inline bool bf16_tile_built(int d_qk, int d_v, int bq, int bkv, bool plain) {
+// Whether a bf16 forward instance exists for these head dims and tile.
+inline bool bf16_tile_built(int d_qk, int d_v, int bq, int bkv, bool split) {
   const Tile d = bf16_default_tile(d_qk, d_v);
   if (bq == d.bq && bkv == d.bkv) return true;
-  if (!plain || d_qk != 128 || d_v != 128) return false;
+  if (d_qk != 128 || d_v != 128) return false;
+  if (bq == kDecodeTile.bq && bkv == kDecodeTile.bkv) return true;
+  if (split) return false;
   for (const Tile& t : kSweepTiles)
     if (t.bq == bq && t.bkv == bkv) return true;
   return false;

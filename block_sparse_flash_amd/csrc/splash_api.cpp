@@ -84,10 +84,14 @@ extern "C" int splash_fwd_tiles(int32_t dtype, int32_t d_qk, int32_t d_v, int32_
     ++n;
   };
   put(def_q, def_kv);
-  if (dtype == SPLASH_BF16)
+  if (dtype == SPLASH_BF16) {
     for (const splash::Tile& t : splash::kSweepTiles)
-      if (!(t.bq == def_q && t.bkv == def_kv) && splash::bf16_tile_built(d_qk, d_v, t.bq, t.bkv, true))
+      if (!(t.bq == def_q && t.bkv == def_kv) && splash::bf16_tile_built(d_qk, d_v, t.bq, t.bkv, false))
         put(t.bq, t.bkv);
+    const splash::Tile t = splash::kDecodeTile;
+    if (!(t.bq == def_q && t.bkv == def_kv) && splash::bf16_tile_built(d_qk, d_v, t.bq, t.bkv, false))
+      put(t.bq, t.bkv);
+  }
   *count = n;
   return SPLASH_OK;
 }
@@ -152,7 +156,7 @@ int prepare(const splash_fwd_args* args, const char* fn, bool split, splash::Fwd
   splash_fwd_tile(a.dtype, a.d_qk, a.d_v, &bq, &bkv);
   const bool default_tile = a.block_q == bq && a.block_kv == bkv;
   if (!default_tile) {
-    if (a.dtype != SPLASH_BF16 || !splash::bf16_tile_built(a.d_qk, a.d_v, a.block_q, a.block_kv, !split))
+    if (a.dtype != SPLASH_BF16 || !splash::bf16_tile_built(a.d_qk, a.d_v, a.block_q, a.block_kv, split))
       return splash::fail(SPLASH_ESHAPE, "%s: no kernel for tables of %dx%d blocks (default tile %dx%d)", fn,
                           a.block_q, a.block_kv, bq, bkv);
     bq = a.block_q;
@@ -229,7 +233,8 @@ int prepare(const splash_fwd_args* args, const char* fn, bool split, splash::Fwd
   p.row_period = 0;
   p.Lseg = a.L;
   splash_fwd_args placed = a;
-  if (a.dtype == SPLASH_BF16 && p.group > 1 && a.L < bq && default_tile) {
+  const bool decode_tile = bq == splash::kDecodeTile.bq && bkv == splash::kDecodeTile.bkv;
+  if (a.dtype == SPLASH_BF16 && p.group > 1 && a.L < bq && (default_tile || decode_tile)) {
     // All query rows fit one table row: pack the query heads of each K/V
     // group into one row space ([B, Hq, L, d] is [B, Hkv, group L, d]), so
     // that an item's row tile holds group * L rows instead of L.

@@ -1,6 +1,6 @@
 // bf16 forward: the 128/128 instances (every variant at the default tile and
-// the other tiles of the block-size sweep) and the launcher for all head
-// dims.  The kernel is in splash_fwd_bf16_kernel.h.
+// the decode tile, the plain forward at the other tiles of the block-size
+// sweep) and the launcher for all head dims.  The kernel is in splash_fwd_bf16_kernel.h.
 
 #include <atomic>
 
@@ -33,7 +33,10 @@ hipError_t launch_fwd_bf16(const FwdParams& p, int d_qk, int d_v, hipStream_t s)
     if (d_qk == 192) return launch_fwd_bf16_d192(p, d_v, n_cu, s);
     return launch_fwd_bf16_d64(p, d_qk, d_v, n_cu, s);
   }
-  if (d_qk != 128 || d_v != 128 || p.ws_o || p.row_period > 0) return hipErrorInvalidValue;
+  if (d_qk != 128 || d_v != 128) return hipErrorInvalidValue;
+  if (p.block_q == kDecodeTile.bq && p.block_kv == kDecodeTile.bkv)
+    return launch_all<128, 128, kDecodeTile.bkv, kDecodeTile.bq / 32>(p, n_cu, s);
+  if (p.ws_o || p.row_period > 0) return hipErrorInvalidValue;
   if (p.block_q == 256 && p.block_kv == 64 && !(def.bq == 256 && def.bkv == 64)) return launch_sweep<256, 64>(p, n_cu, s);
   if (p.block_q == 256 && p.block_kv == 128 && !(def.bq == 256 && def.bkv == 128)) return launch_sweep<256, 128>(p, n_cu, s);
   if (p.block_q == 128 && p.block_kv == 64) return launch_sweep<128, 64>(p, n_cu, s);

@@ -693,7 +693,7 @@ __device__ __forceinline__ void item_fwd(const FwdParams& p, int head, int r, in
     auto exps = [&](f32x16* sv, float mcv, auto copy, auto ncopy_tag) __attribute__((always_inline)) {
       constexpr int NCOPY = SIDX(ncopy_tag);
       const float eb = CAP ? capA - mcv : -mcv;
-      float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      float ps[4];
       sfor<0, 2 * NTILE>([&](auto i_) {
         constexpr int t = SIDX(i_) / 2;
         constexpr int c2 = SIDX(i_) % 2;
@@ -703,7 +703,10 @@ __device__ __forceinline__ void item_fwd(const FwdParams& p, int head, int r, in
           constexpr int q = 4 * SIDX(i_) + e2;   // pair index 0..15
           const float p0 = fast_exp2(fmaf(sv[t][8 * c2 + 2 * e2], ea, eb));
           const float p1 = fast_exp2(fmaf(sv[t][8 * c2 + 2 * e2 + 1], ea, eb));
-          ps[q & 3] += p0 + p1;
+          if constexpr (q < 4)
+            ps[q] = p0 + p1;
+          else
+            ps[q & 3] += p0 + p1;
           w[e2] = pack_bf16(p0, p1);
           if constexpr ((q + 1) * NCOPY / (8 * NTILE) > q * NCOPY / (8 * NTILE)) {
             // Keep each copy at its place between the exponentials.
@@ -975,8 +978,8 @@ void splash_fwd_bf16_kernel(FwdParams p) {
   }
 }
 
-// Grid size: one work-group per CU slot (8 waves per CU: one 8-wave or two
-// 4-wave work-groups) for masks whose rows cost what their block counts say
+// Grid size: one work-group per CU slot (8 waves per CU: one 8-wave work-group
+// or several smaller ones, as many as the LDS holds) for masks whose rows cost what their block counts say
 // (causal, windows), where the static round schedule is balanced; with
 // segment ids, rows mix partial and full blocks unevenly and the hardware's
 // dynamic dispatch of one work-group per item balances better (a grid of one
@@ -985,7 +988,10 @@ template <int DQK, int DV, int BN, int NW, bool CAP, bool SPLIT, bool PACK>
 hipError_t launch(const FwdParams& p, int n_cu, hipStream_t s) {
   const int64_t n_items = (int64_t)p.B * p.Hq * p.n_q_blocks * (SPLIT ? p.n_split : 1);
   const bool persistent = p.seg_q == nullptr;
-  const int64_t slots = (int64_t)n_cu * (8 / NW);
+  // Work-groups a CU holds at once: 8 waves, and the LDS (160 KiB).
+  constexpr int kPerCu = (8 / NW) < (163840 / Cfg<DQK, DV, BN>::LDS_BYTES) ? (8 / NW)
+                                                                          : (163840 / Cfg<DQK, DV, BN>::LDS_BYTES);
+  const int64_t slots = (int64_t)n_cu * kPerCu;
   const int64_t grid = (persistent && n_items > slots) ? slots : n_items;
   const int bytes = Cfg<DQK, DV, BN>::LDS_BYTES;
   auto fn = splash_fwd_bf16_kernel<DQK, DV, BN, NW, CAP, SPLIT, PACK>;
@@ -1008,15 +1014,19 @@ hipError_t launch_cap(const FwdParams& p, int n_cu, hipStream_t s) {
                            : launch<DQK, DV, BN, NW, false, false, PACK>(p, n_cu, s);
 }
 
-// Every variant (split-KV, packed GQA rows) at the head dims' default tile;
-// packed rows use their own instances, so that the unpacked kernels keep
-// their registers.
+// Every variant (split-KV, packed GQA rows) at one tile; packed rows use
+// their own instances, so that the unpacked kernels keep their registers.
+template <int DQK, int DV, int BN, int NW>
+hipError_t launch_all(const FwdParams& p, int n_cu, hipStream_t s) {
+  return p.row_period > 0 ? launch_cap<DQK, DV, BN, NW, true>(p, n_cu, s)
+                          : launch_cap<DQK, DV, BN, NW, false>(p, n_cu, s);
+}
+
+// Every variant at the head dims' default tile.
 template <int DQK, int DV>
 hipError_t launch_default(const FwdParams& p, int n_cu, hipStream_t s) {
   constexpr Tile t = bf16_default_tile(DQK, DV);
-  constexpr int NW = t.bq / 32;
-  return p.row_period > 0 ? launch_cap<DQK, DV, t.bkv, NW, true>(p, n_cu, s)
-                          : launch_cap<DQK, DV, t.bkv, NW, false>(p, n_cu, s);
+  return launch_all<DQK, DV, t.bkv, t.bq / 32>(p, n_cu, s);
 }
 
 // The plain forward (no split, no packing) of 128/128 heads at the other

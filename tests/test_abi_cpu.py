@@ -170,12 +170,12 @@ def test_fwd_tiles_and_bwd_tile():
     lib = _lib.load()
     t = fwd_tiles("bf16", 128, 128)
     assert t[0] == fwd_tile("bf16", 128, 128)
-    assert sorted(t) == [(128, 64), (128, 128), (256, 64), (256, 128)]
+    assert sorted(t) == [(64, 64), (128, 64), (128, 128), (256, 64), (256, 128)]
     for dims in [(192, 128), (192, 64), (64, 64), (128, 64), (64, 128)]:
         assert fwd_tiles("bf16", *dims) == [fwd_tile("bf16", *dims)]
     assert fwd_tiles("f32", 128, 128) == [(64, 64)]
     n = ctypes.c_int32()
-    assert lib.splash_fwd_tiles(1, 128, 128, None, None, 0, ctypes.byref(n)) == 0 and n.value == 4
+    assert lib.splash_fwd_tiles(1, 128, 128, None, None, 0, ctypes.byref(n)) == 0 and n.value == 5
     assert lib.splash_fwd_tiles(1, 128, 128, None, None, 2, ctypes.byref(n)) == 1
     assert lib.splash_fwd_tiles(1, 128, 128, None, None, 0, None) == 1
     assert lib.splash_fwd_tiles(1, 96, 128, None, None, 0, ctypes.byref(n)) == 4
@@ -188,8 +188,9 @@ def test_fwd_tiles_and_bwd_tile():
 
 @pytest.mark.parametrize("bq,bkv,d,code", [
     (256, 128, 128, 0), (128, 64, 128, 0), (128, 128, 128, 0),   # sweep tiles of 128/128
+    (64, 64, 128, 0),                                            # decode tile
     (256, 128, 64, 2), (128, 64, 64, 2),                         # not built for 64/64
-    (64, 64, 128, 2), (512, 64, 128, 2), (256, 32, 128, 2),
+    (64, 64, 64, 2), (512, 64, 128, 2), (256, 32, 128, 2),
 ])
 def test_forward_accepts_built_tiles_only(bq, bkv, d, code):
     """Validation accepts tables of any tile with a kernel and rejects the
@@ -291,7 +292,7 @@ def test_split_workspace_bytes():
     (dict(), 2, 0x20008, 1 << 30, 1),                 # misaligned workspace
     (dict(Hq=3, Hkv=2), 2, 0x20000, 1 << 30, 2),      # errors of splash_attn_fwd apply
     (dict(scale=0.0), 2, 0x20000, 1 << 30, 1),
-    (dict(block_kv=128), 2, 0x20000, 1 << 30, 2),     # split-KV: default tile only
+    (dict(block_kv=128), 2, 0x20000, 1 << 30, 2),     # split-KV: default and decode tiles only
 ])
 def test_split_forward_validation_errors(over, n_split, ws, ws_bytes, code):
     lib = _lib.load()

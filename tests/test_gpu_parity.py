@@ -319,6 +319,40 @@ def test_decode_shapes_every_element(case):
     _announce(f"  max-abs o {eo:.3g} lse {el:.3g}")
 
 
+DECODE_TILE_CASES = [c for c in DECODE_CASES if c[6] == 128 and c[7] == 128] + [
+    # (B, Hq, Hkv, L_q, L_kv, q_offset, d_qk, d_v, mask kwargs, soft_cap, mask_mode, n_split)
+    (1, 8, 1, 40, 2000, 1960, 128, 128, dict(causal=True), 0.0, "computed", 4),   # 320 packed rows
+    (1, 4, 4, 16, 2000, 1984, 128, 128, dict(causal=True, window_left=500), 10.0, "computed", 3),  # MHA
+    (1, 4, 1, 64, 1500, 1436, 128, 128, dict(causal=True, segs=(50, 400)), 0.0, "stored", 1),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_TILE_CASES,
+                         ids=lambda c: f"B{c[0]}H{c[1]}/{c[2]}-Lq{c[3]}-Lkv{c[4]}-off{c[5]}"
+                         f"-{c[10]}-s{c[11]}" + ("-cap" if c[9] else "") + "-" + "-".join(sorted(c[8])))
+def test_decode_tile_every_element(case):
+    """The 64-row decode tile (packed GQA rows, split-KV) against the oracle."""
+    B, Hq, Hkv, Lq, Lkv, off, dqk, dv, mk, cap, mode, S = case
+    _announce(f"decode tile {case}")
+    seed = 9500 + Lq + Lkv + S
+    q, k, v = (stored(a, "bf16")
+               for a in draw_qkv(B, Hq, Hkv, Lq, dqk, dv, seed, qk_std=1.5 if cap else 1.0, L_kv=Lkv))
+    mk = dict(mk)
+    seg_q = seg_kv = None
+    if "segs" in mk:
+        lo, hi = mk.pop("segs")
+        seg_kv = segment_ids(Lkv, seed, lo, hi)
+        seg_q = seg_kv[off:off + Lq].copy()
+    t = compile_mask(Lq, 64, 64, L_kv=Lkv, seg_q=seg_q, seg_kv=seg_kv, q_offset=off, **mk)
+    scale = 1.0 / math.sqrt(dqk)
+    o, lse = _run(q, k, v, scale=scale, soft_cap=cap, seg_q=seg_q, seg_kv=seg_kv, q_offset=off,
+                  mask_mode=mode, n_split=S, tables=t, **mk)
+    o_ref, lse_ref = attention_ref(as_f64(q), as_f64(k), as_f64(v), scale=scale, soft_cap=cap,
+                                   seg_q=seg_q, seg_kv=seg_kv, q_offset=off, **mk)
+    eo, el = _compare(o, lse, o_ref, lse_ref, "bf16")
+    _announce(f"  max-abs o {eo:.3g} lse {el:.3g}")
+
+
 def test_decode_full_length_gqa_split():
     """Decoding 16 new rows against a 32768-key cache: B=4, GQA 32/8, causal,
     q_offset = L_kv - L_q, split into 16 chunks; every row against the
@@ -444,7 +478,7 @@ def test_full_size_workloads_sampled(name, n_split):
     _announce(f"full-size {name} n_split={n_split}")
     q, k, v, seg = make_inputs(w)
     # The tile the bench times this workload at.
-    bq, bkv = w.tile if (w.tile and n_split == 1) else fwd_tile(w.dtype, w.d_qk, w.d_v)
+    bq, bkv = w.tile if w.tile else fwd_tile(w.dtype, w.d_qk, w.d_v)
     tabs = compile_mask(w.L, bq, bkv, L_kv=w.keys, causal=w.causal, window_left=w.window_left,
                         window_right=w.window_right, seg_q=seg, q_offset=w.q_offset)
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
