@@ -407,7 +407,8 @@ def splash_bwd(q, k, v, o, lse, dout, *, scale: Optional[float] = None, soft_cap
     gradient, shaped like o) are contiguous bfloat16 GPU tensors with the
     forward's shapes; ``lse`` is the forward's float32 lse [B, Hq, L]; the
     mask arguments are those of the forward.  Returns (dq, dk, dv) as float32
-    tensors shaped like q, k and v.  Head dims (64, 64) or (128, 128).
+    tensors shaped like q, k and v.  Head dims (64, 64), (128, 128) or
+    (192, 128).
     """
     import torch
     lib = _lib.load()

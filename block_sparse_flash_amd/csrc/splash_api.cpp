@@ -102,7 +102,7 @@ extern "C" int splash_bwd_tile(int32_t dtype, int32_t d_qk, int32_t d_v, int32_t
   if (!block_q || !block_kv) return splash::fail(SPLASH_EINVAL, "splash_bwd_tile: NULL output");
   if (dtype != SPLASH_F32 && dtype != SPLASH_BF16)
     return splash::fail(SPLASH_EDTYPE, "splash_bwd_tile: unknown dtype %d", dtype);
-  if (dtype != SPLASH_BF16 || !((d_qk == 64 && d_v == 64) || (d_qk == 128 && d_v == 128)))
+  if (dtype != SPLASH_BF16 || !splash::bwd_dims_built(d_qk, d_v))
     return splash::fail(SPLASH_EUNSUPPORTED, "splash_bwd_tile: no backward for dtype %d, head dims (%d, %d)",
                         dtype, d_qk, d_v);
   *block_q = splash::kBwdBlockQ;

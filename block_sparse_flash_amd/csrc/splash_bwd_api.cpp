@@ -25,7 +25,7 @@ extern "C" int splash_attn_bwd(const splash_bwd_args* args, void* stream) {
   if (a.dtype != SPLASH_F32 && a.dtype != SPLASH_BF16)
     return splash::fail(SPLASH_EDTYPE, "%s: unknown dtype %d", fn, a.dtype);
   if (a.dtype != SPLASH_BF16) return splash::fail(SPLASH_EUNSUPPORTED, "%s: bf16 only", fn);
-  if (!((a.d_qk == 64 && a.d_v == 64) || (a.d_qk == 128 && a.d_v == 128)))
+  if (!splash::bwd_dims_built(a.d_qk, a.d_v))
     return splash::fail(SPLASH_EUNSUPPORTED, "%s: head dims (%d, %d) not built", fn, a.d_qk, a.d_v);
   if (a.B < 0 || a.Hq < 0 || a.L < 0 || a.Hkv <= 0 || a.L_kv < 0 || a.q_offset < 0)
     return splash::fail(SPLASH_EINVAL, "%s: bad sizes B=%d Hq=%d Hkv=%d L=%d L_kv=%d q_offset=%d", fn,

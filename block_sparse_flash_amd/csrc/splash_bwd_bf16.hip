@@ -42,6 +42,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "bwd_params.h"
 #include "fwd_params.h"
 
@@ -284,7 +286,10 @@ struct DkdvLds {
 };
 
 template <int DQK, int DV, bool CAP>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// Two work-groups per CU where their LDS fits (then 256 registers per
+// lane), else one with the whole register file.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DkdvLds<DQK, DV>::BYTES <= 81920 ? 2 : 1,
+                                                                     DkdvLds<DQK, DV>::BYTES <= 81920 ? 2 : 1)))
 void bwd_dkdv_kernel(BwdParams p) {
   using M = DkdvLds<DQK, DV>;
   using LQ = Lay<DQK, true>;
@@ -334,10 +339,10 @@ void bwd_dkdv_kernel(BwdParams p) {
   if (p.window_right >= 0) rlo = max(rlo, my_key - p.window_right - p.q_off);
   if (p.window_left >= 0) rhi = min(rhi, my_key + p.window_left - p.q_off);
 
-  static_assert(DQK == DV, "one accumulator shape for dK and dV");
-  f32x16 acc[NQ];  // dK or dV of this wave's 32 keys
+  constexpr int NA = NQ > NV ? NQ : NV;
+  f32x16 acc[NA];  // dK (NQ tiles) or dV (NV tiles) of this wave's 32 keys
 #pragma unroll
-  for (int i = 0; i < NQ; ++i) acc[i] = f32x16{};
+  for (int i = 0; i < NA; ++i) acc[i] = f32x16{};
 
   const int x0 = p.col_ptr[c];
   const int x1 = p.col_ptr[c + 1];
@@ -420,16 +425,23 @@ void bwd_dkdv_kernel(BwdParams p) {
     for (int rt = 0; rt < 2; ++rt) {
       f32x16 s = f32x16{}, dp = f32x16{};
       if (dk_wave) {
-        pipelined<DQK / 16, 0>(
+        // S takes DQK / 16 k-steps, dP DV / 16.
+        pipelined<(DQK > DV ? DQK : DV) / 16, 0>(
             [&](int st) {
-              return Op4{ld_op(Qs + LQ::off(32 * rt + l32, 2 * st + hi)),
-                         ld_op(Ks + LQ::off(32 * kh + l32, 2 * st + hi)),
-                         ld_op(Os + LV::off(32 * rt + l32, 2 * st + hi)),
-                         ld_op(Vs + LV::off(32 * kh + l32, 2 * st + hi))};
+              Op4 o{};
+              if (st < DQK / 16) {
+                o.a = ld_op(Qs + LQ::off(32 * rt + l32, 2 * st + hi));
+                o.b = ld_op(Ks + LQ::off(32 * kh + l32, 2 * st + hi));
+              }
+              if (st < DV / 16) {
+                o.c = ld_op(Os + LV::off(32 * rt + l32, 2 * st + hi));
+                o.d = ld_op(Vs + LV::off(32 * kh + l32, 2 * st + hi));
+              }
+              return o;
             },
-            [&](int, const Op4& o) {
-              s = mfma(o.a, o.b, s);
-              dp = mfma(o.c, o.d, dp);
+            [&](int st, const Op4& o) {
+              if (st < DQK / 16) s = mfma(o.a, o.b, s);
+              if (st < DV / 16) dp = mfma(o.c, o.d, dp);
             });
       } else {
         pipelined<DQK / 16, 0>(
@@ -476,39 +488,64 @@ void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
           for (int j = 0; j < 8; ++j) a8[ks][j] = (__bf16)pv[8 * ks + j];
       }
-      const lds_u16* src = dk_wave ? Qs : Os;  // B operand rows: Q for dK, dO for dV
-      pipelined<2 * NQ, 1>(
-          [&](int i) {
-            const int rr = 32 * rt + 16 * (i / NQ) + trow;
-            const int col = 32 * (i % NQ) + tcol;
-            return ld_tr(src + LQ::at(rr, col), src + LQ::at(rr + 8, col));
-          },
-          [&](int i, const bf16x8& bo) { acc[i % NQ] = mfma(a8[i / NQ], bo, acc[i % NQ]); });
+      // B operand rows: Q (laid out by LB = LQ) for dK, dO (LV) for dV, NT
+      // tiles of 32 columns.
+      auto accumulate = [&](auto nt_, auto lay_, const lds_u16* src) __attribute__((always_inline)) {
+        constexpr int NT = decltype(nt_)::value;
+        using LB = decltype(lay_);
+        pipelined<2 * NT, 1>(
+            [&](int i) {
+              const int rr = 32 * rt + 16 * (i / NT) + trow;
+              const int col = 32 * (i % NT) + tcol;
+              return ld_tr(src + LB::at(rr, col), src + LB::at(rr + 8, col));
+            },
+            [&](int i, const bf16x8& bo) { acc[i % NT] = mfma(a8[i / NT], bo, acc[i % NT]); });
+      };
+      if constexpr (DQK == DV) {
+        accumulate(std::integral_constant<int, NQ>{}, LQ{}, dk_wave ? Qs : Os);
+      } else if (dk_wave) {
+        accumulate(std::integral_constant<int, NQ>{}, LQ{}, Qs);
+      } else {
+        accumulate(std::integral_constant<int, NV>{}, LV{}, Os);
+      }
     }
   }
 
-  // Each wave writes its 32 keys: dK (times the scale) or dV.
-  float* outg = (dk_wave ? p.dk : p.dv) + (int64_t)bk * p.Lkv * DQK;
-  const float osc = dk_wave ? p.scale : 1.0f;
+  // Each wave writes its 32 keys: dK (times the scale, D = DQK) or dV (D = DV).
+  auto write = [&](auto d_, float* outg, float osc) __attribute__((always_inline)) {
+    constexpr int D = decltype(d_)::value;
+    outg += (int64_t)bk * p.Lkv * D;
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const int key = key0 + 32 * kh + 8 * (e / 4) + 4 * hi + (e % 4);
-    if (key < p.Lkv) {
+    for (int e = 0; e < 16; ++e) {
+      const int key = key0 + 32 * kh + 8 * (e / 4) + 4 * hi + (e % 4);
+      if (key < p.Lkv) {
 #pragma unroll
-      for (int t = 0; t < NQ; ++t) outg[(int64_t)key * DQK + 32 * t + l32] = osc * acc[t][e];
+        for (int t = 0; t < D / 32; ++t) outg[(int64_t)key * D + 32 * t + l32] = osc * acc[t][e];
+      }
     }
+  };
+  if constexpr (DQK == DV) {
+    write(std::integral_constant<int, DQK>{}, dk_wave ? p.dk : p.dv, dk_wave ? p.scale : 1.0f);
+  } else if (dk_wave) {
+    write(std::integral_constant<int, DQK>{}, p.dk, p.scale);
+  } else {
+    write(std::integral_constant<int, DV>{}, p.dv, 1.0f);
   }
 }
 
 template <int DQK, int DV>
 struct DqLds {
+  // Q rows of 192-wide heads wait in LDS rather than in registers, which
+  // cannot hold them next to dO and the dQ accumulators at 8 waves per CU.
+  static constexpr bool Q_IN_LDS = DQK > 128;
   static constexpr int RK = Lay<DQK, true>::ROW;
   static constexpr int RV = Lay<DV, true>::ROW;
   static constexpr int K_OFF = 0;                      // K [64][RK]
   static constexpr int V_OFF = K_OFF + 64 * RK * 2;    // V [64][RV]
   static constexpr int SEG_OFF = V_OFF + 64 * RV * 2;  // key segment ids [64]
-  static constexpr int BYTES = SEG_OFF + 64 * 4;
-  static_assert(BYTES <= 65536, "default LDS allocation");
+  static constexpr int Q_OFF = SEG_OFF + 64 * 4;       // Q [BQ][RK] when Q_IN_LDS
+  static constexpr int BYTES = Q_OFF + (Q_IN_LDS ? BQ * RK * 2 : 0);
+  static_assert(BYTES <= 163840, "fits the LDS of a CU");
 };
 
 template <int DQK, int DV, bool CAP>
@@ -523,6 +560,7 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
   lds_u16* Ks = (lds_u16*)(lds + M::K_OFF);
   lds_u16* Vs = (lds_u16*)(lds + M::V_OFF);
   lds_i32* segks = (lds_i32*)(lds + M::SEG_OFF);
+  lds_u16* Qs = (lds_u16*)(lds + M::Q_OFF);
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -546,12 +584,18 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
   const uint16_t* vg = static_cast<const uint16_t*>(p.v) + (int64_t)bk * p.Lkv * DV;
 
   // Q and dO of this lane's row as B operands: k-step s -> elements 16s + 8hi .. + 7.
-  bf16x8 qf[DQK / 16], df[DV / 16];
+  // With Q in LDS each lane stores the chunks it reads back later (row
+  // 32 wave + l32, chunks 2s + hi), so no barrier orders them.
+  constexpr bool QL = M::Q_IN_LDS;
+  bf16x8 qf[QL ? 1 : DQK / 16], df[DV / 16];
 #pragma unroll
   for (int st = 0; st < DQK / 16; ++st) {
     u32x4 v = {0u, 0u, 0u, 0u};
     if (in) v = *reinterpret_cast<const u32x4*>(qg + (int64_t)qi * DQK + 16 * st + 8 * hi);
-    qf[st] = __builtin_bit_cast(bf16x8, v);
+    if constexpr (QL)
+      *reinterpret_cast<lds_u32x4*>(Qs + LQ::off(32 * wave + l32, 2 * st + hi)) = v;
+    else
+      qf[st] = __builtin_bit_cast(bf16x8, v);
   }
 #pragma unroll
   for (int st = 0; st < DV / 16; ++st) {
@@ -603,15 +647,18 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
     for (int t = 0; t < 2; ++t) {
       // S^T = K Q^T and dP^T = V dO^T (interleaved chains): keys 32t + items, row l32.
       f32x16 s = f32x16{}, dp = f32x16{};
-      static_assert(DQK == DV, "S and dP take the same number of k-steps");
-      pipelined<DQK / 16, 1>(
+      // S takes DQK / 16 k-steps, dP DV / 16.
+      pipelined<(DQK > DV ? DQK : DV) / 16, 1>(
           [&](int st) {
-            return Op2{ld_op(Ks + LQ::off(32 * t + l32, 2 * st + hi)),
-                       ld_op(Vs + LV::off(32 * t + l32, 2 * st + hi))};
+            Op4 o{};
+            if (st < DQK / 16) o.a = ld_op(Ks + LQ::off(32 * t + l32, 2 * st + hi));
+            if (st < DV / 16) o.b = ld_op(Vs + LV::off(32 * t + l32, 2 * st + hi));
+            if (QL && st < DQK / 16) o.c = ld_op(Qs + LQ::off(32 * wave + l32, 2 * st + hi));
+            return o;
           },
-          [&](int st, const Op2& o) {
-            s = mfma(o.a, qf[st], s);
-            dp = mfma(o.b, df[st], dp);
+          [&](int st, const Op4& o) {
+            if (st < DQK / 16) s = mfma(o.a, QL ? o.c : qf[QL || st >= DQK / 16 ? 0 : st], s);
+            if (st < DV / 16) dp = mfma(o.b, df[st < DV / 16 ? st : 0], dp);
           });
       float pv[16], dsv[16];
 #pragma unroll
@@ -674,6 +721,11 @@ hipError_t launch_all(const BwdParams& p, hipStream_t s) {
   if (n_q_items > 0) {
     constexpr int bytes = DqLds<DQK, DV>::BYTES;
     auto fn = bwd_dq_kernel<DQK, DV, CAP>;
+    if (bytes > 65536) {
+      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+      if (e != hipSuccess) return e;
+    }
     hipLaunchKernelGGL(fn, dim3((unsigned)n_q_items), dim3(512), bytes, s, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -691,6 +743,7 @@ hipError_t launch_cap(const BwdParams& p, hipStream_t s) {
 hipError_t launch_bwd_bf16(const BwdParams& p, int d_qk, int d_v, hipStream_t s) {
   if (d_qk == 128 && d_v == 128) return launch_cap<128, 128>(p, s);
   if (d_qk == 64 && d_v == 64) return launch_cap<64, 64>(p, s);
+  if (d_qk == 192 && d_v == 128) return launch_cap<192, 128>(p, s);
   return hipErrorInvalidValue;
 }
 

@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define SPLASH_VERSION 106
+#define SPLASH_VERSION 107
 
 /* Largest n_split of splash_attn_fwd_split. */
 #define SPLASH_MAX_SPLIT 64
@@ -371,7 +371,8 @@ int splash_attn_fwd_split_noalloc(const splash_fwd_args* args, int32_t n_split, 
 /* Block sizes (block_q, block_kv) of the backward kernels, which its tables
  * (and their column view) must be compiled with; they may differ from the
  * forward's default tile.  Errors: SPLASH_EDTYPE, SPLASH_EUNSUPPORTED (not
- * bf16 with head dims (64, 64) or (128, 128)), SPLASH_EINVAL (NULL outputs). */
+ * bf16 with head dims (64, 64), (128, 128) or (192, 128)), SPLASH_EINVAL
+ * (NULL outputs). */
 int splash_bwd_tile(int32_t dtype, int32_t d_qk, int32_t d_v,
                     int32_t* block_q, int32_t* block_kv);
 
@@ -381,7 +382,7 @@ typedef struct splash_bwd_args {
   int32_t L;             /* query rows */
   int32_t L_kv;          /* key positions; 0: equal to L */
   int32_t q_offset;      /* query row i sits at key position q_offset + i */
-  int32_t d_qk, d_v;     /* (64, 64) or (128, 128) */
+  int32_t d_qk, d_v;     /* (64, 64), (128, 128) or (192, 128) */
   const void* q;         /* device [B, Hq, L, d_qk] */
   const void* k;         /* device [B, Hkv, L_kv, d_qk] */
   const void* v;         /* device [B, Hkv, L_kv, d_v] */

@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
     assert set(declared) == set(_lib.EXPORTED), declared
     for name in declared:
         assert hasattr(lib, name), name
-    assert lib.splash_version() == 106
+    assert lib.splash_version() == 107
 
 
 def _assert_tables_equal(t, ref):
@@ -181,7 +181,10 @@ def test_fwd_tiles_and_bwd_tile():
     assert lib.splash_fwd_tiles(1, 96, 128, None, None, 0, ctypes.byref(n)) == 4
     assert bwd_tile("bf16", 128, 128) == (256, 64) and bwd_tile("bf16", 64, 64) == (256, 64)
     a, b = ctypes.c_int32(), ctypes.c_int32()
-    assert lib.splash_bwd_tile(1, 192, 128, ctypes.byref(a), ctypes.byref(b)) == 4
+    assert lib.splash_bwd_tile(1, 192, 128, ctypes.byref(a), ctypes.byref(b)) == 0
+    assert (a.value, b.value) == (256, 64)
+    assert lib.splash_bwd_tile(1, 192, 64, ctypes.byref(a), ctypes.byref(b)) == 4
+    assert lib.splash_bwd_tile(1, 128, 64, ctypes.byref(a), ctypes.byref(b)) == 4
     assert lib.splash_bwd_tile(0, 128, 128, ctypes.byref(a), ctypes.byref(b)) == 4
     assert lib.splash_bwd_tile(3, 128, 128, ctypes.byref(a), ctypes.byref(b)) == 3
 
@@ -356,7 +359,8 @@ def _good_bwd(**over):
 @pytest.mark.parametrize("over,code", [
     (dict(dtype=5), 3),
     (dict(dtype=0), 4),                         # bf16 only
-    (dict(d_qk=192), 4),
+    (dict(d_qk=192, d_v=64), 4),
+    (dict(d_qk=128, d_v=192), 4),
     (dict(d_qk=64, d_v=128), 4),
     (dict(B=-1), 1),
     (dict(Hkv=0), 1),

@@ -42,11 +42,13 @@ def _check(name, got, ref):
 
 
 def _run_case(B, Hq, Hkv, Lq, Lkv, d, mk, cap, seed, q_offset=0, seg_q=None, seg_kv=None):
-    q, k, v = (stored(a, "bf16") for a in draw_qkv(B, Hq, Hkv, Lq, d, d, seed,
+    """d: the head dim of q, k and v, or a pair (d_qk, d_v)."""
+    d_qk, d_v = (d, d) if isinstance(d, int) else d
+    q, k, v = (stored(a, "bf16") for a in draw_qkv(B, Hq, Hkv, Lq, d_qk, d_v, seed,
                                                    qk_std=1.5 if cap else 1.0, L_kv=Lkv))
     rng = np.random.default_rng(seed + 99)
-    do = stored(rng.standard_normal((B, Hq, Lq, d), dtype=np.float32), "bf16")
-    scale = 1.0 / math.sqrt(d)
+    do = stored(rng.standard_normal((B, Hq, Lq, d_v), dtype=np.float32), "bf16")
+    scale = 1.0 / math.sqrt(d_qk)
     qd, kd, vd, dod = q.cuda(), k.cuda(), v.cuda(), do.cuda()
     o, lse = splash_fwd(qd, kd, vd, scale=scale, soft_cap=cap, seg_q=seg_q, seg_kv=seg_kv,
                         q_offset=q_offset, **mk)
@@ -71,17 +73,26 @@ CASES = [
     # d = 128 with documents and the cap (the build of the documents workload)
     (1, 4, 1, 900, 128, dict(causal=True), 50.0, (40, 300)),
     (1, 4, 2, 640, 128, dict(causal=True, window_left=150), 20.0, (30, 200)),
+    # 192-wide q/k heads with 128-wide v
+    (1, 4, 2, 700, (192, 128), dict(causal=True), 0.0, None),
+    (2, 2, 1, 333, (192, 128), dict(), 0.0, None),
+    (1, 4, 1, 900, (192, 128), dict(causal=True), 50.0, (40, 300)),
+    (1, 2, 2, 600, (192, 128), dict(causal=True, window_left=120, window_right=7), 0.0, None),
 ]
 
 
-@pytest.mark.parametrize("case", CASES, ids=lambda c: f"B{c[0]}H{c[1]}/{c[2]}-L{c[3]}-d{c[4]}"
+def _dims(d):
+    return f"d{d}" if isinstance(d, int) else f"d{d[0]}x{d[1]}"
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"B{c[0]}H{c[1]}/{c[2]}-L{c[3]}-{_dims(c[4])}"
                          + ("-cap" if c[6] else "") + ("-seg" if c[7] else "") + "-"
                          + "-".join(sorted(c[5])))
 def test_backward_every_element(case):
     B, Hq, Hkv, L, d, mk, cap, segs = case
     _announce(f"backward {case}")
     seg = None if segs is None else segment_ids(L, 500 + L, *segs)
-    _run_case(B, Hq, Hkv, L, L, d, mk, cap, 500 + L + d, seg_q=seg)
+    _run_case(B, Hq, Hkv, L, L, d, mk, cap, 500 + L + (d if isinstance(d, int) else sum(d)), seg_q=seg)
 
 
 def test_backward_decode_positions_and_empty_rows():
@@ -91,6 +102,8 @@ def test_backward_decode_positions_and_empty_rows():
     _run_case(1, 4, 2, 40, 900, 128, dict(causal=True), 0.0, 61, q_offset=860)
     _announce("backward rows without keys Lq=64 Lkv=700 off=900")
     _run_case(1, 2, 2, 64, 700, 64, dict(causal=True, window_left=250), 0.0, 62, q_offset=900)
+    _announce("backward decode d192x128 Lq=100 Lkv=800 off=700")
+    _run_case(1, 4, 1, 100, 800, (192, 128), dict(causal=True), 0.0, 63, q_offset=700)
 
 
 def test_backward_per_batch_segments():
@@ -175,5 +188,29 @@ def test_backward_documents_workload_whole_documents():
                  _check("dv", dv[:, kh:kh + 1, s0:s1], rdv))
             _announce(f"  document {di} rows [{s0}, {s1}) K/V head {kh}: relative max-abs errors "
                       f"dq {e[0]:.3g} dk {e[1]:.3g} dv {e[2]:.3g}")
+    for t in (dq, dk, dv):
+        assert bool(torch.isfinite(t).all())
+
+
+def test_backward_wide_head_full_size_sampled_heads():
+    """The 192/128 dense causal workload (L=4096, B=1, Hq=Hkv=128) at full
+    size: every gradient element of two heads against the oracle."""
+    from block_sparse_flash_amd.inputs import ALL_WORKLOADS, make_inputs
+    w = ALL_WORKLOADS["causal_mha_bf16_L4096_d192"]
+    _announce(f"backward full size {w.name}")
+    q, k, v, _ = make_inputs(w)
+    g = torch.Generator().manual_seed(w.seed + 1)
+    do = torch.randn((w.B, w.Hq, w.L, w.d_v), generator=g).to(torch.bfloat16)
+    qd, kd, vd, dod = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    o, lse = splash_fwd(qd, kd, vd, causal=True)
+    dq, dk, dv = splash_bwd(qd, kd, vd, o, lse, dod, causal=True)
+    torch.cuda.synchronize()
+    assert dq.shape == q.shape and dk.shape == k.shape and dv.shape == v.shape
+    for b, h in [(0, 5), (0, 127)]:
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        rdq, rdk, rdv = attention_bwd_ref(as_f64(q[sl]), as_f64(k[sl]), as_f64(v[sl]), as_f64(do[sl]),
+                                          scale=w.softmax_scale, causal=True)
+        e = (_check("dq", dq[sl], rdq), _check("dk", dk[sl], rdk), _check("dv", dv[sl], rdv))
+        _announce(f"  head ({b}, {h}): relative max-abs errors dq {e[0]:.3g} dk {e[1]:.3g} dv {e[2]:.3g}")
     for t in (dq, dk, dv):
         assert bool(torch.isfinite(t).all())
