@@ -20,16 +20,20 @@
 //     every query head of the GQA group, in 64-row sub-tiles, so dk and dv
 //     are summed in registers with no atomics.  Wave w owns keys
 //     32 (w % 2) .. + 31 and accumulates dV (w < 2) or dK (w >= 2) over all
-//     rows: 64 accumulator registers per wave, so two waves fit per SIMD
-//     (both dK and dV in one wave take 128, and then only one fits).
-//     S = Q K^T (and dP = dO V^T in the dK waves) come out of
-//     v_mfma_f32_32x32x16_bf16 with one key per lane and 16 rows per lane;
-//     those accumulator items, rounded to bf16, are directly the A operand
-//     of dV += P^T dO or dK += dS^T Q (the MFMA's reduction index runs over
-//     the rows in the order the accumulator holds them), and the B operands
-//     are read transposed from the row-major Q and dO tiles with
-//     ds_read_b64_tr_b16 (four consecutive rows of one column per lane, the
-//     row grouping the accumulator implies).
+//     rows: 64 accumulator registers per wave, so two work-groups fit per
+//     CU (both dK and dV in one wave take 128 and spill).  Each wave
+//     computes S = Q K^T, dP = dO V^T, P and dS only for its half of the
+//     sub-tile's rows (rows 32 (w / 2) .. + 31), so every element is
+//     computed once; the two waves of a key half then swap the part the
+//     other needs (P to the dV wave, dS to the dK wave) through LDS.
+//     S and dP come out of v_mfma_f32_32x32x16_bf16 with one key per lane
+//     and 16 rows per lane; those accumulator items, rounded to bf16, are
+//     directly the A operand of dV += P^T dO or dK += dS^T Q (the MFMA's
+//     reduction index runs over the rows in the order the accumulator holds
+//     them; the partner's lane of the same index holds its rows in the same
+//     order), and the B operands are read transposed from the row-major Q
+//     and dO tiles with ds_read_b64_tr_b16 (four consecutive rows of one
+//     column per lane, the row grouping the accumulator implies).
 //   * dq kernel: one work-group (8 waves, 32 rows each) per (query head,
 //     256-row q block) walks the row's active kv blocks; S^T = K Q^T and
 //     dP^T = V dO^T hold one row per lane, and dS^T feeds dQ += dS K the same
@@ -272,6 +276,7 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
 
 template <int DQK, int DV>
 struct DkdvLds {
+  static constexpr int NQ = DQK / 32, NV = DV / 32;
   static constexpr int RK = Lay<DQK, true>::ROW;
   static constexpr int RV = Lay<DV, true>::ROW;
   static constexpr int K_OFF = 0;                          // K [64][RK]
@@ -281,7 +286,8 @@ struct DkdvLds {
   static constexpr int LSE_OFF = O_OFF + 64 * RV * 2;      // lse * log2(e) [64]
   static constexpr int D_OFF = LSE_OFF + 64 * 4;           // D [64]
   static constexpr int SEG_OFF = D_OFF + 64 * 4;           // row segment ids [64]
-  static constexpr int BYTES = SEG_OFF + 64 * 4;
+  static constexpr int X_OFF = SEG_OFF + 64 * 4;           // P or dS handed over [4 waves][64 lanes][16 bf16]
+  static constexpr int BYTES = X_OFF + 4 * 64 * 32;
   static_assert(BYTES <= 163840, "fits the LDS of a CU");
 };
 
@@ -311,8 +317,13 @@ void bwd_dkdv_kernel(BwdParams p) {
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
-  const int kh = wave & 1;              // key half of the block
-  const bool dk_wave = (wave >> 1) != 0;  // wave-uniform: accumulates dK (else dV)
+  const int kh = wave & 1;   // key half of the block
+  const int rh = wave >> 1;  // row half of each 64-row sub-tile whose S and dP this wave computes
+  const bool dk_wave = rh != 0;  // wave-uniform: accumulates dK (else dV)
+  // This wave's hand-over slot (32 bytes per lane) and its partner's, the
+  // wave of the same keys and the other row half.
+  lds_u32x4* xme = (lds_u32x4*)(lds + M::X_OFF) + (wave * 64 + lane) * 2;
+  const lds_u32x4* xpart = (const lds_u32x4*)(lds + M::X_OFF) + ((wave ^ 2) * 64 + lane) * 2;
   // Transposed-read address of this lane: row 4 hi + (lane % 16) / 4 of a
   // 16-row step, columns 16 ((lane / 16) % 2) + 4 (lane % 4) of a 32-column tile.
   const int trow = 4 * hi + ((lane & 15) >> 2);
@@ -418,96 +429,92 @@ void bwd_dkdv_kernel(BwdParams p) {
     have = next(&next_g, &next_row0);
     if (have) fetch(next_g, next_row0);
 
-    // Two row tiles of 32 rows each.  S = Q K^T (and dP = dO V^T in the dK
-    // waves, as a second interleaved chain): one key per lane, rows
-    // 32 rt + items.
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      f32x16 s = f32x16{}, dp = f32x16{};
-      if (dk_wave) {
-        // S takes DQK / 16 k-steps, dP DV / 16.
-        pipelined<(DQK > DV ? DQK : DV) / 16, 0>(
-            [&](int st) {
-              Op4 o{};
-              if (st < DQK / 16) {
-                o.a = ld_op(Qs + LQ::off(32 * rt + l32, 2 * st + hi));
-                o.b = ld_op(Ks + LQ::off(32 * kh + l32, 2 * st + hi));
-              }
-              if (st < DV / 16) {
-                o.c = ld_op(Os + LV::off(32 * rt + l32, 2 * st + hi));
-                o.d = ld_op(Vs + LV::off(32 * kh + l32, 2 * st + hi));
-              }
-              return o;
-            },
-            [&](int st, const Op4& o) {
-              if (st < DQK / 16) s = mfma(o.a, o.b, s);
-              if (st < DV / 16) dp = mfma(o.c, o.d, dp);
-            });
-      } else {
-        pipelined<DQK / 16, 0>(
-            [&](int st) {
-              return Op2{ld_op(Qs + LQ::off(32 * rt + l32, 2 * st + hi)),
-                         ld_op(Ks + LQ::off(32 * kh + l32, 2 * st + hi))};
-            },
-            [&](int, const Op2& o) { s = mfma(o.a, o.b, s); });
-      }
-
-      // Row data of the 16 rows 32 rt + 8 (e / 4) + 4 hi + e % 4 (four runs of 4).
-      float pv[16], dsv[16];
-      const bool all_ok = all_allowed(p, row0 + 32 * rt, 32, key0 + 32 * kh, 32);  // wave-uniform
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int rl0 = 32 * rt + 8 * q4 + 4 * hi;
-        const f32x4 l4 = *reinterpret_cast<const lds_f32x4*>(lse2s + rl0);
-        const f32x4 d4 = *reinterpret_cast<const lds_f32x4*>(Ds + rl0);
-        if (all_ok) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            p_and_ds<CAP>(p, true, s[4 * q4 + j], l4[j], dp[4 * q4 + j], d4[j], &pv[4 * q4 + j], &dsv[4 * q4 + j]);
-        } else {
-          const i32x4 s4 = *reinterpret_cast<const lds_i32x4*>(segqs + rl0);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int row = row0 + rl0 + j;
-            const bool ok = (row >= rlo) & (row <= rhi) & (!has_seg || s4[j] == kseg);
-            p_and_ds<CAP>(p, ok, s[4 * q4 + j], l4[j], dp[4 * q4 + j], d4[j], &pv[4 * q4 + j], &dsv[4 * q4 + j]);
+    // S = Q K^T and dP = dO V^T on rows 32 rh .. + 31 of the sub-tile and
+    // the wave's 32 keys (two interleaved chains; S takes DQK / 16 k-steps,
+    // dP DV / 16): one key per lane, rows 32 rh + items.
+    f32x16 s = f32x16{}, dp = f32x16{};
+    pipelined<(DQK > DV ? DQK : DV) / 16, 0>(
+        [&](int st) {
+          Op4 o{};
+          if (st < DQK / 16) {
+            o.a = ld_op(Qs + LQ::off(32 * rh + l32, 2 * st + hi));
+            o.b = ld_op(Ks + LQ::off(32 * kh + l32, 2 * st + hi));
           }
+          if (st < DV / 16) {
+            o.c = ld_op(Os + LV::off(32 * rh + l32, 2 * st + hi));
+            o.d = ld_op(Vs + LV::off(32 * kh + l32, 2 * st + hi));
+          }
+          return o;
+        },
+        [&](int st, const Op4& o) {
+          if (st < DQK / 16) s = mfma(o.a, o.b, s);
+          if (st < DV / 16) dp = mfma(o.c, o.d, dp);
+        });
+
+    // Row data of the 16 rows 32 rh + 8 (e / 4) + 4 hi + e % 4 (four runs of 4).
+    float pv[16], dsv[16];
+    const bool all_ok = all_allowed(p, row0 + 32 * rh, 32, key0 + 32 * kh, 32);  // wave-uniform
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int rl0 = 32 * rh + 8 * q4 + 4 * hi;
+      const f32x4 l4 = *reinterpret_cast<const lds_f32x4*>(lse2s + rl0);
+      const f32x4 d4 = *reinterpret_cast<const lds_f32x4*>(Ds + rl0);
+      if (all_ok) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          p_and_ds<CAP>(p, true, s[4 * q4 + j], l4[j], dp[4 * q4 + j], d4[j], &pv[4 * q4 + j], &dsv[4 * q4 + j]);
+      } else {
+        const i32x4 s4 = *reinterpret_cast<const lds_i32x4*>(segqs + rl0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int row = row0 + rl0 + j;
+          const bool ok = (row >= rlo) & (row <= rhi) & (!has_seg || s4[j] == kseg);
+          p_and_ds<CAP>(p, ok, s[4 * q4 + j], l4[j], dp[4 * q4 + j], d4[j], &pv[4 * q4 + j], &dsv[4 * q4 + j]);
         }
       }
-      // dV += P^T dO (dV waves) or dK += dS^T Q (dK waves) over these 32
-      // rows: two k-steps (ks) of NQ tiles.
-      bf16x8 a8[2];
-      if (dk_wave) {
+    }
+    // P and dS of these 32 rows as bf16 A operands (two k-steps of 16 rows
+    // each).  The dV wave keeps P and hands dS to the dK wave of its keys;
+    // the dK wave keeps dS and hands P over.
+    bf16x8 pa[2], da[2];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-          for (int j = 0; j < 8; ++j) a8[ks][j] = (__bf16)dsv[8 * ks + j];
-      } else {
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-          for (int j = 0; j < 8; ++j) a8[ks][j] = (__bf16)pv[8 * ks + j];
+      for (int j = 0; j < 8; ++j) {
+        pa[ks][j] = (__bf16)pv[8 * ks + j];
+        da[ks][j] = (__bf16)dsv[8 * ks + j];
       }
-      // B operand rows: Q (laid out by LB = LQ) for dK, dO (LV) for dV, NT
-      // tiles of 32 columns.
-      auto accumulate = [&](auto nt_, auto lay_, const lds_u16* src) __attribute__((always_inline)) {
-        constexpr int NT = decltype(nt_)::value;
-        using LB = decltype(lay_);
-        pipelined<2 * NT, 1>(
-            [&](int i) {
-              const int rr = 32 * rt + 16 * (i / NT) + trow;
-              const int col = 32 * (i % NT) + tcol;
-              return ld_tr(src + LB::at(rr, col), src + LB::at(rr + 8, col));
-            },
-            [&](int i, const bf16x8& bo) { acc[i % NT] = mfma(a8[i / NT], bo, acc[i % NT]); });
-      };
-      if constexpr (DQK == DV) {
-        accumulate(std::integral_constant<int, NQ>{}, LQ{}, dk_wave ? Qs : Os);
-      } else if (dk_wave) {
-        accumulate(std::integral_constant<int, NQ>{}, LQ{}, Qs);
-      } else {
-        accumulate(std::integral_constant<int, NV>{}, LV{}, Os);
-      }
+    const bf16x8 keep0 = dk_wave ? da[0] : pa[0], keep1 = dk_wave ? da[1] : pa[1];
+    xme[0] = __builtin_bit_cast(u32x4, dk_wave ? pa[0] : da[0]);
+    xme[1] = __builtin_bit_cast(u32x4, dk_wave ? pa[1] : da[1]);
+    __syncthreads();
+    const bf16x8 got0 = __builtin_bit_cast(bf16x8, xpart[0]);
+    const bf16x8 got1 = __builtin_bit_cast(bf16x8, xpart[1]);
+    // dV += P^T dO (dV waves) or dK += dS^T Q (dK waves) over the 64 rows:
+    // k-steps 0, 1 on this wave's rows, 2, 3 on the partner's, NT tiles each;
+    // the B operand rows are read transposed from the Q or dO tile (layout LB).
+    auto accumulate = [&](auto nt_, auto lay_, const lds_u16* src) __attribute__((always_inline)) {
+      constexpr int NT = decltype(nt_)::value;
+      using LB = decltype(lay_);
+      pipelined<4 * NT, 1>(
+          [&](int i) {
+            const int ks = i / NT;
+            const int rr = 32 * (ks < 2 ? rh : rh ^ 1) + 16 * (ks & 1) + trow;
+            const int col = 32 * (i % NT) + tcol;
+            return ld_tr(src + LB::at(rr, col), src + LB::at(rr + 8, col));
+          },
+          [&](int i, const bf16x8& bo) {
+            const int ks = i / NT;
+            const bf16x8 a = ks == 0 ? keep0 : ks == 1 ? keep1 : ks == 2 ? got0 : got1;
+            acc[i % NT] = mfma(a, bo, acc[i % NT]);
+          });
+    };
+    if constexpr (DQK == DV) {
+      accumulate(std::integral_constant<int, NQ>{}, LQ{}, dk_wave ? Qs : Os);
+    } else if (dk_wave) {
+      accumulate(std::integral_constant<int, NQ>{}, LQ{}, Qs);
+    } else {
+      accumulate(std::integral_constant<int, NV>{}, LV{}, Os);
     }
   }
 
