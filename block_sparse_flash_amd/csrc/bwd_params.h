@@ -6,6 +6,11 @@
 
 namespace splash {
 
+// Head dims (d_qk, d_v) the bf16 backward is built for.
+constexpr bool bwd_dims_built(int d_qk, int d_v) {
+  return (d_qk == 64 && d_v == 64) || (d_qk == 128 && d_v == 128) || (d_qk == 192 && d_v == 128);
+}
+
 struct BwdParams {
   const void* q;        // bf16 [B, Hq, L, d_qk]
   const void* k;        // bf16 [B, Hkv, Lkv, d_qk]

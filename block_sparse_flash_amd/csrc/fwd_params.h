@@ -70,10 +70,6 @@ constexpr int kF32BlockKV = 64;
 // The bf16 backward's tables.
 constexpr int kBwdBlockQ = 256;
 constexpr int kBwdBlockKV = 64;
-// Head dims (d_qk, d_v) the bf16 backward is built for.
-constexpr bool bwd_dims_built(int d_qk, int d_v) {
-  return (d_qk == 64 && d_v == 64) || (d_qk == 128 && d_v == 128) || (d_qk == 192 && d_v == 128);
-}
 
 // A bf16 forward tile: bq query rows (32 per wave) by bkv keys per block.
 struct Tile {

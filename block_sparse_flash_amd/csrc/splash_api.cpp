@@ -7,6 +7,7 @@
 #include <cstdint>
 #include <cstdlib>
 
+#include "bwd_params.h"
 #include "errors.h"
 #include "fwd_params.h"
 #include "splash.h"
