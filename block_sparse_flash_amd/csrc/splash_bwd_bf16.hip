@@ -286,7 +286,7 @@ struct DkdvLds {
   static constexpr int LSE_OFF = O_OFF + 64 * RV * 2;      // lse * log2(e) [64]
   static constexpr int D_OFF = LSE_OFF + 64 * 4;           // D [64]
   static constexpr int SEG_OFF = D_OFF + 64 * 4;           // row segment ids [64]
-  static constexpr int X_OFF = SEG_OFF + 64 * 4;           // P or dS handed over [4 waves][64 lanes][16 bf16]
+  static constexpr int X_OFF = SEG_OFF + 64 * 4;           // P or dS handed over [4 waves][2][64 lanes][8 bf16]
   static constexpr int BYTES = X_OFF + 4 * 64 * 32;
   static_assert(BYTES <= 163840, "fits the LDS of a CU");
 };
@@ -320,10 +320,12 @@ void bwd_dkdv_kernel(BwdParams p) {
   const int kh = wave & 1;   // key half of the block
   const int rh = wave >> 1;  // row half of each 64-row sub-tile whose S and dP this wave computes
   const bool dk_wave = rh != 0;  // wave-uniform: accumulates dK (else dV)
-  // This wave's hand-over slot (32 bytes per lane) and its partner's, the
-  // wave of the same keys and the other row half.
-  lds_u32x4* xme = (lds_u32x4*)(lds + M::X_OFF) + (wave * 64 + lane) * 2;
-  const lds_u32x4* xpart = (const lds_u32x4*)(lds + M::X_OFF) + ((wave ^ 2) * 64 + lane) * 2;
+  // This wave's hand-over slots (two 16-byte runs per lane, laid out
+  // [wave][run][lane] so that a wave's write or read covers consecutive
+  // 16-byte words) and its partner's: the wave of the same keys and the
+  // other row half.
+  lds_u32x4* xme = (lds_u32x4*)(lds + M::X_OFF) + wave * 128 + lane;
+  const lds_u32x4* xpart = (const lds_u32x4*)(lds + M::X_OFF) + (wave ^ 2) * 128 + lane;
   // Transposed-read address of this lane: row 4 hi + (lane % 16) / 4 of a
   // 16-row step, columns 16 ((lane / 16) % 2) + 4 (lane % 4) of a 32-column tile.
   const int trow = 4 * hi + ((lane & 15) >> 2);
@@ -468,7 +470,7 @@ void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int row = row0 + rl0 + j;
-          const bool ok = (row >= rlo) & (row <= rhi) & (!has_seg || s4[j] == kseg);
+          const bool ok = (row >= rlo) & (row <= rhi) & (s4[j] == kseg);  // ids 0 without segments
           p_and_ds<CAP>(p, ok, s[4 * q4 + j], l4[j], dp[4 * q4 + j], d4[j], &pv[4 * q4 + j], &dsv[4 * q4 + j]);
         }
       }
@@ -486,10 +488,10 @@ void bwd_dkdv_kernel(BwdParams p) {
       }
     const bf16x8 keep0 = dk_wave ? da[0] : pa[0], keep1 = dk_wave ? da[1] : pa[1];
     xme[0] = __builtin_bit_cast(u32x4, dk_wave ? pa[0] : da[0]);
-    xme[1] = __builtin_bit_cast(u32x4, dk_wave ? pa[1] : da[1]);
+    xme[64] = __builtin_bit_cast(u32x4, dk_wave ? pa[1] : da[1]);
     __syncthreads();
     const bf16x8 got0 = __builtin_bit_cast(bf16x8, xpart[0]);
-    const bf16x8 got1 = __builtin_bit_cast(bf16x8, xpart[1]);
+    const bf16x8 got1 = __builtin_bit_cast(bf16x8, xpart[64]);
     // dV += P^T dO (dV waves) or dK += dS^T Q (dK waves) over the 64 rows:
     // k-steps 0, 1 on this wave's rows, 2, 3 on the partner's, NT tiles each;
     // the B operand rows are read transposed from the Q or dO tile (layout LB).
@@ -667,13 +669,26 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
             if (st < DQK / 16) s = mfma(o.a, QL ? o.c : qf[QL || st >= DQK / 16 ? 0 : st], s);
             if (st < DV / 16) dp = mfma(o.b, df[st < DV / 16 ? st : 0], dp);
           });
+      // Keys 32 t + 8 (e / 4) + 4 hi + e % 4 of this lane's row: four runs of
+      // 4.  Segment ids are 0 on both sides without segments.
       float pv[16], dsv[16];
+      const bool all_ok = all_allowed(p, r * BQ + 32 * wave, 32, key0 + 32 * t, 32);  // wave-uniform
+      if (all_ok) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int kl = 32 * t + 8 * (e / 4) + 4 * hi + (e % 4);
-        const int key = key0 + kl;
-        const bool ok = (key >= klo) & (key <= khi) & (!has_seg || segks[kl] == qseg);
-        p_and_ds<CAP>(p, ok, s[e], lse2, dp[e], dlt, &pv[e], &dsv[e]);
+        for (int e = 0; e < 16; ++e) p_and_ds<CAP>(p, true, s[e], lse2, dp[e], dlt, &pv[e], &dsv[e]);
+      } else {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int kl0 = 32 * t + 8 * q4 + 4 * hi;
+          const i32x4 s4 = *reinterpret_cast<const lds_i32x4*>(segks + kl0);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int e = 4 * q4 + j;
+            const int key = key0 + kl0 + j;
+            const bool ok = (key >= klo) & (key <= khi) & (s4[j] == qseg);
+            p_and_ds<CAP>(p, ok, s[e], lse2, dp[e], dlt, &pv[e], &dsv[e]);
+          }
+        }
       }
       // dQ += dS K over this tile's 32 keys: two k-steps of NQ tiles.
 #pragma unroll
