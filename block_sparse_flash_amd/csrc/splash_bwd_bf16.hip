@@ -180,14 +180,18 @@ struct Op4 {
 };
 
 // Whether every pair of query rows [r0, r0 + nr) and keys [k0, k0 + nk) is
-// allowed (no segment ids): then no element mask is needed.
-__device__ __forceinline__ bool all_allowed(const BwdParams& p, int r0, int nr, int k0, int nk) {
+// allowed by position (causal, window, bounds; segment ids aside).
+__device__ __forceinline__ bool pos_allowed(const BwdParams& p, int r0, int nr, int k0, int nk) {
   const int pa = p.q_off + r0;  // smallest row position
   const int pz = pa + nr - 1;   // largest
   const int kz = k0 + nk - 1;   // largest key
-  return p.seg_q == nullptr && r0 + nr <= p.L && kz < p.Lkv && (!p.causal || kz <= pa) &&
+  return r0 + nr <= p.L && kz < p.Lkv && (!p.causal || kz <= pa) &&
          (p.window_left < 0 || pz - k0 <= p.window_left) && (p.window_right < 0 || kz - pa <= p.window_right);
 }
+
+// Whether `id` is the same in every lane of the wave and equals `ref`
+// (wave-uniform result).
+__device__ __forceinline__ bool all_equal(int id, int ref) { return __all(id == ref) != 0; }
 
 // Copies rows row0 .. row0 + 63 of a row-major [n_valid, D] bf16 matrix
 // into LDS (zeros past n_valid), laid out by Lay<D, SWZ>.
@@ -345,6 +349,10 @@ void bwd_dkdv_kernel(BwdParams p) {
   const int my_key = key0 + 32 * kh + l32;
   const int32_t* segk = has_seg ? (p.seg_kv ? p.seg_kv + (int64_t)b * p.Lkv : p.seg_q + (int64_t)b * p.L) : nullptr;
   const int kseg = (has_seg && my_key < p.Lkv) ? segk[my_key] : 0;
+  // The wave's 32 keys in one segment (its id kseg0): then a tile whose rows
+  // are all in that segment needs no element test for the ids.
+  const int kseg0 = __builtin_amdgcn_readfirstlane(kseg);
+  const bool kseg_one = !has_seg || all_equal(kseg, kseg0);
   // Rows allowed to see this lane's key by position: causal pos >= key,
   // window pos - key <= left and key - pos <= right, pos = q_off + row.
   int rlo = 0, rhi = my_key < p.Lkv ? p.L - 1 : -1;
@@ -455,7 +463,8 @@ void bwd_dkdv_kernel(BwdParams p) {
 
     // Row data of the 16 rows 32 rh + 8 (e / 4) + 4 hi + e % 4 (four runs of 4).
     float pv[16], dsv[16];
-    const bool all_ok = all_allowed(p, row0 + 32 * rh, 32, key0 + 32 * kh, 32);  // wave-uniform
+    const bool all_ok = pos_allowed(p, row0 + 32 * rh, 32, key0 + 32 * kh, 32) &&
+                        (!has_seg || (kseg_one && all_equal(segqs[32 * rh + l32], kseg0)));  // wave-uniform
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       const int rl0 = 32 * rh + 8 * q4 + 4 * hi;
@@ -616,6 +625,9 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
   const float dlt = in ? p.delta[(int64_t)head * p.L + qi] : 0.0f;
   const bool has_seg = p.seg_q != nullptr;
   const int qseg = (has_seg && in) ? p.seg_q[(int64_t)b * p.L + qi] : 0;
+  // The wave's 32 rows in one segment (its id qseg0); see the dk/dv kernel.
+  const int qseg0 = __builtin_amdgcn_readfirstlane(qseg);
+  const bool qseg_one = !has_seg || all_equal(qseg, qseg0);
   const int32_t* segk = has_seg ? (p.seg_kv ? p.seg_kv + (int64_t)b * p.Lkv : p.seg_q + (int64_t)b * p.L) : nullptr;
   // Keys allowed to this lane's row by position (before segment ids).
   const int qpos = p.q_off + qi;
@@ -672,7 +684,8 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
       // Keys 32 t + 8 (e / 4) + 4 hi + e % 4 of this lane's row: four runs of
       // 4.  Segment ids are 0 on both sides without segments.
       float pv[16], dsv[16];
-      const bool all_ok = all_allowed(p, r * BQ + 32 * wave, 32, key0 + 32 * t, 32);  // wave-uniform
+      const bool all_ok = pos_allowed(p, r * BQ + 32 * wave, 32, key0 + 32 * t, 32) &&
+                          (!has_seg || (qseg_one && all_equal(segks[32 * t + l32], qseg0)));  // wave-uniform
       if (all_ok) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) p_and_ds<CAP>(p, true, s[e], lse2, dp[e], dlt, &pv[e], &dsv[e]);
