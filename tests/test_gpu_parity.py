@@ -515,3 +515,44 @@ def test_full_size_workloads_sampled(name, n_split):
     # Every output row is finite (all workloads are causal: each row sees itself).
     assert bool(torch.isfinite(lse).all()) and bool(torch.isfinite(o.float()).all())
     _announce(f"  {len(heads)} heads x {len(rows)} rows: max-abs o {worst[0]:.3g} lse {worst[1]:.3g}")
+
+
+# Every bf16 forward instance the library compiles at the default tile: head
+# dims x soft cap x split-KV x packed GQA rows (all query rows of a K/V group
+# in one row tile when L is below the tile's rows), and the same for the
+# 64-row decode tile of 128/128 heads (chosen for L <= 64).
+INSTANCE_SHAPES = {
+    # name: (B, Hq, Hkv, L, mask kwargs)
+    "plain": (1, 2, 2, 300, dict(causal=True, window_left=120)),
+    "packed": (1, 4, 1, 90, dict(causal=True)),
+    "decode-tile": (1, 2, 2, 40, dict(causal=True)),
+    "decode-tile-packed": (1, 4, 1, 40, dict(causal=True, window_left=25)),
+}
+INSTANCES = [(dims, shape, cap, n_split)
+             for dims in [(128, 128), (64, 64), (64, 128), (128, 64), (192, 128), (192, 64)]
+             for shape in ("plain", "packed")
+             for cap in (0.0, 10.0)
+             for n_split in (1, 3)]
+INSTANCES += [((128, 128), shape, cap, n_split)
+              for shape in ("decode-tile", "decode-tile-packed")
+              for cap in (0.0, 10.0)
+              for n_split in (1, 3)]
+
+
+@pytest.mark.parametrize("case", INSTANCES, ids=lambda c: f"d{c[0][0]}x{c[0][1]}-{c[1]}"
+                         + ("-cap" if c[2] else "") + f"-s{c[3]}")
+def test_every_kernel_instance(case):
+    """Each compiled variant of the bf16 forward (cap, split-KV, packed rows,
+    decode tile) against the oracle, element by element (Lecture 13 section
+    5.2 kernel body, section 5.4 cap; split-K merge through the lse, joto.ai
+    "LSE and online softmax")."""
+    (dqk, dv), shape, cap, n_split = case
+    B, Hq, Hkv, L, mk = INSTANCE_SHAPES[shape]
+    _announce(f"instance {case}")
+    seed = 9000 + L + dqk + dv + n_split + int(cap)
+    q, k, v = (stored(a, "bf16") for a in draw_qkv(B, Hq, Hkv, L, dqk, dv, seed, qk_std=1.5 if cap else 1.0))
+    scale = 1.0 / math.sqrt(dqk)
+    o, lse = _run(q, k, v, scale=scale, soft_cap=cap, n_split=n_split, **mk)
+    o_ref, lse_ref = attention_ref(as_f64(q), as_f64(k), as_f64(v), scale=scale, soft_cap=cap, **mk)
+    eo, el = _compare(o, lse, o_ref, lse_ref, "bf16")
+    _announce(f"  max-abs o {eo:.3g} lse {el:.3g}")
