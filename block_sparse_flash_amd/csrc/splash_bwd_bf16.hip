@@ -360,195 +360,211 @@ void bwd_dkdv_kernel(BwdParams p) {
   if (p.window_right >= 0) rlo = max(rlo, my_key - p.window_right - p.q_off);
   if (p.window_left >= 0) rhi = min(rhi, my_key + p.window_left - p.q_off);
 
-  constexpr int NA = NQ > NV ? NQ : NV;
-  f32x16 acc[NA];  // dK (NQ tiles) or dV (NV tiles) of this wave's 32 keys
-#pragma unroll
-  for (int i = 0; i < NA; ++i) acc[i] = f32x16{};
+  // The rest of the kernel for role ROLE: 0 = chosen per wave at run time
+  // (dK and dV of the same shape), 1 = dK, 2 = dV.  With different shapes
+  // (192/128) each role runs its own copy, so that each keeps one
+  // accumulator shape (one array used with both shapes makes the compiler
+  // shuffle it between register files).
+  auto body = [&](auto role_) __attribute__((always_inline)) {
+    constexpr int ROLE = decltype(role_)::value;
+    const bool dkw = ROLE == 1 ? true : ROLE == 2 ? false : dk_wave;  // accumulates dK (else dV)
+    constexpr int NA = NQ > NV ? NQ : NV;
+    f32x16 acc[NA];  // dK (NQ tiles) or dV (NV tiles) of this wave's 32 keys
+  #pragma unroll
+    for (int i = 0; i < NA; ++i) acc[i] = f32x16{};
 
-  const int x0 = p.col_ptr[c];
-  const int x1 = p.col_ptr[c + 1];
-  const int32_t* sq = has_seg ? p.seg_q + (int64_t)b * p.L : nullptr;
-  // Cursor over the work-group's sub-tiles: query head cg of the group,
-  // entry cx of the column, sub-tile cs of that q block.  Sub-tiles whose
-  // positions allow no pair with this kv block are skipped.
-  int cg = 0, cx = x0, cs = 0;
-  auto next = [&](int* g_out, int* row0_out) __attribute__((always_inline)) -> bool {
-    while (cg < p.group) {
-      if (cx >= x1) {
-        ++cg;
-        cx = x0;
-        cs = 0;
-        continue;
+    const int x0 = p.col_ptr[c];
+    const int x1 = p.col_ptr[c + 1];
+    const int32_t* sq = has_seg ? p.seg_q + (int64_t)b * p.L : nullptr;
+    // Cursor over the work-group's sub-tiles: query head cg of the group,
+    // entry cx of the column, sub-tile cs of that q block.  Sub-tiles whose
+    // positions allow no pair with this kv block are skipped.
+    int cg = 0, cx = x0, cs = 0;
+    auto next = [&](int* g_out, int* row0_out) __attribute__((always_inline)) -> bool {
+      while (cg < p.group) {
+        if (cx >= x1) {
+          ++cg;
+          cx = x0;
+          cs = 0;
+          continue;
+        }
+        if (cs >= BQ / SUB) {
+          ++cx;
+          cs = 0;
+          continue;
+        }
+        const int row0 = p.col_rows[cx] * BQ + cs * SUB;
+        ++cs;
+        if (row0 >= p.L) {
+          cs = BQ / SUB;
+          continue;
+        }
+        const int pa = p.q_off + row0;
+        const int pz = pa + SUB - 1;
+        if (p.causal && pz < key0) continue;
+        if (p.window_left >= 0 && pa - (key0 + BK - 1) > p.window_left) continue;
+        if (p.window_right >= 0 && key0 - pz > p.window_right) continue;
+        *g_out = cg;
+        *row0_out = row0;
+        return true;
       }
-      if (cs >= BQ / SUB) {
-        ++cx;
-        cs = 0;
-        continue;
+      return false;
+    };
+    // The next sub-tile's Q, dO, lse, D and segment ids are fetched into
+    // registers while the current one is computed.
+    TileRegs<DQK, 256, true> q_next;
+    TileRegs<DV, 256, true> o_next;
+    float lse_next = 0.0f, d_next = 0.0f;
+    int seg_next = 0;
+    auto fetch = [&](int g, int row0) __attribute__((always_inline)) {
+      const int64_t head = b * p.Hq + kvh * p.group + g;
+      q_next.fetch(buffer_rsrc(static_cast<const uint16_t*>(p.q) + head * p.L * DQK, (uint32_t)p.L * DQK * 2),
+                   row0, tid);
+      o_next.fetch(buffer_rsrc(static_cast<const uint16_t*>(p.dout) + head * p.L * DV, (uint32_t)p.L * DV * 2),
+                   row0, tid);
+      if (tid < SUB) {
+        const int qi = row0 + tid;
+        const bool in = qi < p.L;
+        lse_next = in ? p.lse[head * p.L + qi] * kLog2e : INFINITY;
+        d_next = in ? p.delta[head * p.L + qi] : 0.0f;
+        seg_next = (has_seg && in) ? sq[qi] : 0;
       }
-      const int row0 = p.col_rows[cx] * BQ + cs * SUB;
-      ++cs;
-      if (row0 >= p.L) {
-        cs = BQ / SUB;
-        continue;
-      }
-      const int pa = p.q_off + row0;
-      const int pz = pa + SUB - 1;
-      if (p.causal && pz < key0) continue;
-      if (p.window_left >= 0 && pa - (key0 + BK - 1) > p.window_left) continue;
-      if (p.window_right >= 0 && key0 - pz > p.window_right) continue;
-      *g_out = cg;
-      *row0_out = row0;
-      return true;
-    }
-    return false;
-  };
-  // The next sub-tile's Q, dO, lse, D and segment ids are fetched into
-  // registers while the current one is computed.
-  TileRegs<DQK, 256, true> q_next;
-  TileRegs<DV, 256, true> o_next;
-  float lse_next = 0.0f, d_next = 0.0f;
-  int seg_next = 0;
-  auto fetch = [&](int g, int row0) __attribute__((always_inline)) {
-    const int64_t head = b * p.Hq + kvh * p.group + g;
-    q_next.fetch(buffer_rsrc(static_cast<const uint16_t*>(p.q) + head * p.L * DQK, (uint32_t)p.L * DQK * 2),
-                 row0, tid);
-    o_next.fetch(buffer_rsrc(static_cast<const uint16_t*>(p.dout) + head * p.L * DV, (uint32_t)p.L * DV * 2),
-                 row0, tid);
-    if (tid < SUB) {
-      const int qi = row0 + tid;
-      const bool in = qi < p.L;
-      lse_next = in ? p.lse[head * p.L + qi] * kLog2e : INFINITY;
-      d_next = in ? p.delta[head * p.L + qi] : 0.0f;
-      seg_next = (has_seg && in) ? sq[qi] : 0;
-    }
-  };
-  int next_g = 0, next_row0 = 0;
-  bool have = next(&next_g, &next_row0);
-  if (have) fetch(next_g, next_row0);
-  while (have) {
-    const int row0 = next_row0;
-    __syncthreads();  // the previous sub-tile is consumed
-    q_next.store(Qs, tid);
-    o_next.store(Os, tid);
-    if (tid < SUB) {
-      lse2s[tid] = lse_next;
-      Ds[tid] = d_next;
-      segqs[tid] = seg_next;
-    }
-    __syncthreads();
-    have = next(&next_g, &next_row0);
+    };
+    int next_g = 0, next_row0 = 0;
+    bool have = next(&next_g, &next_row0);
     if (have) fetch(next_g, next_row0);
+    while (have) {
+      const int row0 = next_row0;
+      __syncthreads();  // the previous sub-tile is consumed
+      q_next.store(Qs, tid);
+      o_next.store(Os, tid);
+      if (tid < SUB) {
+        lse2s[tid] = lse_next;
+        Ds[tid] = d_next;
+        segqs[tid] = seg_next;
+      }
+      __syncthreads();
+      have = next(&next_g, &next_row0);
+      if (have) fetch(next_g, next_row0);
 
-    // S = Q K^T and dP = dO V^T on rows 32 rh .. + 31 of the sub-tile and
-    // the wave's 32 keys (two interleaved chains; S takes DQK / 16 k-steps,
-    // dP DV / 16): one key per lane, rows 32 rh + items.
-    f32x16 s = f32x16{}, dp = f32x16{};
-    pipelined<(DQK > DV ? DQK : DV) / 16, 0>(
-        [&](int st) {
-          Op4 o{};
-          if (st < DQK / 16) {
-            o.a = ld_op(Qs + LQ::off(32 * rh + l32, 2 * st + hi));
-            o.b = ld_op(Ks + LQ::off(32 * kh + l32, 2 * st + hi));
-          }
-          if (st < DV / 16) {
-            o.c = ld_op(Os + LV::off(32 * rh + l32, 2 * st + hi));
-            o.d = ld_op(Vs + LV::off(32 * kh + l32, 2 * st + hi));
-          }
-          return o;
-        },
-        [&](int st, const Op4& o) {
-          if (st < DQK / 16) s = mfma(o.a, o.b, s);
-          if (st < DV / 16) dp = mfma(o.c, o.d, dp);
-        });
+      // S = Q K^T and dP = dO V^T on rows 32 rh .. + 31 of the sub-tile and
+      // the wave's 32 keys (two interleaved chains; S takes DQK / 16 k-steps,
+      // dP DV / 16): one key per lane, rows 32 rh + items.
+      f32x16 s = f32x16{}, dp = f32x16{};
+      pipelined<(DQK > DV ? DQK : DV) / 16, 0>(
+          [&](int st) {
+            Op4 o{};
+            if (st < DQK / 16) {
+              o.a = ld_op(Qs + LQ::off(32 * rh + l32, 2 * st + hi));
+              o.b = ld_op(Ks + LQ::off(32 * kh + l32, 2 * st + hi));
+            }
+            if (st < DV / 16) {
+              o.c = ld_op(Os + LV::off(32 * rh + l32, 2 * st + hi));
+              o.d = ld_op(Vs + LV::off(32 * kh + l32, 2 * st + hi));
+            }
+            return o;
+          },
+          [&](int st, const Op4& o) {
+            if (st < DQK / 16) s = mfma(o.a, o.b, s);
+            if (st < DV / 16) dp = mfma(o.c, o.d, dp);
+          });
 
-    // Row data of the 16 rows 32 rh + 8 (e / 4) + 4 hi + e % 4 (four runs of 4).
-    float pv[16], dsv[16];
-    const bool all_ok = pos_allowed(p, row0 + 32 * rh, 32, key0 + 32 * kh, 32) &&
-                        (!has_seg || (kseg_one && all_equal(segqs[32 * rh + l32], kseg0)));  // wave-uniform
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int rl0 = 32 * rh + 8 * q4 + 4 * hi;
-      const f32x4 l4 = *reinterpret_cast<const lds_f32x4*>(lse2s + rl0);
-      const f32x4 d4 = *reinterpret_cast<const lds_f32x4*>(Ds + rl0);
-      if (all_ok) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          p_and_ds<CAP>(p, true, s[4 * q4 + j], l4[j], dp[4 * q4 + j], d4[j], &pv[4 * q4 + j], &dsv[4 * q4 + j]);
-      } else {
-        const i32x4 s4 = *reinterpret_cast<const lds_i32x4*>(segqs + rl0);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int row = row0 + rl0 + j;
-          const bool ok = (row >= rlo) & (row <= rhi) & (s4[j] == kseg);  // ids 0 without segments
-          p_and_ds<CAP>(p, ok, s[4 * q4 + j], l4[j], dp[4 * q4 + j], d4[j], &pv[4 * q4 + j], &dsv[4 * q4 + j]);
+      // Row data of the 16 rows 32 rh + 8 (e / 4) + 4 hi + e % 4 (four runs of 4).
+      float pv[16], dsv[16];
+      const bool all_ok = pos_allowed(p, row0 + 32 * rh, 32, key0 + 32 * kh, 32) &&
+                          (!has_seg || (kseg_one && all_equal(segqs[32 * rh + l32], kseg0)));  // wave-uniform
+  #pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int rl0 = 32 * rh + 8 * q4 + 4 * hi;
+        const f32x4 l4 = *reinterpret_cast<const lds_f32x4*>(lse2s + rl0);
+        const f32x4 d4 = *reinterpret_cast<const lds_f32x4*>(Ds + rl0);
+        if (all_ok) {
+  #pragma unroll
+          for (int j = 0; j < 4; ++j)
+            p_and_ds<CAP>(p, true, s[4 * q4 + j], l4[j], dp[4 * q4 + j], d4[j], &pv[4 * q4 + j], &dsv[4 * q4 + j]);
+        } else {
+          const i32x4 s4 = *reinterpret_cast<const lds_i32x4*>(segqs + rl0);
+  #pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int row = row0 + rl0 + j;
+            const bool ok = (row >= rlo) & (row <= rhi) & (s4[j] == kseg);  // ids 0 without segments
+            p_and_ds<CAP>(p, ok, s[4 * q4 + j], l4[j], dp[4 * q4 + j], d4[j], &pv[4 * q4 + j], &dsv[4 * q4 + j]);
+          }
         }
       }
-    }
-    // P and dS of these 32 rows as bf16 A operands (two k-steps of 16 rows
-    // each).  The dV wave keeps P and hands dS to the dK wave of its keys;
-    // the dK wave keeps dS and hands P over.
-    bf16x8 pa[2], da[2];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        pa[ks][j] = (__bf16)pv[8 * ks + j];
-        da[ks][j] = (__bf16)dsv[8 * ks + j];
+      // P and dS of these 32 rows as bf16 A operands (two k-steps of 16 rows
+      // each).  The dV wave keeps P and hands dS to the dK wave of its keys;
+      // the dK wave keeps dS and hands P over.
+      bf16x8 pa[2], da[2];
+  #pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+  #pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          pa[ks][j] = (__bf16)pv[8 * ks + j];
+          da[ks][j] = (__bf16)dsv[8 * ks + j];
+        }
+      const bf16x8 keep0 = dkw ? da[0] : pa[0], keep1 = dkw ? da[1] : pa[1];
+      xme[0] = __builtin_bit_cast(u32x4, dkw ? pa[0] : da[0]);
+      xme[64] = __builtin_bit_cast(u32x4, dkw ? pa[1] : da[1]);
+      __syncthreads();
+      const bf16x8 got0 = __builtin_bit_cast(bf16x8, xpart[0]);
+      const bf16x8 got1 = __builtin_bit_cast(bf16x8, xpart[64]);
+      // dV += P^T dO (dV waves) or dK += dS^T Q (dK waves) over the 64 rows:
+      // k-steps 0, 1 on this wave's rows, 2, 3 on the partner's, NT tiles each;
+      // the B operand rows are read transposed from the Q or dO tile (layout LB).
+      auto accumulate = [&](auto nt_, auto lay_, const lds_u16* src) __attribute__((always_inline)) {
+        constexpr int NT = decltype(nt_)::value;
+        using LB = decltype(lay_);
+        pipelined<4 * NT, 1>(
+            [&](int i) {
+              const int ks = i / NT;
+              const int rr = 32 * (ks < 2 ? rh : rh ^ 1) + 16 * (ks & 1) + trow;
+              const int col = 32 * (i % NT) + tcol;
+              return ld_tr(src + LB::at(rr, col), src + LB::at(rr + 8, col));
+            },
+            [&](int i, const bf16x8& bo) {
+              const int ks = i / NT;
+              const bf16x8 a = ks == 0 ? keep0 : ks == 1 ? keep1 : ks == 2 ? got0 : got1;
+              acc[i % NT] = mfma(a, bo, acc[i % NT]);
+            });
+      };
+      if constexpr (DQK == DV) {
+        accumulate(std::integral_constant<int, NQ>{}, LQ{}, dkw ? Qs : Os);
+      } else if (dkw) {
+        accumulate(std::integral_constant<int, NQ>{}, LQ{}, Qs);
+      } else {
+        accumulate(std::integral_constant<int, NV>{}, LV{}, Os);
       }
-    const bf16x8 keep0 = dk_wave ? da[0] : pa[0], keep1 = dk_wave ? da[1] : pa[1];
-    xme[0] = __builtin_bit_cast(u32x4, dk_wave ? pa[0] : da[0]);
-    xme[64] = __builtin_bit_cast(u32x4, dk_wave ? pa[1] : da[1]);
-    __syncthreads();
-    const bf16x8 got0 = __builtin_bit_cast(bf16x8, xpart[0]);
-    const bf16x8 got1 = __builtin_bit_cast(bf16x8, xpart[64]);
-    // dV += P^T dO (dV waves) or dK += dS^T Q (dK waves) over the 64 rows:
-    // k-steps 0, 1 on this wave's rows, 2, 3 on the partner's, NT tiles each;
-    // the B operand rows are read transposed from the Q or dO tile (layout LB).
-    auto accumulate = [&](auto nt_, auto lay_, const lds_u16* src) __attribute__((always_inline)) {
-      constexpr int NT = decltype(nt_)::value;
-      using LB = decltype(lay_);
-      pipelined<4 * NT, 1>(
-          [&](int i) {
-            const int ks = i / NT;
-            const int rr = 32 * (ks < 2 ? rh : rh ^ 1) + 16 * (ks & 1) + trow;
-            const int col = 32 * (i % NT) + tcol;
-            return ld_tr(src + LB::at(rr, col), src + LB::at(rr + 8, col));
-          },
-          [&](int i, const bf16x8& bo) {
-            const int ks = i / NT;
-            const bf16x8 a = ks == 0 ? keep0 : ks == 1 ? keep1 : ks == 2 ? got0 : got1;
-            acc[i % NT] = mfma(a, bo, acc[i % NT]);
-          });
+    }
+
+    // Each wave writes its 32 keys: dK (times the scale, D = DQK) or dV (D = DV).
+    auto write = [&](auto d_, float* outg, float osc) __attribute__((always_inline)) {
+      constexpr int D = decltype(d_)::value;
+      outg += (int64_t)bk * p.Lkv * D;
+  #pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int key = key0 + 32 * kh + 8 * (e / 4) + 4 * hi + (e % 4);
+        if (key < p.Lkv) {
+  #pragma unroll
+          for (int t = 0; t < D / 32; ++t) outg[(int64_t)key * D + 32 * t + l32] = osc * acc[t][e];
+        }
+      }
     };
     if constexpr (DQK == DV) {
-      accumulate(std::integral_constant<int, NQ>{}, LQ{}, dk_wave ? Qs : Os);
-    } else if (dk_wave) {
-      accumulate(std::integral_constant<int, NQ>{}, LQ{}, Qs);
+      write(std::integral_constant<int, DQK>{}, dkw ? p.dk : p.dv, dkw ? p.scale : 1.0f);
+    } else if (dkw) {
+      write(std::integral_constant<int, DQK>{}, p.dk, p.scale);
     } else {
-      accumulate(std::integral_constant<int, NV>{}, LV{}, Os);
+      write(std::integral_constant<int, DV>{}, p.dv, 1.0f);
     }
-  }
 
-  // Each wave writes its 32 keys: dK (times the scale, D = DQK) or dV (D = DV).
-  auto write = [&](auto d_, float* outg, float osc) __attribute__((always_inline)) {
-    constexpr int D = decltype(d_)::value;
-    outg += (int64_t)bk * p.Lkv * D;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int key = key0 + 32 * kh + 8 * (e / 4) + 4 * hi + (e % 4);
-      if (key < p.Lkv) {
-#pragma unroll
-        for (int t = 0; t < D / 32; ++t) outg[(int64_t)key * D + 32 * t + l32] = osc * acc[t][e];
-      }
-    }
   };
-  if constexpr (DQK == DV) {
-    write(std::integral_constant<int, DQK>{}, dk_wave ? p.dk : p.dv, dk_wave ? p.scale : 1.0f);
-  } else if (dk_wave) {
-    write(std::integral_constant<int, DQK>{}, p.dk, p.scale);
-  } else {
-    write(std::integral_constant<int, DV>{}, p.dv, 1.0f);
-  }
+  if constexpr (DQK == DV)
+    body(std::integral_constant<int, 0>{});
+  else if (dk_wave)
+    body(std::integral_constant<int, 1>{});
+  else
+    body(std::integral_constant<int, 2>{});
 }
 
 template <int DQK, int DV>
