@@ -162,15 +162,12 @@ __device__ __forceinline__ void dma16(u32x4 rsrc, uint32_t lds_addr, int voff) {
                     (uint32_t)__builtin_amdgcn_readfirstlane(rsrc[1]),
                     (uint32_t)__builtin_amdgcn_readfirstlane(rsrc[2]),
                     (uint32_t)__builtin_amdgcn_readfirstlane(rsrc[3])};
-  uint32_t saved;
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
+      "s_mov_b32 m0, %0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      :
       : "s"(base), "v"(voff), "s"(rs)
-      : "memory");
+      : "memory", "m0");
 }
 
 // One 4-byte-per-lane HBM -> LDS copy (lane i's dword lands at
@@ -181,15 +178,12 @@ __device__ __forceinline__ void dma4(u32x4 rsrc, uint32_t lds_addr, int voff) {
                     (uint32_t)__builtin_amdgcn_readfirstlane(rsrc[1]),
                     (uint32_t)__builtin_amdgcn_readfirstlane(rsrc[2]),
                     (uint32_t)__builtin_amdgcn_readfirstlane(rsrc[3])};
-  uint32_t saved;
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "buffer_load_dword %2, %3, 0 offen lds\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
+      "s_mov_b32 m0, %0\n\t"
+      "buffer_load_dword %1, %2, 0 offen lds"
+      :
       : "s"(base), "v"(voff), "s"(rs)
-      : "memory");
+      : "memory", "m0");
 }
 
 // Wait until at most N tile copies of this wave are in flight and all LDS
