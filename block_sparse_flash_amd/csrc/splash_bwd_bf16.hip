@@ -38,8 +38,13 @@
 //     256-row q block) walks the row's active kv blocks; S^T = K Q^T and
 //     dP^T = V dO^T hold one row per lane, and dS^T feeds dQ += dS K the same
 //     way, with K read transposed.
-//   * LDS tiles are row-major with rows padded by 16 bytes, so that the 16
-//     lanes of a ds_read_b128 operand read fall in distinct banks.
+//   * LDS tiles are row-major; 128-wide rows take an XOR swizzle of their
+//     16-byte chunks and other widths a 16-byte row pad, so that operand and
+//     transposing reads fall in distinct banks (see Lay).
+//   * 192-wide q/k heads (with 128-wide v): S takes 12 k-steps and dP 8, dK
+//     6 accumulator tiles and dV 4; the dk/dv kernel then runs one work-group
+//     per CU with one inlined copy of its body per role, and the dq kernel
+//     keeps Q in LDS.
 //   * Gradients are accumulated and written in float32.
 
 #include <hip/hip_runtime.h>
