@@ -456,7 +456,7 @@ void bwd_dkdv_kernel(BwdParams p) {
       // the wave's 32 keys (two interleaved chains; S takes DQK / 16 k-steps,
       // dP DV / 16): one key per lane, rows 32 rh + items.
       f32x16 s = f32x16{}, dp = f32x16{};
-      pipelined<(DQK > DV ? DQK : DV) / 16, 0>(
+      pipelined<(DQK > DV ? DQK : DV) / 16, 1>(
           [&](int st) {
             Op4 o{};
             if (st < DQK / 16) {
