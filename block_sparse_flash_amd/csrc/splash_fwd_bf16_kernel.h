@@ -155,7 +155,7 @@ __device__ __forceinline__ void sfor(F&& f) {
 // voff of the buffer land at LDS address lds_addr + 16 i.  Issued as inline
 // assembly so that the compiler does not treat later LDS reads of *other*
 // buffers as dependent on it; completion is tracked explicitly with vmcnt.
-// M0 (the LDS base of the copy) is saved and restored around it.
+// M0 (the LDS base of the copy) is set here and declared clobbered.
 __device__ __forceinline__ void dma16(u32x4 rsrc, uint32_t lds_addr, int voff) {
   const uint32_t base = (uint32_t)__builtin_amdgcn_readfirstlane(lds_addr);
   const u32x4 rs = {(uint32_t)__builtin_amdgcn_readfirstlane(rsrc[0]),
