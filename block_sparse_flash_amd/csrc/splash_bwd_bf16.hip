@@ -375,7 +375,7 @@ void bwd_dkdv_kernel(BwdParams p) {
     const bool dkw = ROLE == 1 ? true : ROLE == 2 ? false : dk_wave;  // accumulates dK (else dV)
     constexpr int NA = NQ > NV ? NQ : NV;
     f32x16 acc[NA];  // dK (NQ tiles) or dV (NV tiles) of this wave's 32 keys
-  #pragma unroll
+#pragma unroll
     for (int i = 0; i < NA; ++i) acc[i] = f32x16{};
 
     const int x0 = p.col_ptr[c];
@@ -478,18 +478,18 @@ void bwd_dkdv_kernel(BwdParams p) {
       float pv[16], dsv[16];
       const bool all_ok = pos_allowed(p, row0 + 32 * rh, 32, key0 + 32 * kh, 32) &&
                           (!has_seg || (kseg_one && all_equal(segqs[32 * rh + l32], kseg0)));  // wave-uniform
-  #pragma unroll
+#pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int rl0 = 32 * rh + 8 * q4 + 4 * hi;
         const f32x4 l4 = *reinterpret_cast<const lds_f32x4*>(lse2s + rl0);
         const f32x4 d4 = *reinterpret_cast<const lds_f32x4*>(Ds + rl0);
         if (all_ok) {
-  #pragma unroll
+#pragma unroll
           for (int j = 0; j < 4; ++j)
             p_and_ds<CAP>(p, true, s[4 * q4 + j], l4[j], dp[4 * q4 + j], d4[j], &pv[4 * q4 + j], &dsv[4 * q4 + j]);
         } else {
           const i32x4 s4 = *reinterpret_cast<const lds_i32x4*>(segqs + rl0);
-  #pragma unroll
+#pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int row = row0 + rl0 + j;
             const bool ok = (row >= rlo) & (row <= rhi) & (s4[j] == kseg);  // ids 0 without segments
@@ -501,9 +501,9 @@ void bwd_dkdv_kernel(BwdParams p) {
       // each).  The dV wave keeps P and hands dS to the dK wave of its keys;
       // the dK wave keeps dS and hands P over.
       bf16x8 pa[2], da[2];
-  #pragma unroll
+#pragma unroll
       for (int ks = 0; ks < 2; ++ks)
-  #pragma unroll
+#pragma unroll
         for (int j = 0; j < 8; ++j) {
           pa[ks][j] = (__bf16)pv[8 * ks + j];
           da[ks][j] = (__bf16)dsv[8 * ks + j];
@@ -546,11 +546,11 @@ void bwd_dkdv_kernel(BwdParams p) {
     auto write = [&](auto d_, float* outg, float osc) __attribute__((always_inline)) {
       constexpr int D = decltype(d_)::value;
       outg += (int64_t)bk * p.Lkv * D;
-  #pragma unroll
+#pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int key = key0 + 32 * kh + 8 * (e / 4) + 4 * hi + (e % 4);
         if (key < p.Lkv) {
-  #pragma unroll
+#pragma unroll
           for (int t = 0; t < D / 32; ++t) outg[(int64_t)key * D + 32 * t + l32] = osc * acc[t][e];
         }
       }
