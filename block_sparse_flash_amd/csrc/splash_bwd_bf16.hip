@@ -113,6 +113,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
                                            __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000);
 }
 
+// Table entry t[i] read through the scalar cache: the tables are read-only
+// for the whole launch and i is wave-uniform.
+__device__ __forceinline__ int32_t sload(const int32_t* t, int i) {
+  return ((const __attribute__((address_space(4))) int32_t*)t)[__builtin_amdgcn_readfirstlane(i)];
+}
+
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -383,22 +389,26 @@ void bwd_dkdv_kernel(BwdParams p) {
     const int32_t* sq = has_seg ? p.seg_q + (int64_t)b * p.L : nullptr;
     // Cursor over the work-group's sub-tiles: query head cg of the group,
     // entry cx of the column, sub-tile cs of that q block.  Sub-tiles whose
-    // positions allow no pair with this kv block are skipped.
+    // positions allow no pair with this kv block are skipped.  crow, the
+    // first row of entry cx's q block, is read once per entry.
     int cg = 0, cx = x0, cs = 0;
+    int crow = x0 < x1 ? sload(p.col_rows, x0) * BQ : 0;
     auto next = [&](int* g_out, int* row0_out) __attribute__((always_inline)) -> bool {
       while (cg < p.group) {
         if (cx >= x1) {
           ++cg;
           cx = x0;
           cs = 0;
+          if (x0 < x1) crow = sload(p.col_rows, x0) * BQ;
           continue;
         }
         if (cs >= BQ / SUB) {
           ++cx;
           cs = 0;
+          if (cx < x1) crow = sload(p.col_rows, cx) * BQ;
           continue;
         }
-        const int row0 = p.col_rows[cx] * BQ + cs * SUB;
+        const int row0 = crow + cs * SUB;
         ++cs;
         if (row0 >= p.L) {
           cs = BQ / SUB;
