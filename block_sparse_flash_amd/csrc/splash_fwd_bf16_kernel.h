@@ -19,9 +19,9 @@
 //     fills a CU with two waves per SIMD (waves w and w + 4 share a SIMD).
 //     Every K/V tile copied into LDS serves 256 queries.
 //   * Ping-pong schedule (default loop): waves 0-3 and 4-7 form two groups
-//     with one wave per SIMD each.  They alternate, one barrier apart, between
-//     a matrix phase (O += P V of the previous block, S = Q K^T of this one)
-//     and a softmax phase, so on every SIMD one wave feeds the matrix pipe
+//     with one wave per SIMD each.  They alternate, half a block apart,
+//     between a matrix phase (O += P V of the previous block, S = Q K^T of
+//     this one) and a softmax phase, so on every SIMD one wave feeds the matrix pipe
 //     while the other uses the vector unit (section 5.3: the vector work must
 //     hide behind the matrix work).  On gfx950 a matrix-only wave and a
 //     vector-only wave overlap almost perfectly, while one wave mixing both
@@ -446,12 +446,12 @@ __device__ __forceinline__ void item_fwd(const FwdParams& p, int head, int r, in
   // ---------------------------------------------------------------------
   // Ping-pong loop.  Waves w and w + NW/2 run on the same SIMD, so waves
   // [0, NW/2) (group 0) and [NW/2, NW) (group 1) each hold one wave per SIMD.
-  // Both groups run the same sequence MM(0) SM(0) MM(1) SM(1) ... MM(n), a
-  // work-group barrier after every phase, but group 1 starts one barrier
-  // later.  MM(i) is the matrix phase (O += P_{i-1} V_{i-1} for i >= 1,
-  // S_i = Q K_i^T for i < n), SM(i) the softmax phase (S_i -> P_i, l, lazy O
-  // rescale).  So in every half-step one wave of each SIMD feeds the matrix
-  // pipe while the other works on the vector unit:
+  // Both groups run the same sequence MM(0) SM(0) MM(1) SM(1) ... MM(n), but
+  // group 1 half a step later.  MM(i) is the matrix phase
+  // (O += P_{i-1} V_{i-1} for i >= 1, S_i = Q K_i^T for i < n), SM(i) the
+  // softmax phase (S_i -> P_i, l, lazy O rescale).  So in every half-step
+  // one wave of each SIMD feeds the matrix pipe while the other works on the
+  // vector unit:
   //   half-step 2i:     group 0 MM(i)      group 1 SM(i-1)
   //   half-step 2i+1:   group 0 SM(i)      group 1 MM(i)
   // The tiles of block i+2 (K) and i+1 (V) are copied in half-step 2i+2,
@@ -789,6 +789,17 @@ __device__ __forceinline__ void item_fwd(const FwdParams& p, int head, int r, in
 
 
     // Each group runs its own copy of the sequence (no per-phase branches).
+    // Barriers: with heads up to 128 wide there is one work-group barrier per
+    // step, X_i between half-steps 2i+1 and 2i+2 (group 0: after SM(i);
+    // group 1: after MM(i)), plus the two that open the first step.  X_i is
+    // the only ordering the data needs: the copies into the buffers of K_i
+    // and V_{i-1} start after it (every MM(i) is done), and the copies of
+    // K_{i+1} and V_i issued before it are waited for in it (both groups'
+    // MM(i+1) read them after it).  Inside a step the groups keep their half-step
+    // offset by themselves, since the two phases take about equally long;
+    // a barrier in the middle of the step as well cost 1-3%.  Per item both
+    // groups pass n + 2 barriers.  With 192-wide heads every phase ends at a
+    // barrier.
     // Group 1 copies the first tiles (K_0, then K_1 and V_0).  From then on
     // K_{i+2} and V_{i+1} are copied in half-step 2i+2 into the buffers of K_i
     // and V_{i-1} (last read by MM(i) in half-steps 2i and 2i+1) and waited
@@ -842,6 +853,7 @@ __device__ __forceinline__ void item_fwd(const FwdParams& p, int head, int r, in
         lds_barrier();   // group 1 starts one half-step late
       }
       mm(0, Idx<0>{}, Idx<1>{}, no_copy, Idx<0>{});
+      if constexpr (kCopyInMM && !G1) lds_barrier();   // group 1's second barrier (K_1, V_0 issued)
       for (int i = 0; i + 1 < n; ++i) {
         int nmn, c4;
         if constexpr (!kCopyInMM) {
@@ -864,10 +876,8 @@ __device__ __forceinline__ void item_fwd(const FwdParams& p, int head, int r, in
           tab_issue(i, &nmn, &c4);
           sm(i, tw.mn, tw.c0, no_copy, Idx<0>{});
           tab_advance(tw, nmn, c4);
-          lds_barrier();
           mm(i + 1, Idx<1>{}, Idx<1>{}, no_copy, Idx<0>{});
         } else {
-          lds_barrier();
           tab_issue(i, &nmn, &c4);
           sm(i, tw.mn, tw.c0, no_copy, Idx<0>{});
           tab_advance(tw, nmn, c4);
@@ -882,17 +892,18 @@ __device__ __forceinline__ void item_fwd(const FwdParams& p, int head, int r, in
              Idx<KL + VL>{});
         }
       }
-      if constexpr (G1 || !kCopyInMM)
+      if constexpr (kCopyInMM) {
+        if constexpr (G1) wait_copies_and_barrier<0>();
+        sm(n - 1, tw.mn, tw.c0, no_copy, Idx<0>{});
+        if constexpr (!G1) wait_copies_and_barrier<0>();
+        mm(n, Idx<1>{}, Idx<0>{}, no_copy, Idx<0>{});
+      } else {
         wait_copies_and_barrier<0>();
-      else
+        sm(n - 1, tw.mn, tw.c0, no_copy, Idx<0>{});
         lds_barrier();
-      sm(n - 1, tw.mn, tw.c0, no_copy, Idx<0>{});
-      if constexpr (G1 || !kCopyInMM)
-        lds_barrier();
-      else
-        wait_copies_and_barrier<0>();
-      mm(n, Idx<1>{}, Idx<0>{}, no_copy, Idx<0>{});
-      if constexpr (!G1) lds_barrier();   // matches group 1's extra barrier
+        mm(n, Idx<1>{}, Idx<0>{}, no_copy, Idx<0>{});
+        if constexpr (!G1) lds_barrier();   // matches group 1's extra barrier
+      }
     };
     if (grp1)
       run(Idx<1>{});
