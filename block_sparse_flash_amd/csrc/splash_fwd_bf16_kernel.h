@@ -789,21 +789,19 @@ __device__ __forceinline__ void item_fwd(const FwdParams& p, int head, int r, in
 
 
     // Each group runs its own copy of the sequence (no per-phase branches).
-    // Barriers: with heads up to 128 wide there is one work-group barrier per
-    // step, X_i between half-steps 2i+1 and 2i+2 (group 0: after SM(i);
-    // group 1: after MM(i)), plus the two that open the first step.  X_i is
-    // the only ordering the data needs: the copies into the buffers of K_i
-    // and V_{i-1} start after it (every MM(i) is done), and the copies of
-    // K_{i+1} and V_i issued before it are waited for in it (both groups'
-    // MM(i+1) read them after it).  Inside a step the groups keep their half-step
-    // offset by themselves, since the two phases take about equally long;
-    // a barrier in the middle of the step as well cost 1-3%.  Per item both
-    // groups pass n + 2 barriers.  With 192-wide heads every phase ends at a
-    // barrier.
+    // Barriers: one work-group barrier per step, X_i between half-steps 2i+1
+    // and 2i+2 (group 0: after SM(i); group 1: after MM(i)), plus the two
+    // that open the first step.  X_i is the only ordering the data needs: the
+    // copies into the buffers of K_i and V_{i-1} start after it (every MM(i)
+    // is done), and the copies of K_{i+1} and V_i issued before it are waited
+    // for in it (both groups' MM(i+1) read them after it).  Inside a step the
+    // groups keep their half-step offset by themselves, since the two phases
+    // take about equally long; a barrier in the middle of the step as well
+    // cost 1-3%.  Per item both groups pass n + 2 barriers.
     // Group 1 copies the first tiles (K_0, then K_1 and V_0).  From then on
     // K_{i+2} and V_{i+1} are copied in half-step 2i+2 into the buffers of K_i
     // and V_{i-1} (last read by MM(i) in half-steps 2i and 2i+1) and waited
-    // for before the barrier that opens MM(i+2) of group 0 (half-step 2i+4):
+    // for in X_{i+1}, before MM(i+2) of group 0 (half-step 2i+4):
     //   heads up to 128 wide: by group 0 during its MM(i+1), where issuing a
     //     copy costs little (the matrix pipe works meanwhile);
     //   192-wide heads: by group 1 during its SM(i), since the copy addresses
@@ -853,57 +851,45 @@ __device__ __forceinline__ void item_fwd(const FwdParams& p, int head, int r, in
         lds_barrier();   // group 1 starts one half-step late
       }
       mm(0, Idx<0>{}, Idx<1>{}, no_copy, Idx<0>{});
-      if constexpr (kCopyInMM && !G1) lds_barrier();   // group 1's second barrier (K_1, V_0 issued)
+      if constexpr (!G1) lds_barrier();   // group 1's second barrier (K_1, V_0 issued)
       for (int i = 0; i + 1 < n; ++i) {
         int nmn, c4;
-        if constexpr (!kCopyInMM) {
+        // X_i: group 1 passes it after MM(i), group 0 after SM(i).
+        if constexpr (G1) wait_copies_and_barrier<0>();
+        tab_issue(i, &nmn, &c4);
+        if constexpr (G1 && !kCopyInMM) {
+          // K_{i+2} (past the end: a repeat of K_{n-1} into the free buffer)
+          // and V_{i+1}; the segment ids of block i+2 go to ring slot
+          // (i+2) % 3, last read by SM(i-1).
+          const int ck = tw.c2, cv = tw.c1;
+          const int kbf = i & 1, vbf = (i + 1) & 1, sslot = (i + 2) % 3;
+          sm(i, tw.mn, tw.c0,
+             [&](auto k_) __attribute__((always_inline)) { copy_part(k_, ck, kbf, cv, vbf, sslot); },
+             Idx<KL + VL>{});
+        } else {
+          sm(i, tw.mn, tw.c0, no_copy, Idx<0>{});
+        }
+        tab_advance(tw, nmn, c4);
+        if constexpr (G1) {
+          mm(i + 1, Idx<1>{}, Idx<1>{}, no_copy, Idx<0>{});
+        } else {
           wait_copies_and_barrier<0>();
-          tab_issue(i, &nmn, &c4);
-          if constexpr (G1) {
-            const int ck = tw.c2, cv = tw.c1;
+          if constexpr (kCopyInMM) {
+            // The same copies, issued between the MFMAs (tw has advanced).
+            const int ck = tw.c1, cv = tw.c0;
             const int kbf = i & 1, vbf = (i + 1) & 1, sslot = (i + 2) % 3;
-            sm(i, tw.mn, tw.c0,
+            mm(i + 1, Idx<1>{}, Idx<1>{},
                [&](auto k_) __attribute__((always_inline)) { copy_part(k_, ck, kbf, cv, vbf, sslot); },
                Idx<KL + VL>{});
           } else {
-            sm(i, tw.mn, tw.c0, no_copy, Idx<0>{});
+            mm(i + 1, Idx<1>{}, Idx<1>{}, no_copy, Idx<0>{});
           }
-          tab_advance(tw, nmn, c4);
-          lds_barrier();
-          mm(i + 1, Idx<1>{}, Idx<1>{}, no_copy, Idx<0>{});
-        } else if constexpr (G1) {
-          wait_copies_and_barrier<0>();
-          tab_issue(i, &nmn, &c4);
-          sm(i, tw.mn, tw.c0, no_copy, Idx<0>{});
-          tab_advance(tw, nmn, c4);
-          mm(i + 1, Idx<1>{}, Idx<1>{}, no_copy, Idx<0>{});
-        } else {
-          tab_issue(i, &nmn, &c4);
-          sm(i, tw.mn, tw.c0, no_copy, Idx<0>{});
-          tab_advance(tw, nmn, c4);
-          wait_copies_and_barrier<0>();
-          // K_{i+2} (past the end: a repeat of K_{n-1} into the free buffer)
-          // and V_{i+1}; the segment ids of block i+2 go to ring slot
-          // (i+2) % 3, last read by SM(i-1) in half-steps 2i-1 and 2i.
-          const int ck = tw.c1, cv = tw.c0;
-          const int kbf = i & 1, vbf = (i + 1) & 1, sslot = (i + 2) % 3;
-          mm(i + 1, Idx<1>{}, Idx<1>{},
-             [&](auto k_) __attribute__((always_inline)) { copy_part(k_, ck, kbf, cv, vbf, sslot); },
-             Idx<KL + VL>{});
         }
       }
-      if constexpr (kCopyInMM) {
-        if constexpr (G1) wait_copies_and_barrier<0>();
-        sm(n - 1, tw.mn, tw.c0, no_copy, Idx<0>{});
-        if constexpr (!G1) wait_copies_and_barrier<0>();
-        mm(n, Idx<1>{}, Idx<0>{}, no_copy, Idx<0>{});
-      } else {
-        wait_copies_and_barrier<0>();
-        sm(n - 1, tw.mn, tw.c0, no_copy, Idx<0>{});
-        lds_barrier();
-        mm(n, Idx<1>{}, Idx<0>{}, no_copy, Idx<0>{});
-        if constexpr (!G1) lds_barrier();   // matches group 1's extra barrier
-      }
+      if constexpr (G1) wait_copies_and_barrier<0>();
+      sm(n - 1, tw.mn, tw.c0, no_copy, Idx<0>{});
+      if constexpr (!G1) wait_copies_and_barrier<0>();
+      mm(n, Idx<1>{}, Idx<0>{}, no_copy, Idx<0>{});
     };
     if (grp1)
       run(Idx<1>{});
