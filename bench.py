@@ -25,6 +25,7 @@ sys.path.insert(0, ROOT)
 DEFAULT_WORKLOAD = "causal_mha_bf16_L4096_d128"
 PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}   # dense MFMA bf16; fp32 vector
 PEAK_HBM_GBS = 8000.0                           # HBM3E
+PEAK_CLOCK_HZ = 2.4e9                           # clock of the published peaks (256 CUs)
 KERNEL_SOURCES = {"bf16": ("splash_fwd_bf16_kernel.h", "splash_fwd_bf16.hip"),
                   "f32": ("splash_fwd_f32.hip",)}
 
@@ -208,13 +209,51 @@ def median_min(xs):
     return 0.5 * (srt[(len(srt) - 1) // 2] + srt[len(srt) // 2]), srt[0]
 
 
-def time_steps(step, stream, steps, warmup):
+class ClockProbe:
+    """Mean shader clock of each XCD over the timed steps: the library's clock
+    probe (one single-wave work-group per XCD records its core-clock cycle
+    counter, the constant-rate real-time counter and its XCD id) enqueued on
+    the launch stream just before and just after them."""
+
+    N = 8   # work-groups per probe: one per XCD (round-robin placement)
+
+    def __init__(self, dev, stream):
+        import torch
+        from block_sparse_flash_amd.api import clock_probe, realtime_khz
+        self._probe = clock_probe
+        self.buf = torch.zeros((2, 3 * self.N), dtype=torch.int64, device=dev)
+        self.stream = stream
+        self.khz = realtime_khz()
+
+    def __call__(self, i):
+        self._probe(self.buf[i], self.N, self.stream.cuda_stream)
+
+    def per_xcd_hz(self):
+        """{XCD id: mean clock in Hz} for the XCDs stamped by both probes."""
+        b = self.buf.cpu().numpy().reshape(2, self.N, 3)
+        pre = {int(r[2]): r for r in b[0]}
+        post = {int(r[2]): r for r in b[1]}
+        out = {}
+        for x, r0 in pre.items():
+            r1 = post.get(x)
+            if r1 is None:
+                continue
+            dc, dr = int(r1[0]) - int(r0[0]), int(r1[1]) - int(r0[1])
+            if dc > 0 and dr > 0:
+                out[x] = dc / (dr / (self.khz * 1e3))
+        return out
+
+
+def time_steps(step, stream, steps, warmup, probe=None):
     """Run ``warmup`` untimed steps, then ``steps`` timed ones with a HIP
     event pair around each call (on the launch stream) and one pair around
-    all of them.  Returns (total ms, per-call ms list, wall s)."""
+    all of them; ``probe`` (a ClockProbe) is enqueued just outside that
+    pair.  Returns (total ms, per-call ms list, wall s)."""
     import torch
     for _ in range(warmup):
         step()
+    if probe is not None:
+        probe(0)   # first launch of the probe kernel outside the timed region
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
@@ -222,12 +261,16 @@ def time_steps(step, stream, steps, warmup):
     ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
+    if probe is not None:
+        probe(0)
     ev0.record(stream)
     for a, b in ev:
         a.record(stream)
         step()
         b.record(stream)
     ev1.record(stream)
+    if probe is not None:
+        probe(1)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     return ev0.elapsed_time(ev1), [a.elapsed_time(b) for a, b in ev], wall
@@ -341,7 +384,9 @@ def main():
     else:
         step = lambda: splash_fwd(qd, kd, vd, **kw)
     stream = torch.cuda.current_stream(dev)
-    ms_total, per_call, wall = time_steps(step, stream, args.steps, args.warmup)
+    probe = ClockProbe(dev, stream)
+    ms_total, per_call, wall = time_steps(step, stream, args.steps, args.warmup, probe)
+    clock_hz = probe.per_xcd_hz()
     ms_per_step = ms_total / args.steps
     ms_median, ms_min = median_min(per_call)
     ms_cold = None if args.no_cold else time_cold(step, stream, dev)
@@ -370,6 +415,23 @@ def main():
         roofline = {"bound": "mfma" if w.dtype == "bf16" else "alu",
                     "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
                     "frac": round(tflops / peak, 4), "traffic": traffic}
+
+    # The shader clock over the timed steps (median over the XCDs).  The
+    # matrix and vector peaks scale with it (the published ones assume
+    # 2.4 GHz on 256 CUs); HBM bandwidth does not.
+    clock = None
+    if clock_hz:
+        ghz = sorted(clock_hz.values())
+        f = 0.5 * (ghz[(len(ghz) - 1) // 2] + ghz[len(ghz) // 2])
+        n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
+        clock = {"ghz": round(f / 1e9, 3), "xcd_min_ghz": round(ghz[0] / 1e9, 3),
+                 "xcd_max_ghz": round(ghz[-1] / 1e9, 3), "n_xcd": len(ghz), "n_cu": n_cu,
+                 "method": "per-XCD core-clock cycles over real time between two clock "
+                           "probes enqueued around the timed steps"}
+        if roofline["bound"] != "hbm":
+            peak_clk = peak * (n_cu / 256.0) * (f / PEAK_CLOCK_HZ)
+            roofline["peak_at_clock"] = round(peak_clk, 1)
+            roofline["frac_at_clock"] = round(tflops / peak_clk, 4)
 
     # Skipped-block speedup against mask sparsity (Lecture 13 section 6.4):
     # the same shape and inputs under the causal mask alone.
@@ -422,6 +484,8 @@ def main():
                    "n_split": args.n_split, "pass": "backward" if args.backward else "forward",
                    "parallelism": "single GPU"},
         "pct_of_peak": round(100.0 * tflops / peak, 2),
+        "pct_of_peak_at_clock": roofline.get("frac_at_clock") and round(100.0 * roofline["frac_at_clock"], 2),
+        "clock": clock,
         "unmasked_tflop_per_step": flop_per_step / 1e12,
         "active_blocks": tabs.n_active, "partial_blocks": tabs.n_partial,
         "mask_compile_ms": round(mask_ms, 3),

@@ -30,7 +30,8 @@ EXPORTED = ("splash_version", "splash_last_error", "attn_mask_compile",
             "splash_fwd_tile", "splash_fwd_tiles", "splash_attn_fwd",
             "splash_split_workspace_bytes", "splash_attn_fwd_split",
             "splash_attn_fwd_split_noalloc", "attn_mask_columns",
-            "splash_bwd_tile", "splash_attn_bwd")
+            "splash_bwd_tile", "splash_attn_bwd", "splash_clock_probe",
+            "splash_realtime_khz")
 SPLASH_MAX_SPLIT = 64
 SPLASH_STATIC_SCRATCH_BYTES = 16 << 20
 
@@ -145,6 +146,10 @@ def load():
         lib.attn_mask_columns.argtypes = [c_i32, c_i32, c_i32, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr]
         lib.splash_attn_bwd.restype = ctypes.c_int
         lib.splash_attn_bwd.argtypes = [ctypes.POINTER(BwdArgs), c_ptr]
+        lib.splash_clock_probe.restype = ctypes.c_int
+        lib.splash_clock_probe.argtypes = [c_ptr, c_i32, c_ptr]
+        lib.splash_realtime_khz.restype = ctypes.c_int
+        lib.splash_realtime_khz.argtypes = [ctypes.POINTER(c_i32)]
         _lib = lib
         return lib
 

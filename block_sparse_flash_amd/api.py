@@ -383,6 +383,29 @@ def split_workspace_bytes(n_split: int, B: int, Hq: int, L: int, d_v: int) -> in
     return nb.value
 
 
+def clock_probe(out, n_groups: int = 8, stream=None) -> None:
+    """Enqueue ``splash_clock_probe``: ``n_groups`` single-wave work-groups
+    write (shader-clock cycles, real-time counter, XCD id) into ``out``, an
+    int64 device tensor of at least 3 * n_groups elements (measurement only),
+    on ``stream`` (a raw stream handle; None: torch's current stream)."""
+    import torch
+    lib = _lib.load()
+    if out.dtype != torch.int64 or not out.is_cuda or not out.is_contiguous() or out.numel() < 3 * n_groups:
+        raise ValueError("out must be a contiguous int64 device tensor of >= 3 * n_groups elements")
+    if stream is None:
+        stream = torch.cuda.current_stream(out.device).cuda_stream
+    _lib.check(lib.splash_clock_probe(ctypes.c_void_p(out.data_ptr()), int(n_groups),
+                                      ctypes.c_void_p(stream)))
+
+
+def realtime_khz() -> int:
+    """Rate of the current device's real-time counter in kHz (``splash_realtime_khz``)."""
+    lib = _lib.load()
+    khz = ctypes.c_int32()
+    _lib.check(lib.splash_realtime_khz(ctypes.byref(khz)))
+    return khz.value
+
+
 def _segment_rows(seg, B, n, device, name):
     """Segment ids [n] or [B, n] as a device int32 tensor [B, n] (None stays None)."""
     import torch

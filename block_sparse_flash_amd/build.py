@@ -32,6 +32,7 @@ SOURCES = [
     "splash_bwd_api.cpp",
     "splash_bwd_bf16.hip",
     "splash_noalloc.hip",
+    "clock_probe.hip",
 ]
 
 ARCH = "gfx950"

@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define SPLASH_VERSION 107
+#define SPLASH_VERSION 108
 
 /* Largest n_split of splash_attn_fwd_split. */
 #define SPLASH_MAX_SPLIT 64
@@ -430,6 +430,32 @@ typedef struct splash_bwd_args {
  * SPLASH_EHIP (a launch failed).  B, Hq or L equal to 0 writes dk and dv
  * only if it has keys (zeros); all sizes 0 is a no-op. */
 int splash_attn_bwd(const splash_bwd_args* args, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Clock probe (measurement only; not part of the attention computation).
+ * The MFMA peak scales with the shader clock, which the chip lowers under
+ * load; these two calls let a caller measure the mean clock over a run of
+ * kernels and price its throughput against the peak at that clock.
+ * ---------------------------------------------------------------------- */
+
+/* Enqueue on `stream` (a hipStream_t; NULL = the default stream) n_groups
+ * work-groups of one wave.  Work-group g writes out[3g] = the shader clock
+ * counter (s_memtime: core clock cycles, counted per XCD), out[3g + 1] = the
+ * constant-rate real-time counter (s_memrealtime) and out[3g + 2] = the id of
+ * the XCD it ran on.  `out`: caller-owned device memory of 3 * n_groups
+ * uint64 values.  Consecutive work-groups go round-robin over the XCDs, so
+ * n_groups = 8 stamps every XCD of an MI355X once.  Two probes enqueued
+ * before and after a run of kernels give each XCD's mean clock over the run:
+ * (cycles after - cycles before) / (real after - real before) times the
+ * real-time counter's rate (splash_realtime_khz), pairing records by XCD id.
+ * Errors: SPLASH_EINVAL (NULL out, n_groups outside 1..64), SPLASH_EHIP
+ * (launch failed). */
+int splash_clock_probe(uint64_t* out, int n_groups, void* stream);
+
+/* Rate of the current device's real-time counter in kHz
+ * (hipDeviceAttributeWallClockRate) into *khz.  Errors: SPLASH_EINVAL (NULL),
+ * SPLASH_EHIP. */
+int splash_realtime_khz(int* khz);
 
 #ifdef __cplusplus
 }  /* extern "C" */
