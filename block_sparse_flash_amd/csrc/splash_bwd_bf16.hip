@@ -589,10 +589,16 @@ struct DqLds {
   static constexpr bool Q_IN_LDS = DQK > 128;
   static constexpr int RK = Lay<DQK, true>::ROW;
   static constexpr int RV = Lay<DV, true>::ROW;
+  // One buffer of a kv block: K, V and key segment ids (offsets inside it).
   static constexpr int K_OFF = 0;                      // K [64][RK]
   static constexpr int V_OFF = K_OFF + 64 * RK * 2;    // V [64][RV]
   static constexpr int SEG_OFF = V_OFF + 64 * RV * 2;  // key segment ids [64]
-  static constexpr int Q_OFF = SEG_OFF + 64 * 4;       // Q [BQ][RK] when Q_IN_LDS
+  static constexpr int BUF = SEG_OFF + 64 * 4;
+  // Two buffers where they fit beside Q (heads up to 128 wide): block x+1 is
+  // stored while no wave reads its buffer any more, so one barrier per block
+  // orders both the reuse and the visibility.
+  static constexpr int NBUF = Q_IN_LDS ? 1 : 2;
+  static constexpr int Q_OFF = NBUF * BUF;             // Q [BQ][RK] when Q_IN_LDS
   static constexpr int BYTES = Q_OFF + (Q_IN_LDS ? BQ * RK * 2 : 0);
   static_assert(BYTES <= 163840, "fits the LDS of a CU");
 };
@@ -606,9 +612,6 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   typedef __attribute__((address_space(3))) uint8_t lds_u8;
   lds_u8* lds = (lds_u8*)smem;
-  lds_u16* Ks = (lds_u16*)(lds + M::K_OFF);
-  lds_u16* Vs = (lds_u16*)(lds + M::V_OFF);
-  lds_i32* segks = (lds_i32*)(lds + M::SEG_OFF);
   lds_u16* Qs = (lds_u16*)(lds + M::Q_OFF);
 
   const int tid = threadIdx.x;
@@ -686,15 +689,35 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
     v_next.fetch(v_rs, key0, tid);
     if (tid < BK) seg_next = (has_seg && key0 + tid < p.Lkv) ? segk[key0 + tid] : 0;
   };
+  auto store_next = [&](int buf) __attribute__((always_inline)) {
+    k_next.store((lds_u16*)(lds + buf * M::BUF + M::K_OFF), tid);
+    v_next.store((lds_u16*)(lds + buf * M::BUF + M::V_OFF), tid);
+    if (tid < BK) ((lds_i32*)(lds + buf * M::BUF + M::SEG_OFF))[tid] = seg_next;
+  };
+  constexpr bool DB = M::NBUF == 2;
   if (x0 < x1) fetch(x0);
+  if constexpr (DB) {
+    // Double buffering: block x+1 goes into the buffer of block x-1, which
+    // every wave finished reading before the barrier that closed block x-1;
+    // the barrier that closes block x makes it visible.
+    if (x0 < x1) {
+      store_next(0);
+      if (x0 + 1 < x1) fetch(x0 + 1);
+    }
+    __syncthreads();
+  }
   for (int x = x0; x < x1; ++x) {
     const int key0 = p.active_cols[x] * BK;
-    __syncthreads();  // the previous block is consumed
-    k_next.store(Ks, tid);
-    v_next.store(Vs, tid);
-    if (tid < BK) segks[tid] = seg_next;
-    __syncthreads();
-    if (x + 1 < x1) fetch(x + 1);
+    const int cur = DB ? (x - x0) & 1 : 0;
+    if constexpr (!DB) {
+      __syncthreads();  // the previous block is consumed
+      store_next(0);
+      __syncthreads();
+      if (x + 1 < x1) fetch(x + 1);
+    }
+    const lds_u16* Ks = (const lds_u16*)(lds + cur * M::BUF + M::K_OFF);
+    const lds_u16* Vs = (const lds_u16*)(lds + cur * M::BUF + M::V_OFF);
+    const lds_i32* segks = (const lds_i32*)(lds + cur * M::BUF + M::SEG_OFF);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       // S^T = K Q^T and dP^T = V dO^T (interleaved chains): keys 32t + items, row l32.
@@ -747,6 +770,13 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
             },
             [&](int dt, const bf16x8& b) { dqacc[dt] = mfma(da8, b, dqacc[dt]); });
       }
+    }
+    if constexpr (DB) {
+      if (x + 1 < x1) {
+        store_next(cur ^ 1);
+        if (x + 2 < x1) fetch(x + 2);
+      }
+      __syncthreads();
     }
   }
 
