@@ -32,20 +32,76 @@ def _seg_array(seg, L):
     return a
 
 
-def _mask_key(causal, window_left, window_right, seg_q, seg_kv, q_offset):
-    """What a table was compiled for: the mask parameters and a digest of
-    the segment ids (key ids default to the query ids)."""
+def _seg_digest(seg_q, seg_kv):
+    """Digest of one row of query and key segment ids (key ids default to
+    the query ids)."""
     import hashlib
-    digest = None
-    if seg_q is not None:
-        h = hashlib.sha256()
-        sq = np.ascontiguousarray(np.asarray(seg_q).reshape(-1), dtype=np.int32)
-        skv = sq if seg_kv is None else np.ascontiguousarray(np.asarray(seg_kv).reshape(-1), dtype=np.int32)
-        h.update(sq.tobytes())
-        h.update(b"|")
-        h.update(skv.tobytes())
-        digest = h.hexdigest()
+    h = hashlib.sha256()
+    sq = np.ascontiguousarray(np.asarray(seg_q).reshape(-1), dtype=np.int32)
+    skv = sq if seg_kv is None else np.ascontiguousarray(np.asarray(seg_kv).reshape(-1), dtype=np.int32)
+    h.update(sq.tobytes())
+    h.update(b"|")
+    h.update(skv.tobytes())
+    return h.hexdigest()
+
+
+def _mask_key(causal, window_left, window_right, seg_q, seg_kv, q_offset, digest=None):
+    """What a table was compiled for: the mask parameters and a digest of
+    the segment ids (``digest``, or computed from seg_q / seg_kv)."""
+    if digest is None and seg_q is not None:
+        digest = _seg_digest(seg_q, seg_kv)
     return (bool(causal), int(window_left), int(window_right), digest, int(q_offset))
+
+
+def _host_rows(seg, n, name):
+    """Segment ids ([n] or [rows, n], numpy or torch) as a host int32 array
+    [rows, n]."""
+    a = seg.detach().cpu().numpy() if hasattr(seg, "detach") else np.asarray(seg)
+    a = np.ascontiguousarray(a, dtype=np.int32)
+    if a.ndim not in (1, 2) or a.shape[-1] != n:
+        raise ValueError(f"{name} must be [{n}] or [B, {n}]; got shape {tuple(a.shape)}")
+    return a.reshape(-1, n)
+
+
+def _segments(seg_q, seg_kv, B, L, L_kv, device, cache=None):
+    """The segment ids of a call: host rows ``hq`` / ``hkv`` (1 or B rows),
+    whether the batch rows differ (``per_batch``), device copies
+    ``dev_q`` [B, L] / ``dev_kv`` [B, L_kv] and the digest of row 0
+    (``digest0``); None without segment ids.  With ``cache`` (the dict of the
+    MaskTables the call uses) a call with the same ids as the previous one
+    reuses its device copies and digest: no host-device copy, no
+    synchronisation and no hashing per call."""
+    import torch
+    if seg_q is None:
+        if seg_kv is not None:
+            raise ValueError("seg_kv given without seg_q")
+        return None
+    hq = _host_rows(seg_q, L, "seg_q")
+    hkv = None if seg_kv is None else _host_rows(seg_kv, L_kv, "seg_kv")
+    if hkv is None and L_kv != L:
+        raise ValueError("seg_kv is required when L_kv != L")
+    if hq.shape[0] not in (1, B) or (hkv is not None and hkv.shape[0] not in (1, B)):
+        raise ValueError("segment ids must be [L] or [B, L] ([L_kv] or [B, L_kv] for seg_kv)")
+    dkey = str(torch.device(device))
+    if cache is not None:
+        c = cache.get("seg")
+        if (c is not None and c["B"] == B and c["device"] == dkey and np.array_equal(c["hq"], hq)
+                and ((hkv is None and c["hkv"] is None)
+                     or (hkv is not None and c["hkv"] is not None and np.array_equal(c["hkv"], hkv)))):
+            return c
+    per_batch = B > 1 and (bool((hq != hq[:1]).any()) or (hkv is not None and bool((hkv != hkv[:1]).any())))
+    up = lambda h, n: torch.from_numpy(np.array(np.broadcast_to(h, (B, n)), dtype=np.int32)).to(device)
+    rec = {"B": B, "device": dkey, "hq": hq.copy(), "hkv": None if hkv is None else hkv.copy(),
+           "per_batch": per_batch, "dev_q": up(hq, L), "dev_kv": None if hkv is None else up(hkv, L_kv),
+           "digest0": _seg_digest(hq[0], None if hkv is None else hkv[0])}
+    if cache is not None:
+        cache["seg"] = rec
+    return rec
+
+
+def _seg_row(h, b):
+    """Row b of host segment ids held as 1 or B rows (None stays None)."""
+    return None if h is None else h[b if h.shape[0] > 1 else 0]
 
 
 def _check_tables(tabs, bq, bkv, L, L_kv, key):
@@ -278,26 +334,11 @@ def splash_fwd(q, k, v, *, scale: Optional[float] = None, soft_cap: float = 0.0,
     bq, bkv = ((tables.block_q, tables.block_kv) if tables is not None
                else pick_tile(dt, d_qk, d_v, L, Hq // max(Hkv, 1)))
 
-    seg_q_dev = seg_kv_dev = None
-    per_batch = False
-    if seg_q is not None:
-        sq = torch.as_tensor(np.asarray(seg_q.cpu() if hasattr(seg_q, "cpu") else seg_q),
-                             dtype=torch.int32)
-        sq = sq.reshape(-1, L)
-        skv = None
-        if seg_kv is not None:
-            skv = torch.as_tensor(np.asarray(seg_kv.cpu() if hasattr(seg_kv, "cpu") else seg_kv),
-                                  dtype=torch.int32).reshape(-1, L_kv)
-        elif L_kv != L:
-            raise ValueError("seg_kv is required when L_kv != L")
-        rows_q = sq.expand(B, L) if sq.shape[0] == 1 else sq
-        rows_kv = None if skv is None else (skv.expand(B, L_kv) if skv.shape[0] == 1 else skv)
-        if rows_q.shape[0] != B or (rows_kv is not None and rows_kv.shape[0] != B):
-            raise ValueError("segment ids must be [L] or [B, L] ([L_kv] or [B, L_kv] for seg_kv)")
-        per_batch = B > 1 and (not bool((rows_q == rows_q[:1]).all()) or
-                               (rows_kv is not None and not bool((rows_kv == rows_kv[:1]).all())))
-        seg_q_dev = rows_q.contiguous().to(q.device)
-        seg_kv_dev = None if rows_kv is None else rows_kv.contiguous().to(q.device)
+    segs = _segments(seg_q, seg_kv, B, L, L_kv, q.device,
+                     None if tables is None else tables._device)
+    seg_q_dev = None if segs is None else segs["dev_q"]
+    seg_kv_dev = None if segs is None else segs["dev_kv"]
+    per_batch = segs is not None and segs["per_batch"]
 
     _check_out(out, "out", (B, Hq, L, d_v), q.dtype, q.device)
     _check_out(lse, "lse", (B, Hq, L), torch.float32, q.device)
@@ -324,18 +365,18 @@ def splash_fwd(q, k, v, *, scale: Optional[float] = None, soft_cap: float = 0.0,
 
     batches = range(B) if per_batch else [None]
     for bsel in batches:
+        ids_q = None if segs is None else _seg_row(segs["hq"], bsel or 0)
+        ids_kv = None if segs is None else _seg_row(segs["hkv"], bsel or 0)
         if tables is None or per_batch:
-            ids_q = None if seg_q_dev is None else seg_q_dev[bsel or 0].cpu().numpy()
-            ids_kv = None if seg_kv_dev is None else seg_kv_dev[bsel or 0].cpu().numpy()
             tabs = compile_mask(L, bq, bkv, L_kv=L_kv, causal=causal, window_left=window_left,
                                 window_right=window_right, seg_q=ids_q, seg_kv=ids_kv,
                                 q_offset=q_offset)
+            digest = None
         else:
             tabs = tables
-            ids_q = None if seg_q_dev is None else seg_q_dev[0].cpu().numpy()
-            ids_kv = None if seg_kv_dev is None else seg_kv_dev[0].cpu().numpy()
+            digest = None if segs is None else segs["digest0"]
         _check_tables(tabs, bq, bkv, L, L_kv,
-                      _mask_key(causal, window_left, window_right, ids_q, ids_kv, q_offset))
+                      _mask_key(causal, window_left, window_right, ids_q, ids_kv, q_offset, digest))
         dev = tabs.device(q.device)
         if bsel is None:
             qb, kb, vb, ob = q, k, v, out
@@ -406,20 +447,6 @@ def realtime_khz() -> int:
     return khz.value
 
 
-def _segment_rows(seg, B, n, device, name):
-    """Segment ids [n] or [B, n] as a device int32 tensor [B, n] (None stays None)."""
-    import torch
-    if seg is None:
-        return None
-    t = torch.as_tensor(np.asarray(seg.cpu() if hasattr(seg, "cpu") else seg), dtype=torch.int32)
-    t = t.reshape(-1, n)
-    if t.shape[0] == 1:
-        t = t.expand(B, n)
-    if t.shape[0] != B:
-        raise ValueError(f"{name} must be [{n}] or [B, {n}]")
-    return t.contiguous().to(device)
-
-
 def splash_bwd(q, k, v, o, lse, dout, *, scale: Optional[float] = None, soft_cap: float = 0.0,
                causal: bool = False, window_left: int = -1, window_right: int = -1,
                seg_q=None, seg_kv=None, q_offset: int = 0, tables: Optional[MaskTables] = None,
@@ -451,14 +478,11 @@ def splash_bwd(q, k, v, o, lse, dout, *, scale: Optional[float] = None, soft_cap
     if scale is None:
         scale = 1.0 / float(d_qk) ** 0.5
     bq, bkv = bwd_tile("bf16", d_qk, d_v)
-    if seg_q is None and seg_kv is not None:
-        raise ValueError("seg_kv given without seg_q")
-    if seg_q is not None and seg_kv is None and L_kv != L:
-        raise ValueError("seg_kv is required when L_kv != L")
-    sq = _segment_rows(seg_q, B, L, q.device, "seg_q")
-    skv = _segment_rows(seg_kv, B, L_kv, q.device, "seg_kv")
-    per_batch = B > 1 and sq is not None and (
-        not bool((sq == sq[:1]).all()) or (skv is not None and not bool((skv == skv[:1]).all())))
+    segs = _segments(seg_q, seg_kv, B, L, L_kv, q.device,
+                     None if tables is None else tables._device)
+    sq = None if segs is None else segs["dev_q"]
+    skv = None if segs is None else segs["dev_kv"]
+    per_batch = segs is not None and segs["per_batch"]
     dq = torch.empty((B, Hq, L, d_qk), dtype=torch.float32, device=q.device)
     dk = torch.empty((B, Hkv, L_kv, d_qk), dtype=torch.float32, device=q.device)
     dv = torch.empty((B, Hkv, L_kv, d_v), dtype=torch.float32, device=q.device)
@@ -467,16 +491,18 @@ def splash_bwd(q, k, v, o, lse, dout, *, scale: Optional[float] = None, soft_cap
         stream = torch.cuda.current_stream(q.device).cuda_stream
     for bsel in (range(B) if per_batch else [None]):
         b0 = bsel or 0
-        ids_q = None if sq is None else sq[b0].cpu().numpy()
-        ids_kv = None if skv is None else skv[b0].cpu().numpy()
+        ids_q = None if segs is None else _seg_row(segs["hq"], b0)
+        ids_kv = None if segs is None else _seg_row(segs["hkv"], b0)
         if tables is None or per_batch:
             tabs = compile_mask(L, bq, bkv, L_kv=L_kv, causal=causal, window_left=window_left,
                                 window_right=window_right, q_offset=q_offset,
                                 seg_q=ids_q, seg_kv=ids_kv)
+            digest = None
         else:
             tabs = tables
+            digest = None if segs is None else segs["digest0"]
         _check_tables(tabs, bq, bkv, L, L_kv,
-                      _mask_key(causal, window_left, window_right, ids_q, ids_kv, q_offset))
+                      _mask_key(causal, window_left, window_right, ids_q, ids_kv, q_offset, digest))
         dev = tabs.device(q.device)
         cdev = tabs.device_columns(q.device)
         sl = slice(None) if bsel is None else slice(bsel, bsel + 1)

@@ -421,3 +421,35 @@ def test_tables_refuse_another_mask():
             _check_tables(t, bq, bkv, L, L, key)
     with pytest.raises(ValueError, match="block_q"):
         _check_tables(t, bq, bkv, L + 1, L + 1, same)
+
+
+def test_segment_ids_are_cached_per_tables():
+    """The binding's segment-id handling: host rows, the per-batch flag, the
+    digest the table check uses, and reuse of the device copies while the
+    ids stay the same (no copy, synchronisation or hashing per call)."""
+    from block_sparse_flash_amd.api import _seg_digest, _segments
+    L = 300
+    seg = segment_ids(L, 7, 20, 90)
+    cache = {}
+    a = _segments(seg, None, 2, L, L, "cpu", cache)
+    assert not a["per_batch"] and a["hq"].shape == (1, L) and a["hkv"] is None
+    assert tuple(a["dev_q"].shape) == (2, L) and (a["dev_q"].numpy() == seg).all()
+    assert a["digest0"] == _seg_digest(seg, None) == _seg_digest(seg, seg)
+    assert _segments(seg.copy(), None, 2, L, L, "cpu", cache) is a          # same ids: cached
+    other = seg.copy()
+    other[L // 2:] += 1
+    b = _segments(other, None, 2, L, L, "cpu", cache)
+    assert b is not a and b["digest0"] != a["digest0"] and cache["seg"] is b
+    c = _segments(np.stack([seg, other]), None, 2, L, L, "cpu", cache)
+    assert c["per_batch"] and c["hq"].shape == (2, L)
+    d = _segments(np.stack([seg, seg]), None, 2, L, L, "cpu", None)
+    assert not d["per_batch"]
+    assert _segments(None, None, 2, L, L, "cpu", cache) is None
+    with pytest.raises(ValueError, match="seg_kv given without seg_q"):
+        _segments(None, seg, 2, L, L, "cpu")
+    with pytest.raises(ValueError, match="seg_kv is required"):
+        _segments(seg, None, 2, L, L + 5, "cpu")
+    with pytest.raises(ValueError, match="must be"):
+        _segments(np.stack([seg, seg, seg]), None, 2, L, L, "cpu")
+    with pytest.raises(ValueError, match="must be"):
+        _segments(seg[:-1], None, 2, L, L, "cpu")
