@@ -240,6 +240,25 @@ def test_more_items_than_work_groups():
     _announce(f"  max-abs o {eo:.3g} lse {el:.3g}")
 
 
+def test_persistent_rounds_items_of_one_to_many_blocks():
+    """The ping-pong loop passes n + 2 work-group barriers per item of n
+    blocks, the same count in both wave groups.  The 64-row decode tile on
+    causal L=700 gives items of 1 to 11 blocks; 2 x 24 heads make 528 items,
+    more than the 512 persistent work-groups (two per CU), so work-groups
+    chain items of different lengths (one-block items included).  Every
+    output element is checked."""
+    _announce("persistent rounds, 64x64 tile: B=2 Hq=24 Hkv=8 L=700 d=128, causal")
+    B, Hq, Hkv, L, d = 2, 24, 8, 700, 128
+    q, k, v = (stored(a, "bf16") for a in draw_qkv(B, Hq, Hkv, L, d, d, 37))
+    t = compile_mask(L, 64, 64, causal=True)
+    rows = np.diff(t.row_ptr)
+    assert rows.min() == 1 and rows.max() == 11
+    o, lse = _run(q, k, v, causal=True, tables=t)
+    o_ref, lse_ref = attention_ref(as_f64(q), as_f64(k), as_f64(v), scale=d ** -0.5, causal=True)
+    eo, el = _compare(o, lse, o_ref, lse_ref, "bf16")
+    _announce(f"  max-abs o {eo:.3g} lse {el:.3g}")
+
+
 SPLIT_CASES = [
     # (B, Hq, Hkv, L, d_qk, d_v, mask kwargs, soft_cap, n_split)
     (1, 2, 2, 1000, 128, 128, dict(causal=True), 0.0, 2),
