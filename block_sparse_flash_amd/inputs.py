@@ -97,10 +97,10 @@ EXTRA_WORKLOADS = {
     # Decoding 16 new rows per sequence (speculative or multi-token decode)
     # against a 32768-position K/V cache: GQA 32/8, causal, the new rows at
     # the last 16 positions; the 4 query heads of a K/V head packed into one
-    # 64-row decode tile, split-KV into 8 chunks per row.
+    # 64-row decode tile, split-KV into 4 chunks per row.
     "decode_gqa_bf16_Lq16_Lkv32768": Workload(
         "decode_gqa_bf16_Lq16_Lkv32768", "bf16", 8, 32, 8, 16, 128, 128,
-        causal=True, seed=7, L_kv=32768, q_offset=32768 - 16, n_split=8, tile=(64, 64)),
+        causal=True, seed=7, L_kv=32768, q_offset=32768 - 16, n_split=4, tile=(64, 64)),
 }
 ALL_WORKLOADS = {**WORKLOADS, **EXTRA_WORKLOADS}
 
