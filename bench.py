@@ -210,12 +210,14 @@ def median_min(xs):
 
 
 class ClockProbe:
-    """Mean shader clock of each XCD over the timed steps: the library's clock
-    probe (one single-wave work-group per XCD records its core-clock cycle
-    counter, the constant-rate real-time counter and its XCD id) enqueued on
-    the launch stream just before and just after them."""
+    """Mean shader clock of the CUs over the timed steps: the library's clock
+    probe (single-wave work-groups that record their CU's core-clock cycle
+    counter, the constant-rate real-time counter and their location)
+    enqueued on the launch stream just before and just after them.  The
+    cycle counters of different CUs are not in step, so only a CU stamped by
+    both probes gives a clock."""
 
-    N = 8   # work-groups per probe: one per XCD (round-robin placement)
+    N = 256   # work-groups per probe (the dispatcher spreads them over the CUs)
 
     def __init__(self, dev, stream):
         import torch
@@ -228,19 +230,18 @@ class ClockProbe:
     def __call__(self, i):
         self._probe(self.buf[i], self.N, self.stream.cuda_stream)
 
-    def per_xcd_hz(self):
-        """{XCD id: mean clock in Hz} for the XCDs stamped by both probes."""
+    def per_cu_hz(self):
+        """{location: mean clock in Hz} for the CUs stamped once by each probe."""
         b = self.buf.cpu().numpy().reshape(2, self.N, 3)
-        pre = {int(r[2]): r for r in b[0]}
-        post = {int(r[2]): r for r in b[1]}
         out = {}
-        for x, r0 in pre.items():
-            r1 = post.get(x)
-            if r1 is None:
-                continue
-            dc, dr = int(r1[0]) - int(r0[0]), int(r1[1]) - int(r0[1])
+        for loc in set(int(x) for x in b[0, :, 2]) & set(int(x) for x in b[1, :, 2]):
+            r0 = b[0][b[0, :, 2] == loc]
+            r1 = b[1][b[1, :, 2] == loc]
+            if len(r0) != 1 or len(r1) != 1:
+                continue   # two work-groups on one CU: which came first is unknown
+            dc, dr = int(r1[0, 0]) - int(r0[0, 0]), int(r1[0, 1]) - int(r0[0, 1])
             if dc > 0 and dr > 0:
-                out[x] = dc / (dr / (self.khz * 1e3))
+                out[loc] = dc / (dr / (self.khz * 1e3))
         return out
 
 
@@ -386,7 +387,7 @@ def main():
     stream = torch.cuda.current_stream(dev)
     probe = ClockProbe(dev, stream)
     ms_total, per_call, wall = time_steps(step, stream, args.steps, args.warmup, probe)
-    clock_hz = probe.per_xcd_hz()
+    clock_hz = probe.per_cu_hz()
     ms_per_step = ms_total / args.steps
     ms_median, ms_min = median_min(per_call)
     ms_cold = None if args.no_cold else time_cold(step, stream, dev)
@@ -416,17 +417,18 @@ def main():
                     "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
                     "frac": round(tflops / peak, 4), "traffic": traffic}
 
-    # The shader clock over the timed steps (median over the XCDs).  The
-    # matrix and vector peaks scale with it (the published ones assume
-    # 2.4 GHz on 256 CUs); HBM bandwidth does not.
+    # The shader clock over the timed steps (median over the CUs stamped by
+    # both probes).  The matrix and vector peaks scale with it (the published
+    # ones assume 2.4 GHz on 256 CUs); HBM bandwidth does not.
     clock = None
-    if clock_hz:
+    n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
+    if len(clock_hz) >= n_cu // 4:
         ghz = sorted(clock_hz.values())
         f = 0.5 * (ghz[(len(ghz) - 1) // 2] + ghz[len(ghz) // 2])
-        n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
-        clock = {"ghz": round(f / 1e9, 3), "xcd_min_ghz": round(ghz[0] / 1e9, 3),
-                 "xcd_max_ghz": round(ghz[-1] / 1e9, 3), "n_xcd": len(ghz), "n_cu": n_cu,
-                 "method": "per-XCD core-clock cycles over real time between two clock "
+        clock = {"ghz": round(f / 1e9, 3), "cu_p10_ghz": round(ghz[len(ghz) // 10] / 1e9, 3),
+                 "cu_p90_ghz": round(ghz[(9 * len(ghz)) // 10] / 1e9, 3), "n_cu_stamped": len(ghz),
+                 "n_cu": n_cu,
+                 "method": "per-CU core-clock cycles over real time between two clock "
                            "probes enqueued around the timed steps"}
         if roofline["bound"] != "hbm":
             peak_clk = peak * (n_cu / 256.0) * (f / PEAK_CLOCK_HZ)

@@ -11,21 +11,26 @@
 
 namespace {
 
-// s_getreg operand of HW_REG_XCC_ID (hardware register 20 on gfx940 and
-// later), bits 3:0: the XCD the wave runs on.
+// s_getreg operands: HW_REG_XCC_ID (hardware register 20 on gfx940 and
+// later), bits 3:0 = the XCD; HW_REG_HW_ID (register 4), bits 15:8 = the
+// CU, shader array and shader engine inside it.
 constexpr int kXccIdReg = (3 << 11) | 20;
+constexpr int kHwIdReg = (31 << 11) | 4;
 
 // One wave per work-group: the core-clock cycle counter, the constant-rate
-// real-time counter and the XCD id, read back to back and stored by lane 0.
+// real-time counter and where the wave runs, read back to back and stored by
+// lane 0.  The cycle counters of different CUs are not in step, so only
+// stamps taken on the same CU (same location word) can be subtracted.
 __global__ __launch_bounds__(64) void clock_probe_kernel(uint64_t* out) {
   const uint64_t cycles = __builtin_amdgcn_s_memtime();
   const uint64_t real = __builtin_amdgcn_s_memrealtime();
   const uint32_t xcc = (uint32_t)__builtin_amdgcn_s_getreg(kXccIdReg) & 15u;
+  const uint32_t hw = (uint32_t)__builtin_amdgcn_s_getreg(kHwIdReg) & 0xff00u;
   if (threadIdx.x == 0) {
     uint64_t* o = out + 3 * (size_t)blockIdx.x;
     o[0] = cycles;
     o[1] = real;
-    o[2] = xcc;
+    o[2] = (xcc << 16) | hw;
   }
 }
 
@@ -34,8 +39,8 @@ __global__ __launch_bounds__(64) void clock_probe_kernel(uint64_t* out) {
 extern "C" int splash_clock_probe(uint64_t* out, int n_groups, void* stream) {
   splash::clear_error();
   if (!out) return splash::fail(SPLASH_EINVAL, "splash_clock_probe: NULL out");
-  if (n_groups < 1 || n_groups > 64)
-    return splash::fail(SPLASH_EINVAL, "splash_clock_probe: n_groups %d outside 1..64", n_groups);
+  if (n_groups < 1 || n_groups > 4096)
+    return splash::fail(SPLASH_EINVAL, "splash_clock_probe: n_groups %d outside 1..4096", n_groups);
   hipLaunchKernelGGL(clock_probe_kernel, dim3((unsigned)n_groups), dim3(64), 0,
                      static_cast<hipStream_t>(stream), out);
   const hipError_t e = hipGetLastError();

@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define SPLASH_VERSION 108
+#define SPLASH_VERSION 109
 
 /* Largest n_split of splash_attn_fwd_split. */
 #define SPLASH_MAX_SPLIT 64
@@ -440,16 +440,18 @@ int splash_attn_bwd(const splash_bwd_args* args, void* stream);
 
 /* Enqueue on `stream` (a hipStream_t; NULL = the default stream) n_groups
  * work-groups of one wave.  Work-group g writes out[3g] = the shader clock
- * counter (s_memtime: core clock cycles, counted per XCD), out[3g + 1] = the
- * constant-rate real-time counter (s_memrealtime) and out[3g + 2] = the id of
- * the XCD it ran on.  `out`: caller-owned device memory of 3 * n_groups
- * uint64 values.  Consecutive work-groups go round-robin over the XCDs, so
- * n_groups = 8 stamps every XCD of an MI355X once.  Two probes enqueued
- * before and after a run of kernels give each XCD's mean clock over the run:
- * (cycles after - cycles before) / (real after - real before) times the
- * real-time counter's rate (splash_realtime_khz), pairing records by XCD id.
- * Errors: SPLASH_EINVAL (NULL out, n_groups outside 1..64), SPLASH_EHIP
- * (launch failed). */
+ * counter (s_memtime: core clock cycles of the CU it ran on), out[3g + 1] =
+ * the constant-rate real-time counter (s_memrealtime) and out[3g + 2] = where
+ * it ran: (XCD id << 16) | (HW_ID bits 15:8: CU, shader array, shader
+ * engine).  `out`: caller-owned device memory of 3 * n_groups uint64 values.
+ * The cycle counters of different CUs are not in step, so two probes
+ * enqueued before and after a run of kernels give a CU's mean clock over the
+ * run only from records of the same location: (cycles after - cycles before)
+ * / (real after - real before) times the real-time counter's rate
+ * (splash_realtime_khz).  Which CUs a probe's work-groups land on is up to
+ * the dispatcher; with n_groups = 256 on an MI355X most CUs are stamped by
+ * both probes.  Errors: SPLASH_EINVAL (NULL out, n_groups outside 1..4096),
+ * SPLASH_EHIP (launch failed). */
 int splash_clock_probe(uint64_t* out, int n_groups, void* stream);
 
 /* Rate of the current device's real-time counter in kHz
