@@ -14,7 +14,8 @@
 // every visited block.
 //
 // gfx950 design:
-//   * delta kernel: one wave per query row computes D_i from o and do.
+//   * The dq kernel runs first and also computes D_i from o and do for its
+//     rows, writing it for the dk/dv kernel.
 //   * dk/dv kernel: one work-group (4 waves) per (K/V head, 64-key block)
 //     walks the block's column of the table (the q blocks that read it) for
 //     every query head of the GQA group, in 64-row sub-tiles, so dk and dv
@@ -123,7 +124,6 @@ __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ float bf16_to_f32(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
 
 __device__ __forceinline__ bf16x8 ld_op(const lds_u16* ptr) { return *reinterpret_cast<const lds_bf16x8*>(ptr); }
 
@@ -271,22 +271,6 @@ __device__ __forceinline__ void p_and_ds(const BwdParams& p, bool ok, float s, f
   const float e = ok ? __builtin_amdgcn_exp2f(z2 - lse2) : 0.0f;
   *pe = e;
   *ds = e * (dpv - dlt) * fac;
-}
-
-template <int DV>
-__global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
-  const int lane = threadIdx.x & 63;
-  const int64_t n_rows = (int64_t)p.B * p.Hq * p.L;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= n_rows) return;
-  const uint16_t* o = static_cast<const uint16_t*>(p.o) + row * DV;
-  const uint16_t* d = static_cast<const uint16_t*>(p.dout) + row * DV;
-  float acc = 0.0f;
-#pragma unroll
-  for (int e = lane; e < DV; e += 64) acc += bf16_to_f32(o[e]) * bf16_to_f32(d[e]);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
-  if (lane == 0) p.delta[row] = acc;
 }
 
 template <int DQK, int DV>
@@ -656,7 +640,27 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
     df[st] = __builtin_bit_cast(bf16x8, v);
   }
   const float lse2 = in ? p.lse[(int64_t)head * p.L + qi] * kLog2e : INFINITY;
-  const float dlt = in ? p.delta[(int64_t)head * p.L + qi] : 0.0f;
+  // D_i = do_i . o_i: each lane holds half of its row's do (above) and reads
+  // the same half of o; the two halves meet across the half-waves.  Written
+  // for the dk/dv kernel, which runs after this one.
+  float dlt;
+  {
+    const uint16_t* ogr = static_cast<const uint16_t*>(p.o) + (int64_t)head * p.L * DV;
+    float acc = 0.0f;
+#pragma unroll
+    for (int st = 0; st < DV / 16; ++st) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (in) v = *reinterpret_cast<const u32x4*>(ogr + (int64_t)qi * DV + 16 * st + 8 * hi);
+      const u32x4 d = __builtin_bit_cast(u32x4, df[st]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc = fmaf(__uint_as_float(d[j] << 16), __uint_as_float(v[j] << 16), acc);
+        acc = fmaf(__uint_as_float(d[j] & 0xffff0000u), __uint_as_float(v[j] & 0xffff0000u), acc);
+      }
+    }
+    dlt = acc + __shfl_xor(acc, 32);
+    if (in && hi == 0) p.delta[(int64_t)head * p.L + qi] = dlt;
+  }
   const bool has_seg = p.seg_q != nullptr;
   const int qseg = (has_seg && in) ? p.seg_q[(int64_t)b * p.L + qi] : 0;
   // The wave's 32 rows in one segment (its id qseg0); see the dk/dv kernel.
@@ -794,9 +798,17 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
 
 template <int DQK, int DV, bool CAP>
 hipError_t launch_all(const BwdParams& p, hipStream_t s) {
-  const int64_t rows = (int64_t)p.B * p.Hq * p.L;
-  if (rows > 0) {
-    hipLaunchKernelGGL(bwd_delta_kernel<DV>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, p);
+  // dq first: it also writes D_i (p.delta), which the dk/dv kernel reads.
+  const int64_t n_q_items = (int64_t)p.B * p.Hq * p.n_q_blocks;
+  if (n_q_items > 0) {
+    constexpr int bytes = DqLds<DQK, DV>::BYTES;
+    auto fn = bwd_dq_kernel<DQK, DV, CAP>;
+    if (bytes > 65536) {
+      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(fn, dim3((unsigned)n_q_items), dim3(512), bytes, s, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -810,19 +822,6 @@ hipError_t launch_all(const BwdParams& p, hipStream_t s) {
       if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(fn, dim3((unsigned)n_kv_items), dim3(256), bytes, s, p);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  const int64_t n_q_items = (int64_t)p.B * p.Hq * p.n_q_blocks;
-  if (n_q_items > 0) {
-    constexpr int bytes = DqLds<DQK, DV>::BYTES;
-    auto fn = bwd_dq_kernel<DQK, DV, CAP>;
-    if (bytes > 65536) {
-      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-      if (e != hipSuccess) return e;
-    }
-    hipLaunchKernelGGL(fn, dim3((unsigned)n_q_items), dim3(512), bytes, s, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

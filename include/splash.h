@@ -418,10 +418,10 @@ typedef struct splash_bwd_args {
 } splash_bwd_args;
 
 /* Enqueue the backward on `stream` (a hipStream_t; NULL = the default
- * stream): a kernel for delta, one for dk and dv (one work-group per K/V
- * head and kv block, looping over the column's q blocks and the group's
- * query heads: no atomics) and one for dq (one work-group per query head
- * and q block, looping over the row's kv blocks).  Every element of dq, dk
+ * stream): a kernel for dq (one work-group per query head and q block,
+ * looping over the row's kv blocks), which also writes delta, then one for
+ * dk and dv (one work-group per K/V head and kv block, looping over the
+ * column's q blocks and the group's query heads: no atomics).  Every element of dq, dk
  * and dv is written (0 where no allowed pair reaches it).  Validation
  * errors are returned synchronously: SPLASH_EINVAL (NULL or misaligned
  * buffers, bad flag or window, scale, soft_cap, negative sizes),
