@@ -155,7 +155,12 @@ __device__ __forceinline__ void sfor(F&& f) {
 // voff of the buffer land at LDS address lds_addr + 16 i.  Issued as inline
 // assembly so that the compiler does not treat later LDS reads of *other*
 // buffers as dependent on it; completion is tracked explicitly with vmcnt.
-// M0 (the LDS base of the copy) is set here and declared clobbered.
+// M0 (the LDS base of the copy) is set here and declared clobbered.  clang
+// warns that it does not preserve a clobbered M0 for its own uses; these
+// kernels make none (a CPU test scans the generated code: M0 is written
+// only right before these copies), so the warning is silenced here.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(u32x4 rsrc, uint32_t lds_addr, int voff) {
   const uint32_t base = (uint32_t)__builtin_amdgcn_readfirstlane(lds_addr);
   const u32x4 rs = {(uint32_t)__builtin_amdgcn_readfirstlane(rsrc[0]),
@@ -185,6 +190,7 @@ __device__ __forceinline__ void dma4(u32x4 rsrc, uint32_t lds_addr, int voff) {
       : "s"(base), "v"(voff), "s"(rs)
       : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 // Wait until at most N tile copies of this wave are in flight and all LDS
 // reads are done, then synchronise the work-group.
