@@ -372,42 +372,35 @@ void bwd_dkdv_kernel(BwdParams p) {
     const int x1 = p.col_ptr[c + 1];
     const int32_t* sq = has_seg ? p.seg_q + (int64_t)b * p.L : nullptr;
     // Cursor over the work-group's sub-tiles: query head cg of the group,
-    // entry cx of the column, sub-tile cs of that q block.  Sub-tiles whose
-    // positions allow no pair with this kv block are skipped.  crow, the
-    // first row of entry cx's q block, is read once per entry.
-    int cg = 0, cx = x0, cs = 0;
-    int crow = x0 < x1 ? sload(p.col_rows, x0) * BQ : 0;
+    // entry cx of the column, sub-tile cs of that q block.  The sub-tiles
+    // whose positions allow a pair with this kv block form one run per entry
+    // (every bound below is monotone in the row): rows row_lo .. row_hi, so
+    // cs runs from cs to chi, both set once per entry from its first row crow.
+    static_assert(SUB == 64, "sub-tile index by shift");
+    int row_lo = 0, row_hi = p.L - 1;
+    if (p.causal) row_lo = max(row_lo, key0 - p.q_off - SUB + 1);                      // q_off + row + SUB - 1 >= key0
+    if (p.window_right >= 0) row_lo = max(row_lo, key0 - p.window_right - p.q_off - SUB + 1);
+    if (p.window_left >= 0) row_hi = min(row_hi, key0 + BK - 1 + p.window_left - p.q_off);
+    int cg = 0, cx = x0, cs = 0, chi = -1, crow = 0;
+    auto enter = [&]() __attribute__((always_inline)) {
+      crow = sload(p.col_rows, cx) * BQ;
+      cs = max(0, (row_lo - crow + SUB - 1) >> 6);          // ceil((row_lo - crow) / SUB)
+      chi = min(BQ / SUB - 1, (row_hi - crow) >> 6);        // floor((row_hi - crow) / SUB)
+    };
+    if (x0 < x1) enter();
     auto next = [&](int* g_out, int* row0_out) __attribute__((always_inline)) -> bool {
-      while (cg < p.group) {
-        if (cx >= x1) {
-          ++cg;
+      if (x0 >= x1) return false;
+      while (cs > chi) {
+        if (++cx >= x1) {
+          if (++cg >= p.group) return false;
           cx = x0;
-          cs = 0;
-          if (x0 < x1) crow = sload(p.col_rows, x0) * BQ;
-          continue;
         }
-        if (cs >= BQ / SUB) {
-          ++cx;
-          cs = 0;
-          if (cx < x1) crow = sload(p.col_rows, cx) * BQ;
-          continue;
-        }
-        const int row0 = crow + cs * SUB;
-        ++cs;
-        if (row0 >= p.L) {
-          cs = BQ / SUB;
-          continue;
-        }
-        const int pa = p.q_off + row0;
-        const int pz = pa + SUB - 1;
-        if (p.causal && pz < key0) continue;
-        if (p.window_left >= 0 && pa - (key0 + BK - 1) > p.window_left) continue;
-        if (p.window_right >= 0 && key0 - pz > p.window_right) continue;
-        *g_out = cg;
-        *row0_out = row0;
-        return true;
+        enter();
       }
-      return false;
+      *g_out = cg;
+      *row0_out = crow + cs * SUB;
+      ++cs;
+      return true;
     };
     // The next sub-tile's Q, dO, lse, D and segment ids are fetched into
     // registers while the current one is computed.
