@@ -90,10 +90,15 @@ def _segments(seg_q, seg_kv, B, L, L_kv, device, cache=None):
                      or (hkv is not None and c["hkv"] is not None and np.array_equal(c["hkv"], hkv)))):
             return c
     per_batch = B > 1 and (bool((hq != hq[:1]).any()) or (hkv is not None and bool((hkv != hkv[:1]).any())))
-    up = lambda h, n: torch.from_numpy(np.array(np.broadcast_to(h, (B, n)), dtype=np.int32)).to(device)
+    # A row-major copy: numpy's default order would follow the broadcast's
+    # zero stride and lay [1, n] ids broadcast to [B, n] out column-major.
+    up = lambda h, n: torch.from_numpy(np.array(np.broadcast_to(h, (B, n)), dtype=np.int32, order="C")).to(device)
     rec = {"B": B, "device": dkey, "hq": hq.copy(), "hkv": None if hkv is None else hkv.copy(),
            "per_batch": per_batch, "dev_q": up(hq, L), "dev_kv": None if hkv is None else up(hkv, L_kv),
            "digest0": _seg_digest(hq[0], None if hkv is None else hkv[0])}
+    for t in (rec["dev_q"], rec["dev_kv"]):
+        if t is not None and not t.is_contiguous():
+            raise RuntimeError("segment ids must reach the kernels row-major")
     if cache is not None:
         cache["seg"] = rec
     return rec

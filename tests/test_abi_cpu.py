@@ -434,6 +434,8 @@ def test_segment_ids_are_cached_per_tables():
     a = _segments(seg, None, 2, L, L, "cpu", cache)
     assert not a["per_batch"] and a["hq"].shape == (1, L) and a["hkv"] is None
     assert tuple(a["dev_q"].shape) == (2, L) and (a["dev_q"].numpy() == seg).all()
+    # the kernels read [B, L] row-major through the raw pointer
+    assert a["dev_q"].is_contiguous() and a["dev_q"].stride() == (L, 1)
     assert a["digest0"] == _seg_digest(seg, None) == _seg_digest(seg, seg)
     assert _segments(seg.copy(), None, 2, L, L, "cpu", cache) is a          # same ids: cached
     other = seg.copy()
@@ -442,6 +444,9 @@ def test_segment_ids_are_cached_per_tables():
     assert b is not a and b["digest0"] != a["digest0"] and cache["seg"] is b
     c = _segments(np.stack([seg, other]), None, 2, L, L, "cpu", cache)
     assert c["per_batch"] and c["hq"].shape == (2, L)
+    assert c["dev_q"].stride() == (L, 1) and (c["dev_q"].numpy()[1] == other).all()
+    e = _segments(seg, other, 3, L, L, "cpu", None)
+    assert e["dev_kv"].stride() == (L, 1) and (e["dev_kv"].numpy() == other).all()
     d = _segments(np.stack([seg, seg]), None, 2, L, L, "cpu", None)
     assert not d["per_batch"]
     assert _segments(None, None, 2, L, L, "cpu", cache) is None
