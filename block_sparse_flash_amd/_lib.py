@@ -87,8 +87,8 @@ class BwdArgs(ctypes.Structure):
                 ("seg_q", c_ptr), ("seg_kv", c_ptr),
                 ("block_q", c_i32), ("block_kv", c_i32), ("n_q_blocks", c_i32),
                 ("n_kv_blocks", c_i32), ("n_active", c_i32),
-                ("row_ptr", c_ptr), ("active_cols", c_ptr), ("col_ptr", c_ptr),
-                ("col_rows", c_ptr),
+                ("row_ptr", c_ptr), ("row_order", c_ptr), ("active_cols", c_ptr),
+                ("col_ptr", c_ptr), ("col_rows", c_ptr),
                 ("scale", ctypes.c_float), ("soft_cap", ctypes.c_float)]
 
 

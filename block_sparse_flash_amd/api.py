@@ -518,7 +518,7 @@ def splash_bwd(q, k, v, o, lse, dout, *, scale: Optional[float] = None, soft_cap
             ptr(q), ptr(k), ptr(v), ptr(o), ptr(lse), ptr(dout), ptr(dq), ptr(dk), ptr(dv),
             ptr(delta), int(bool(causal)), window_left, window_right, ptr(sq), ptr(skv),
             bq, bkv, tabs.n_q_blocks, tabs.n_kv_blocks, tabs.n_active,
-            dev["row_ptr"].data_ptr(), dev["active_cols"].data_ptr(),
+            dev["row_ptr"].data_ptr(), dev["row_order"].data_ptr(), dev["active_cols"].data_ptr(),
             cdev["col_ptr"].data_ptr(), cdev["col_rows"].data_ptr(),
             float(scale), float(soft_cap))
         _lib.check(lib.splash_attn_bwd(ctypes.byref(args), ctypes.c_void_p(stream)))

@@ -28,6 +28,7 @@ struct BwdParams {
   const int32_t* seg_kv;  // [B, Lkv] or null (then seg_q, Lkv = L)
   int32_t n_q_blocks, n_kv_blocks;
   const int32_t* row_ptr;
+  const int32_t* row_order;  // rows longest first, or null (natural order)
   const int32_t* active_cols;
   const int32_t* col_ptr;
   const int32_t* col_rows;

@@ -99,6 +99,7 @@ extern "C" int splash_attn_bwd(const splash_bwd_args* args, void* stream) {
   p.n_q_blocks = static_cast<int32_t>(nq);
   p.n_kv_blocks = static_cast<int32_t>(nkv);
   p.row_ptr = a.row_ptr;
+  p.row_order = a.row_order;
   p.active_cols = a.active_cols;
   p.col_ptr = a.col_ptr;
   p.col_rows = a.col_rows;

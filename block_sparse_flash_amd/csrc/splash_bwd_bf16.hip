@@ -164,6 +164,32 @@ __device__ __forceinline__ void xcd_map(int w, int n_units, int n_per, int* unit
   }
 }
 
+// The dq kernel's order: as xcd_map, but the q blocks of a unit are taken
+// by rank (0 = the longest row), and on an XCD with several units the ranks
+// of two units at a time interleave (unit pair g: rank 0 of both, rank 1 of
+// both, ...).  With one work-group per item and the hardware handing items
+// to CUs in order, the longest rows then start first, as in a
+// longest-processing-time-first schedule, while only two units' K/V are in
+// flight per XCD (units in plain order, each shortest row first, left the
+// longest causal rows to run last: a 29% tail in a simulation of the
+// dispatch).
+__device__ __forceinline__ void xcd_map_ranked(int w, int n_units, int n_per, int* unit, int* rank) {
+  if (n_units % kNumXcd == 0) {
+    constexpr int G = 2;
+    const int xcd = w % kNumXcd;
+    const int slot = w / kNumXcd;
+    const int U = n_units / kNumXcd;            // units on this XCD
+    const int g = slot / (G * n_per);           // unit pair
+    const int gsz = min(G, U - g * G);          // units in it (1 for an odd last one)
+    const int rem = slot - g * G * n_per;
+    const int rk = rem / gsz;
+    *unit = (g * G + (rem - rk * gsz)) * kNumXcd + xcd;
+    *rank = rk;
+  } else {
+    xcd_map(w, n_units, n_per, unit, rank);
+  }
+}
+
 // Runs N unrolled steps: step i's operands are loaded by ld(i) DIST steps
 // before use(i, operands) consumes them, with scheduling fences so that the
 // compiler keeps the loads that far ahead (left alone it moves every LDS
@@ -600,7 +626,8 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
   const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
   int r, head;  // q block, b * Hq + h
-  xcd_map(blockIdx.x, p.B * p.Hq, p.n_q_blocks, &head, &r);
+  xcd_map_ranked(blockIdx.x, p.B * p.Hq, p.n_q_blocks, &head, &r);
+  if (p.row_order) r = p.row_order[r];
   const int b = head / p.Hq;
   const int h = head - b * p.Hq;
   const int bk = b * p.Hkv + h / p.group;

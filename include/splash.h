@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define SPLASH_VERSION 109
+#define SPLASH_VERSION 110
 
 /* Largest n_split of splash_attn_fwd_split. */
 #define SPLASH_MAX_SPLIT 64
@@ -410,6 +410,12 @@ typedef struct splash_bwd_args {
   int32_t n_kv_blocks;   /* ceil(L_kv / block_kv) */
   int32_t n_active;
   const int32_t* row_ptr;      /* device [n_q_blocks + 1] */
+  const int32_t* row_order;    /* device [n_q_blocks]: the rows longest first
+                                  (attn_mask_compile's row_order, a
+                                  permutation of 0 .. n_q_blocks - 1), the
+                                  order in which the dq kernel takes them;
+                                  NULL: row order 0, 1, ... (slower where
+                                  row lengths differ) */
   const int32_t* active_cols;  /* device [n_active] */
   const int32_t* col_ptr;      /* device [n_kv_blocks + 1] */
   const int32_t* col_rows;     /* device [n_active] */
