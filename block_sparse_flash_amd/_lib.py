@@ -29,7 +29,7 @@ SPLASH_MASK_STORED = 1
 EXPORTED = ("splash_version", "splash_last_error", "attn_mask_compile",
             "splash_fwd_tile", "splash_fwd_tiles", "splash_attn_fwd",
             "splash_split_workspace_bytes", "splash_attn_fwd_split",
-            "splash_attn_fwd_split_noalloc", "attn_mask_columns",
+            "splash_attn_fwd_split_noalloc", "attn_mask_columns", "attn_mask_column_order",
             "splash_bwd_tile", "splash_attn_bwd", "splash_clock_probe",
             "splash_realtime_khz")
 SPLASH_MAX_SPLIT = 64
@@ -88,7 +88,7 @@ class BwdArgs(ctypes.Structure):
                 ("block_q", c_i32), ("block_kv", c_i32), ("n_q_blocks", c_i32),
                 ("n_kv_blocks", c_i32), ("n_active", c_i32),
                 ("row_ptr", c_ptr), ("row_order", c_ptr), ("active_cols", c_ptr),
-                ("col_ptr", c_ptr), ("col_rows", c_ptr),
+                ("col_ptr", c_ptr), ("col_rows", c_ptr), ("col_order", c_ptr),
                 ("scale", ctypes.c_float), ("soft_cap", ctypes.c_float)]
 
 
@@ -144,6 +144,8 @@ def load():
         lib.splash_attn_fwd_split_noalloc.argtypes = [ctypes.POINTER(FwdArgs), c_i32, c_ptr]
         lib.attn_mask_columns.restype = ctypes.c_int
         lib.attn_mask_columns.argtypes = [c_i32, c_i32, c_i32, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr]
+        lib.attn_mask_column_order.restype = ctypes.c_int
+        lib.attn_mask_column_order.argtypes = [c_i32, c_ptr, c_ptr]
         lib.splash_attn_bwd.restype = ctypes.c_int
         lib.splash_attn_bwd.argtypes = [ctypes.POINTER(BwdArgs), c_ptr]
         lib.splash_clock_probe.restype = ctypes.c_int

@@ -161,7 +161,8 @@ class MaskTables:
     def columns(self):
         """Column-major view of the active list (``attn_mask_columns``):
         host arrays ``col_ptr`` [n_kv_blocks + 1], ``col_rows`` and
-        ``col_entry`` [n_active]."""
+        ``col_entry`` [n_active], and ``col_order`` [n_kv_blocks], the
+        columns most active blocks first (``attn_mask_column_order``)."""
         if self._columns is None:
             lib = _lib.load()
             cols = {"col_ptr": np.zeros(self.n_kv_blocks + 1, np.int32),
@@ -173,11 +174,15 @@ class MaskTables:
                                              _ptr(row_ptr), _ptr(active_cols),
                                              _ptr(cols["col_ptr"]), _ptr(cols["col_rows"]),
                                              _ptr(cols["col_entry"])))
+            cols["col_order"] = np.zeros(self.n_kv_blocks, np.int32)
+            _lib.check(lib.attn_mask_column_order(self.n_kv_blocks, _ptr(cols["col_ptr"]),
+                                                  _ptr(cols["col_order"])))
             self._columns = cols
         return self._columns
 
     def device_columns(self, device):
-        """Device copies (torch tensors) of ``col_ptr`` and ``col_rows``."""
+        """Device copies (torch tensors) of ``col_ptr``, ``col_rows`` and
+        ``col_order``."""
         import torch
         key = "cols:" + str(torch.device(device))
         if key not in self._device:
@@ -185,7 +190,7 @@ class MaskTables:
             def up(a):
                 t = torch.from_numpy(np.ascontiguousarray(a)).to(torch.int32)
                 return (t if t.numel() else torch.zeros(1, dtype=torch.int32)).to(device)
-            self._device[key] = {"col_ptr": up(cols["col_ptr"]), "col_rows": up(cols["col_rows"])}
+            self._device[key] = {k: up(cols[k]) for k in ("col_ptr", "col_rows", "col_order")}
         return self._device[key]
 
     def device(self, device):
@@ -519,7 +524,7 @@ def splash_bwd(q, k, v, o, lse, dout, *, scale: Optional[float] = None, soft_cap
             ptr(delta), int(bool(causal)), window_left, window_right, ptr(sq), ptr(skv),
             bq, bkv, tabs.n_q_blocks, tabs.n_kv_blocks, tabs.n_active,
             dev["row_ptr"].data_ptr(), dev["row_order"].data_ptr(), dev["active_cols"].data_ptr(),
-            cdev["col_ptr"].data_ptr(), cdev["col_rows"].data_ptr(),
+            cdev["col_ptr"].data_ptr(), cdev["col_rows"].data_ptr(), cdev["col_order"].data_ptr(),
             float(scale), float(soft_cap))
         _lib.check(lib.splash_attn_bwd(ctypes.byref(args), ctypes.c_void_p(stream)))
     return dq, dk, dv

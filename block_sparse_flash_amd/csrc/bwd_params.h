@@ -32,6 +32,7 @@ struct BwdParams {
   const int32_t* active_cols;
   const int32_t* col_ptr;
   const int32_t* col_rows;
+  const int32_t* col_order;  // columns most active blocks first, or null (natural order)
   float scale;       // softmax scale
   float scale_log2;  // scale * log2(e)
   float soft_cap;    // > 0 when the cap is on

@@ -324,3 +324,19 @@ extern "C" int attn_mask_columns(int32_t n_q_blocks, int32_t n_kv_blocks, int32_
   }
   return SPLASH_OK;
 }
+
+extern "C" int attn_mask_column_order(int32_t n_kv_blocks, const int32_t* col_ptr, int32_t* col_order) {
+  splash::clear_error();
+  if (n_kv_blocks < 0) return splash::fail(SPLASH_EINVAL, "attn_mask_column_order: negative size");
+  if (!col_ptr || (n_kv_blocks > 0 && !col_order))
+    return splash::fail(SPLASH_EINVAL, "attn_mask_column_order: NULL array");
+  if (col_ptr[0] != 0) return splash::fail(SPLASH_EINVAL, "attn_mask_column_order: col_ptr must start at 0");
+  for (int32_t c = 0; c < n_kv_blocks; ++c)
+    if (col_ptr[c + 1] < col_ptr[c])
+      return splash::fail(SPLASH_EINVAL, "attn_mask_column_order: col_ptr decreases at column %d", c);
+  for (int32_t c = 0; c < n_kv_blocks; ++c) col_order[c] = c;
+  std::stable_sort(col_order, col_order + n_kv_blocks, [col_ptr](int32_t a, int32_t b) {
+    return col_ptr[a + 1] - col_ptr[a] > col_ptr[b + 1] - col_ptr[b];
+  });
+  return SPLASH_OK;
+}

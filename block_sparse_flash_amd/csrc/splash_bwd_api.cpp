@@ -103,6 +103,7 @@ extern "C" int splash_attn_bwd(const splash_bwd_args* args, void* stream) {
   p.active_cols = a.active_cols;
   p.col_ptr = a.col_ptr;
   p.col_rows = a.col_rows;
+  p.col_order = a.col_order;
   p.scale = a.scale;
   p.scale_log2 = a.scale * 1.4426950408889634f;
   p.soft_cap = a.soft_cap > 0.0f ? a.soft_cap : 0.0f;

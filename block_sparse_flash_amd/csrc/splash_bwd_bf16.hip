@@ -358,6 +358,7 @@ void bwd_dkdv_kernel(BwdParams p) {
 
   int c, bk;  // kv block, b * Hkv + kv head
   xcd_map(blockIdx.x, p.B * p.Hkv, p.n_kv_blocks, &bk, &c);
+  if (p.col_order) c = p.col_order[c];  // the longest columns first
   const int b = bk / p.Hkv;
   const int kvh = bk - b * p.Hkv;
   const int key0 = c * BK;

@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define SPLASH_VERSION 110
+#define SPLASH_VERSION 111
 
 /* Largest n_split of splash_attn_fwd_split. */
 #define SPLASH_MAX_SPLIT 64
@@ -199,6 +199,15 @@ int attn_mask_compile(const splash_mask_desc* desc, splash_mask_sizes* sizes,
 int attn_mask_columns(int32_t n_q_blocks, int32_t n_kv_blocks, int32_t n_active,
                       const int32_t* row_ptr, const int32_t* active_cols,
                       int32_t* col_ptr, int32_t* col_rows, int32_t* col_entry);
+
+/* The kv-block columns ordered by their number of active blocks, most
+ * first, ties in column order (a stable sort): the order in which the
+ * backward's dK/dV kernel takes its columns (splash_bwd_args.col_order),
+ * so that the longest columns start first.  From col_ptr [n_kv_blocks + 1]
+ * of attn_mask_columns; writes the host array col_order [n_kv_blocks].
+ * Errors: SPLASH_EINVAL (negative size, NULL array, col_ptr not starting at
+ * 0 or decreasing). */
+int attn_mask_column_order(int32_t n_kv_blocks, const int32_t* col_ptr, int32_t* col_order);
 
 /* ------------------------------------------------------------------------
  * Forward.
@@ -419,6 +428,11 @@ typedef struct splash_bwd_args {
   const int32_t* active_cols;  /* device [n_active] */
   const int32_t* col_ptr;      /* device [n_kv_blocks + 1] */
   const int32_t* col_rows;     /* device [n_active] */
+  const int32_t* col_order;    /* device [n_kv_blocks]: the columns in the
+                                  order of attn_mask_column_order (a
+                                  permutation of 0 .. n_kv_blocks - 1), the
+                                  order in which the dK/dV kernel takes
+                                  them; NULL: column order 0, 1, ... */
   float scale;           /* as in the forward */
   float soft_cap;        /* as in the forward; <= 0 disables it */
 } splash_bwd_args;

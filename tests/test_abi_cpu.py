@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
     assert set(declared) == set(_lib.EXPORTED), declared
     for name in declared:
         assert hasattr(lib, name), name
-    assert lib.splash_version() == 110
+    assert lib.splash_version() == 111
 
 
 def _assert_tables_equal(t, ref):
@@ -341,6 +341,30 @@ def test_columns_errors():
     assert lib.attn_mask_columns(2, 2, 3, P(row_ptr), P(bad), P(cp), P(cr), P(ce)) == 1
     out = np.array([0, 2, 1], np.int32)          # column out of range
     assert lib.attn_mask_columns(2, 2, 3, P(row_ptr), P(out), P(cp), P(cr), P(ce)) == 1
+    assert len(lib.splash_last_error()) > 0
+
+
+def test_column_order():
+    """attn_mask_column_order: columns by active-block count, most first,
+    ties in column order (numpy's stable argsort of the negated counts)."""
+    lib = _lib.load()
+    P = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    cp = np.array([0, 2, 7, 12, 13, 13], np.int32)   # counts 2, 5, 5, 1, 0
+    out = np.full(5, -1, np.int32)
+    assert lib.attn_mask_column_order(5, P(cp), P(out)) == 0
+    assert out.tolist() == [1, 2, 0, 3, 4]
+    rng = np.random.default_rng(7)
+    for n in (1, 3, 64, 513):
+        counts = rng.integers(0, 6, n).astype(np.int32)
+        cp = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+        out = np.zeros(n, np.int32)
+        assert lib.attn_mask_column_order(n, P(cp), P(out)) == 0
+        assert out.tolist() == np.argsort(-counts, kind="stable").tolist()
+    assert lib.attn_mask_column_order(0, P(np.zeros(1, np.int32)), None) == 0
+    assert lib.attn_mask_column_order(-1, P(cp), P(out)) == 1
+    assert lib.attn_mask_column_order(2, None, P(out)) == 1
+    assert lib.attn_mask_column_order(2, P(np.array([1, 2, 3], np.int32)), P(out)) == 1
+    assert lib.attn_mask_column_order(2, P(np.array([0, 2, 1], np.int32)), P(out)) == 1
     assert len(lib.splash_last_error()) > 0
 
 
