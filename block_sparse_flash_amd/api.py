@@ -460,7 +460,7 @@ def realtime_khz() -> int:
 def splash_bwd(q, k, v, o, lse, dout, *, scale: Optional[float] = None, soft_cap: float = 0.0,
                causal: bool = False, window_left: int = -1, window_right: int = -1,
                seg_q=None, seg_kv=None, q_offset: int = 0, tables: Optional[MaskTables] = None,
-               stream=None):
+               stream=None, natural_order: bool = False):
     """Block-sparse attention backward on the GPU (``splash_attn_bwd``).
 
     q, k, v, ``o`` (the forward's output) and ``dout`` (the upstream
@@ -468,7 +468,10 @@ def splash_bwd(q, k, v, o, lse, dout, *, scale: Optional[float] = None, soft_cap
     forward's shapes; ``lse`` is the forward's float32 lse [B, Hq, L]; the
     mask arguments are those of the forward.  Returns (dq, dk, dv) as float32
     tensors shaped like q, k and v.  Head dims (64, 64), (128, 128) or
-    (192, 128).
+    (192, 128).  ``natural_order`` passes no row and column orders, so the
+    kernels take their items in table order instead of longest first (the
+    results are the same; it is slower where rows or columns differ in
+    length).
     """
     import torch
     lib = _lib.load()
@@ -523,8 +526,9 @@ def splash_bwd(q, k, v, o, lse, dout, *, scale: Optional[float] = None, soft_cap
             ptr(q), ptr(k), ptr(v), ptr(o), ptr(lse), ptr(dout), ptr(dq), ptr(dk), ptr(dv),
             ptr(delta), int(bool(causal)), window_left, window_right, ptr(sq), ptr(skv),
             bq, bkv, tabs.n_q_blocks, tabs.n_kv_blocks, tabs.n_active,
-            dev["row_ptr"].data_ptr(), dev["row_order"].data_ptr(), dev["active_cols"].data_ptr(),
-            cdev["col_ptr"].data_ptr(), cdev["col_rows"].data_ptr(), cdev["col_order"].data_ptr(),
+            dev["row_ptr"].data_ptr(), None if natural_order else dev["row_order"].data_ptr(),
+            dev["active_cols"].data_ptr(), cdev["col_ptr"].data_ptr(), cdev["col_rows"].data_ptr(),
+            None if natural_order else cdev["col_order"].data_ptr(),
             float(scale), float(soft_cap))
         _lib.check(lib.splash_attn_bwd(ctypes.byref(args), ctypes.c_void_p(stream)))
     return dq, dk, dv

@@ -127,6 +127,26 @@ def test_backward_deterministic():
         assert torch.equal(a, b)
 
 
+def test_backward_item_order_changes_nothing():
+    """The kernels' item orders (longest q blocks and kv columns first, from
+    the tables) against table order (NULL orders through the C ABI): a
+    schedule only, so the gradients are bit-identical.  GQA with documents,
+    16 query heads (two per XCD, interleaved by the dq kernel) and uneven
+    columns."""
+    _announce("backward item order")
+    L = 1500
+    seg = segment_ids(L, 91, 40, 600)
+    q, k, v = (stored(a, "bf16").cuda() for a in draw_qkv(2, 8, 2, L, 128, 128, 92))
+    do = torch.randn(2, 8, L, 128, generator=torch.Generator().manual_seed(93)).to(torch.bfloat16).cuda()
+    mk = dict(causal=True, seg_q=seg)
+    o, lse = splash_fwd(q, k, v, **mk)
+    g1 = splash_bwd(q, k, v, o, lse, do, **mk)
+    g2 = splash_bwd(q, k, v, o, lse, do, natural_order=True, **mk)
+    torch.cuda.synchronize()
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+
+
 def test_backward_full_size_sampled_heads():
     """The bench's backward workload (dense causal L=4096, B=2, Hq=Hkv=32,
     d=128) at full size: every gradient element of three heads against the
