@@ -77,6 +77,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kTau = 8.0f;      // log2 of the largest p allowed before a rescale
+constexpr float kPsum = 256.0f;   // 2^kTau
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit dwords
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -472,6 +473,9 @@ __device__ __forceinline__ void item_fwd(const FwdParams& p, int head, int r, in
     const int gw = wave - (grp1 ? GW : 0);   // wave index inside its group
     float mc = mle ? p.mle_log2 : 0.0f;  // reference exponent offset m zc (0 while m = -inf)
     float mthr = -INFINITY;       // m + kTau / zc: block maxima above it move m
+    // A lane's partial row sum of p above it may mean a move: -1 until the
+    // row has a reference (every block then checks), then 2^kTau.
+    float psthr = -1.0f;
 
     // Key segment ids of a block, for the element mask of partial blocks,
     // are copied into an LDS ring (slot = block index mod 3) by one wave of
@@ -752,7 +756,11 @@ __device__ __forceinline__ void item_fwd(const FwdParams& p, int head, int r, in
         asm volatile("" ::"v"(ps));
       }
       // With the max logit estimate the reference is fixed: no max at all.
-      if (!mle) {
+      // Otherwise the row max is needed only when some p of the block
+      // exceeds 2^kTau, and then the lane's partial sum of its p (all >= 0)
+      // does too: that one compare stands in for the max tree on almost every
+      // block.  A sum above the bound without such a p only costs the tree.
+      if (!mle && __any(ps > psthr)) {
         // Row max: a tree of three-input maxima over the lane's 16 NTILE scores
         // (32 -> 11 -> 4 -> 2 -> 1, 16 instructions for one 64-key block),
         // then the other half-wave; with the cap a tree of minima over u,
@@ -779,6 +787,7 @@ __device__ __forceinline__ void item_fwd(const FwdParams& p, int head, int r, in
           mref = mnew;
           mc = (mnew == -INFINITY) ? 0.0f : mnew * zc;
           mthr = mnew + kTau / zc;
+          psthr = (mnew == -INFINITY) ? -1.0f : kPsum;
           ps = exps(sv, mc, [&](auto) __attribute__((always_inline)) {}, Idx<0>{});
           lsum *= alpha;
           sfor<0, DT>([&](auto i_) { oacc[SIDX(i_)] *= alpha; });
