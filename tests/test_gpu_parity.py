@@ -47,6 +47,69 @@ def _compare(o, lse, o_ref, lse_ref, dtype):
     return err_o, err_l
 
 
+
+def _lane_keys():
+    """Keys of a 64-key block held by the lanes of each half-wave in the
+    bf16 forward (two 32-key score tiles; item e of tile t is key
+    32 t + 8 (e / 4) + 4 hi + e % 4)."""
+    return [[32 * t + 8 * (e // 4) + 4 * hi + e % 4 for t in range(2) for e in range(16)] for hi in range(2)]
+
+
+def _reference_moves(q, k, scale, rows):
+    """A float64 model of the forward's lazy reference on causal rows at the
+    256x64 tile: a block's row max is taken when some lane's partial sum of
+    p exceeds 2^8 (or the row has no reference yet) and moves the reference
+    when it exceeds it by more than 8 in log2 units.  Returns (moves after a
+    row's first block, blocks whose sum passed the bound without a move)."""
+    lanes = _lane_keys()
+    moves = no_move = 0
+    for h in range(q.shape[0]):
+        s = (q[h] @ k[h].T) * scale / math.log(2.0)
+        for i in rows:
+            mc, seen = 0.0, False
+            for b in range(i // 64 + 1):
+                keys = np.arange(64 * b, 64 * b + 64)
+                x = np.where(keys <= i, s[i, np.minimum(keys, s.shape[1] - 1)], -np.inf) - mc
+                p = np.exp2(x)
+                if seen and max(p[lanes[0]].sum(), p[lanes[1]].sum()) <= 256.0:
+                    continue
+                mx = x.max()
+                if (not seen and mx > -np.inf) or mx > 8.0:
+                    moves += seen
+                    mc, seen = mc + mx, True
+                elif seen:
+                    no_move += 1
+    return moves, no_move
+
+
+def test_rising_and_falling_logits_move_the_reference():
+    """Logits that rise along the keys (head 0: fast, then slowly) and fall
+    (head 1), up to about 120, causal: on head 0 a row's exponent reference
+    moves again and again after its first block, and some blocks' partial
+    sums of p pass 2^8 without any p doing so (the guard takes the row max
+    and nothing moves); on head 1 the first block's reference holds.  Every
+    element against the oracle."""
+    _announce("rising and falling logits")
+    L, d = 1024, 128
+    rng = np.random.default_rng(11)
+    u = rng.standard_normal(d)
+    u /= np.linalg.norm(u)
+    q = np.stack([4.0 * u + 0.05 * rng.standard_normal((L, d)) for _ in range(2)])
+    j = np.arange(L)
+    rise = np.where(j < L // 2, 0.25 * j, 0.25 * (L // 2) + 0.07 * (j - L // 2))
+    g = np.stack([rise, rise[::-1].copy()]) * math.sqrt(d) / 4.0 * math.log(2.0)
+    k = g[:, :, None] * u[None, None, :] + 0.3 * rng.standard_normal((2, L, d))
+    v = rng.standard_normal((2, L, d))
+    qs, ks, vs = (stored(torch.from_numpy(a[None].astype(np.float32)), "bf16") for a in (q, k, v))
+    scale = 1.0 / math.sqrt(d)
+    moves, no_move = _reference_moves(as_f64(qs)[0], as_f64(ks)[0], scale, range(0, L, 7))
+    assert moves > 100 and no_move > 10, (moves, no_move)
+    o, lse = _run(qs, ks, vs, scale=scale, causal=True)
+    o_ref, lse_ref = attention_ref(as_f64(qs), as_f64(ks), as_f64(vs), scale=scale, causal=True)
+    assert float(lse_ref.max()) > 100.0
+    eo, el = _compare(o, lse, o_ref, lse_ref, "bf16")
+    _announce(f"  moves {moves}, guard without move {no_move}; max-abs o {eo:.3g} lse {el:.3g}")
+
 SMALL = [
     # (dtype, B, Hq, Hkv, L, d_qk, d_v, mask kwargs, soft_cap, mask_mode)
     ("f32", 1, 1, 1, 256, 64, 64, dict(causal=True), 0.0, "computed"),
