@@ -6,7 +6,7 @@ matrix is materialised (in row panels of at most ``panel`` rows, each over
 every key), the mask is applied element by element, and the softmax is taken
 over the allowed keys of each row.
 
-Readings of the pages taken here (each one is also listed in the design doc):
+Readings of the pages taken here:
 
 * Scale first, then the soft cap: ``s = cap * tanh(scale * q.k / cap)``;
   ``cap <= 0`` means no cap.  (Lecture 13, section 5.2 kernel body: the cap

@@ -10,8 +10,8 @@ with every element allowed is full (no mask work), anything else is partial
 pattern, selected through ``mask_next``; ``bounds_start``/``bounds_end`` mark
 the first/last active block of a query-block row (initialise / finalise).
 
-Encodings (the pages name the arrays but not their encodings; readings listed
-in DESIGN.md):
+Encodings (the pages name the arrays but not their encodings, so these are
+readings of them):
 
 * ``block_mask`` [nq, nkv] int8: 0 empty, 1 partial, 2 full.
 * Active blocks in row-major order (q-block row, then kv-block column
