@@ -110,6 +110,44 @@ def test_rising_and_falling_logits_move_the_reference():
     eo, el = _compare(o, lse, o_ref, lse_ref, "bf16")
     _announce(f"  moves {moves}, guard without move {no_move}; max-abs o {eo:.3g} lse {el:.3g}")
 
+
+RISING = [
+    # (name, Hq, Hkv, L_q, L_kv, q_offset, d_qk, d_v, soft_cap, n_split)
+    ("d64", 2, 2, 700, 700, 0, 64, 64, 0.0, 1),
+    ("d192x128", 2, 2, 700, 700, 0, 192, 128, 0.0, 1),
+    ("cap30", 2, 2, 700, 700, 0, 128, 128, 30.0, 1),
+    ("decode-gqa-split3", 8, 2, 16, 2000, 1984, 128, 128, 0.0, 3),
+]
+
+
+@pytest.mark.parametrize("case", RISING, ids=lambda c: c[0])
+def test_rising_logits_other_instances(case):
+    """The rising-logit inputs (the exponent reference moves block after
+    block) on the other kernel instances that share the guarded row max:
+    64- and 192-wide heads, the soft cap (logits capped at 30), and a decode
+    shape (16 rows at the end of 2000 keys, packed GQA rows, split-KV in
+    three chunks, the 64-row decode tile).  Every element against the
+    oracle."""
+    name, Hq, Hkv, Lq, Lkv, off, dqk, dv, cap, S = case
+    _announce(f"rising logits {name}")
+    rng = np.random.default_rng(12)
+    u = rng.standard_normal(dqk)
+    u /= np.linalg.norm(u)
+    j = np.arange(Lkv)
+    # logits rise by up to 0.25 (log2 units) per key, to about 120 at the last key
+    g = (0.25 * min(1.0, 700 / Lkv) * j) * math.sqrt(dqk) / 4.0 * math.log(2.0)
+    q = 4.0 * u + 0.05 * rng.standard_normal((Hq, Lq, dqk))
+    k = g[None, :, None] * u[None, None, :] + 0.3 * rng.standard_normal((Hkv, Lkv, dqk))
+    v = rng.standard_normal((Hkv, Lkv, dv))
+    qs, ks, vs = (stored(torch.from_numpy(a[None].astype(np.float32)), "bf16") for a in (q, k, v))
+    scale = 1.0 / math.sqrt(dqk)
+    o, lse = _run(qs, ks, vs, scale=scale, soft_cap=cap, causal=True, q_offset=off, n_split=S)
+    o_ref, lse_ref = attention_ref(as_f64(qs), as_f64(ks), as_f64(vs), scale=scale, soft_cap=cap,
+                                   causal=True, q_offset=off)
+    assert float(lse_ref.max()) > (20.0 if cap else 100.0)
+    eo, el = _compare(o, lse, o_ref, lse_ref, "bf16")
+    _announce(f"  max-abs o {eo:.3g} lse {el:.3g}")
+
 SMALL = [
     # (dtype, B, Hq, Hkv, L, d_qk, d_v, mask kwargs, soft_cap, mask_mode)
     ("f32", 1, 1, 1, 256, 64, 64, dict(causal=True), 0.0, "computed"),
